@@ -1,0 +1,122 @@
+/*
+ * svref.h -- CPU oracle for the speculative-decoding verify step.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This is the plain, slow, single-threaded fp64
+ * definition of what the verify step computes.  It shares no code, header,
+ * table or constant with the HIP library under rejection_sampling_amd/csrc,
+ * and only the test suite, the smoke check and the CPU-baseline leg of the
+ * benchmark may load it.  The product path never calls it.
+ *
+ * Sources (the pages are web pages; citations name page and section):
+ *  - "Adaptive verification for DFLASH ... built on upstream DSpark"
+ *    (jianc99/sglang PR #8), commit note on build_speculative_verify_target_probs:
+ *    top-k is selected on the raw logits and only the selected values are
+ *    divided by the temperature; top-k/top-p distribution; deterministic ties.
+ *  - Same page, commit note "run DFLASH through the existing DSpark machinery":
+ *    every accept path stops at the planned verify length, greedy accept with
+ *    precomputed argmax ids, the bonus comes from the last verified row.
+ *  - "dspark-upstream-consolidation" study (rtx6kpro), section 2: greedy accepts
+ *    iff draft == target argmax; temperature > 0 runs the Leviathan ratio test;
+ *    Gumbel noise keyed by position.  Sections 3-4: fp64 acceptance uniforms.
+ *  - TensorRT-LLM PR #17056 "DSpark confidence scheduling", first commit note and
+ *    description: prefix survival is a cumulative product of per-position
+ *    probabilities, the budget goes out by global survival rank with a
+ *    value-independent tie-break, windows are packed with a qo_indptr; the
+ *    review-pass note: tokens submitted per request are verify_len + 1.
+ *  - Philox4x32-10: Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As
+ *    Easy as 1, 2, 3", SC'11.
+ *  - Ratio test and residual max(0, p - q): Leviathan, Kalman, Matias, "Fast
+ *    Inference from Transformers via Speculative Decoding", ICML 2023.
+ *
+ * Row layout: request r owns rows [qo_indptr[r], qo_indptr[r+1]).  Its first
+ * gamma_r = rows_r - 1 rows verify drafted tokens 0..gamma_r-1; its last row is
+ * the bonus row.  All pointers are host pointers.  Every function returns 0 on
+ * success and a negative value on a malformed argument.
+ */
+#ifndef SVREF_H
+#define SVREF_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { SVREF_F32 = 0, SVREF_BF16 = 1 };
+
+/* Row flag bits written by svref_rejection_sample. */
+enum {
+  SVREF_ROW_ACCEPT = 1,     /* this draft row's test accepted its token          */
+  SVREF_ROW_SAMPLED = 2,    /* this row produced the emitted correction/bonus    */
+  SVREF_ROW_NEAR_RATIO = 4, /* |u - ratio| < 1e-5                                */
+  SVREF_ROW_NEAR_TOPP = 8,  /* top-p boundary mass within 1e-6 * Z_K             */
+  SVREF_ROW_NEAR_RACE = 16, /* best and second race keys within 1e-6 (relative)  */
+  SVREF_ROW_RESID_EMPTY = 32,/* residual was zero on the kept set: raced over p  */
+  SVREF_ROW_BAD_DRAFT = 64  /* draft id outside [0, V): rejected                 */
+};
+
+typedef struct {
+  const float* temperature;  /* [R]  T <= 0 or NaN: greedy                    */
+  const int32_t* top_k;      /* [R]  k <= 0 or k >= V: off; NULL: off         */
+  const float* top_p;        /* [R]  P >= 1 or NaN: off; P <= 0: top-1; NULL: off */
+  const uint32_t* request_id;/* [R]  Philox counter word; NULL: r             */
+  const uint32_t* position0; /* [R]  absolute position of window row 0; NULL: 0 */
+  uint64_t seed;             /* Philox key                                    */
+  uint32_t flags;            /* unused by the oracle                          */
+} svref_sampling;
+
+/* Philox4x32-10 block function: out = Philox(key, ctr). */
+void svref_philox4x32_10(const uint32_t key[2], const uint32_t ctr[4], uint32_t out[4]);
+
+/* Acceptance uniform in [0,1) for (seed, request id, absolute position). */
+double svref_uniform_accept(uint64_t seed, uint32_t request_id, uint32_t position);
+
+/* Race uniform in (0,1) for token `token` under stream `tag` (1 verify, 2 draft). */
+double svref_uniform_race(uint64_t seed, uint32_t request_id, uint32_t position,
+                          uint32_t tag, uint32_t token);
+
+/* Target distribution per row.  Every output pointer may be NULL.
+ *   probs     [rows, ld_probs] fp64, p on the kept set, 0 elsewhere
+ *   row_max, row_argmax, row_lse (lse at T_eff = T, or 1 on greedy rows)
+ *   kept_count [rows], kept_idx [rows, kmax] in order (value desc, index asc),
+ *   row_zn    [rows] mass of the kept set relative to the row max (Z_N)
+ *   row_flags [rows] SVREF_ROW_NEAR_TOPP where the top-p boundary is a near tie */
+int32_t svref_build_target_probs(const void* logits, int32_t dtype, int64_t ld_logits,
+                                 int32_t num_rows, int32_t vocab, const int32_t* qo_indptr,
+                                 int32_t num_requests, const svref_sampling* sp, double* probs,
+                                 int64_t ld_probs, double* row_max, int32_t* row_argmax,
+                                 double* row_lse, int32_t* kept_count, int32_t* kept_idx,
+                                 int32_t kmax, double* row_zn, uint8_t* row_flags);
+
+/* The verify step.  draft_probs may be NULL only when every request is greedy.
+ * verify_cap may be NULL.  row_ratio / row_u (diagnostics, may be NULL) get the
+ * ratio and the uniform of each tested draft row (NaN elsewhere). */
+int32_t svref_rejection_sample(const void* logits, int32_t dtype, int64_t ld_logits,
+                               int32_t vocab, const int32_t* qo_indptr, int32_t num_requests,
+                               int32_t num_rows, const int32_t* draft_tokens,
+                               const float* draft_probs, int64_t ld_q, const int32_t* verify_cap,
+                               const svref_sampling* sp, int32_t* accept_len, int32_t* out_tokens,
+                               int32_t* next_token, uint8_t* row_flags, double* row_ratio,
+                               double* row_u);
+
+/* Confidence planner: survival cumprod (fp32), rank (S desc, j asc, r asc),
+ * budget -> verify_len [R], qo_indptr [R+1], survival [R, block] (may be NULL). */
+int32_t svref_plan_windows(const float* confidence, int64_t ld_conf, int32_t num_requests,
+                           int32_t block, int32_t budget, int32_t* verify_len,
+                           int32_t* qo_indptr, float* survival);
+
+/* Accepted prefix length per request from per-row accept bytes. */
+int32_t svref_accept_prefix(const uint8_t* accepted, const int32_t* qo_indptr,
+                            int32_t num_requests, const int32_t* verify_cap, int32_t* accept_len);
+
+/* Harness helper: one exponential-race sample per row from dense fp32
+ * probability rows, keyed (seed, request id, position0 + j, tag). */
+int32_t svref_sample_probs(const float* probs, int64_t ld_probs, int32_t num_rows, int32_t vocab,
+                           const int32_t* qo_indptr, int32_t num_requests,
+                           const uint32_t* request_id, const uint32_t* position0, uint64_t seed,
+                           uint32_t tag, int32_t* out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,25 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
+    config.addinivalue_line("markers", "slow: takes more than a few seconds on CPU")
+
+
+def progress(msg: str) -> None:
+    """Print and flush one progress line (names the case before a GPU step)."""
+    print(f"[case] {msg}", flush=True)
+
+
+@pytest.fixture(scope="session")
+def oracle():
+    from oracle import svref
+    svref.lib()
+    return svref
