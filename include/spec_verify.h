@@ -1,0 +1,175 @@
+/*
+ * spec_verify.h -- C ABI of the MI355X (gfx950) verify step of speculative
+ * decoding.
+ *
+ * One shared library, libspecverify.so, exports the calls below.  They take
+ * plain device pointers and sizes; every tensor is device memory owned by the
+ * caller.  Every call is asynchronous on the given HIP stream, reads no device
+ * memory on the host, never synchronises and allocates nothing, so a caller may
+ * capture it in a HIP graph.  Results are bitwise reproducible and do not
+ * depend on batch composition: every random draw is keyed by (seed, request id,
+ * absolute position), never by batch slot.
+ *
+ * Layout.  Request r owns the packed rows [qo_indptr[r], qo_indptr[r+1]) of
+ * every per-row tensor (the qo_indptr packing of TensorRT-LLM PR #17056,
+ * "DSpark confidence scheduling", description).  Its first gamma_r = rows_r - 1
+ * rows verify drafted tokens 0..gamma_r-1 and its last row is the bonus row
+ * (tokens submitted per request are verify_len + 1: same page, review-pass
+ * commit note).  qo_indptr is int32 [R+1], non-decreasing, qo_indptr[0] = 0,
+ * qo_indptr[R] = num_rows; every request owns at least its bonus row.
+ *
+ * Per-request sampling values live in device arrays and are clamped on the
+ * device, never reported: T <= 0 or NaN -> greedy; k <= 0 or k >= V -> top-k
+ * off; P >= 1 or NaN -> top-p off; P <= 0 -> keep the top token only.
+ *
+ * Errors.  Every call returns SV_OK (0) or a negative code for a problem the
+ * host can see (null pointer, bad size, bad dtype, workspace too small, HIP
+ * launch error).  spec_verify_status_string() names a code and
+ * spec_verify_last_error() gives a thread-local message for the last failure.
+ * Contract violations inside device data (a non-monotone qo_indptr, a
+ * qo_indptr[R] different from num_rows) are undefined.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* sv_stream_t; /* a hipStream_t; NULL is the default stream */
+
+typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
+
+enum {
+  SV_OK = 0,
+  SV_ERR_NULL = -1,      /* a required pointer is NULL                          */
+  SV_ERR_SHAPE = -2,     /* a size or leading dimension is out of range         */
+  SV_ERR_DTYPE = -3,     /* unknown logit dtype, or a pointer misaligned for it */
+  SV_ERR_WORKSPACE = -4, /* workspace missing or smaller than the size query    */
+  SV_ERR_HIP = -5        /* a HIP call failed (message in spec_verify_last_error) */
+};
+
+/* Hints in sv_sampling.flags. */
+enum {
+  SV_ALL_GREEDY = 1u /* every request is greedy: draft_probs may be NULL. The
+                        host-side all-greedy skip of the consolidation study,
+                        section 6 (sampling prep is inert at temperature 0). */
+};
+
+/* Row flag bits written by spec_verify_rejection_sample (row_flags). */
+enum {
+  SV_ROW_ACCEPT = 1,      /* this draft row's test accepted its token       */
+  SV_ROW_SAMPLED = 2,     /* this row produced the correction / bonus token */
+  SV_ROW_RESID_EMPTY = 32 /* residual was zero on the kept set; sampled p   */
+};
+
+typedef struct {
+  const float* temperature;  /* [R] device; T <= 0 or NaN: greedy                   */
+  const int32_t* top_k;      /* [R] device or NULL (off)                            */
+  const float* top_p;        /* [R] device or NULL (off)                            */
+  const uint32_t* request_id;/* [R] device or NULL (r): Philox counter word         */
+  const uint32_t* position0; /* [R] device or NULL (0): absolute position of row 0  */
+  uint64_t seed;             /* Philox4x32-10 key                                   */
+  uint32_t flags;            /* SV_ALL_GREEDY                                       */
+} sv_sampling;
+
+/* Bytes of device workspace the calls below need for these sizes (block: the
+ * planner's positions per request, 0 when the planner is not used).  The
+ * workspace is scratch: its contents need no initialisation and are
+ * meaningless after the call. */
+size_t spec_verify_workspace_bytes(int32_t num_rows, int32_t vocab, int32_t num_requests,
+                                   int32_t block);
+
+/* Target distribution per row ("Adaptive verification for DFLASH ... built on
+ * upstream DSpark", commit note on build_speculative_verify_target_probs):
+ * top-k selected on the raw logits, the temperature applied to the selected
+ * values only, then top-p over the top-k renormalised distribution, softmax.
+ * Ties are broken by lower token id everywhere.
+ *   logits     [num_rows, ld_logits] row-major, dt = SV_BF16 or SV_F32
+ *   probs      [num_rows, ld_probs] fp32 or NULL: p on the kept set, 0 elsewhere
+ *   row_max, row_argmax, row_lse [num_rows] or NULL; lse is log sum exp(x / T_eff)
+ *              over the whole row with T_eff = T, or 1 on greedy rows
+ *   kept_count [num_rows] or NULL; kept_idx [num_rows, kmax] or NULL: the first
+ *              min(kept_count, kmax) kept ids in order (value desc, id asc), then -1.
+ *              kmax <= 1024.
+ * Returns SV_ERR_SHAPE when ld_logits < vocab, ld_probs < vocab, kmax > 1024. */
+int32_t spec_verify_build_target_probs(const void* logits, sv_dtype dt, int64_t ld_logits,
+                                       int32_t num_rows, int32_t vocab,
+                                       const int32_t* qo_indptr, int32_t num_requests,
+                                       const sv_sampling* sp, float* probs, int64_t ld_probs,
+                                       float* row_max, int32_t* row_argmax, float* row_lse,
+                                       int32_t* kept_count, int32_t* kept_idx, int32_t kmax,
+                                       void* workspace, size_t workspace_bytes,
+                                       sv_stream_t stream);
+
+/* The fused verify step.  Per draft row: greedy accepts iff the draft equals
+ * the target argmax; temperature > 0 runs the ratio test u < min(1, p(d)/q(d))
+ * of Leviathan et al. with an fp64 Philox uniform keyed (seed, request id,
+ * position0 + j) (consolidation study, sections 2-4).  At the first rejection
+ * the row samples the residual max(0, p - q) by an exponential race (Gumbel-max
+ * keyed by position); after a full accept the bonus is sampled from p at the
+ * row after the last verified draft ("the bonus comes from the last verified
+ * row", DFLASH-through-DSpark commit note).  verify_cap (cap-accept) stops
+ * acceptance at min(gamma_r, verify_cap[r]) without changing the rule.
+ *   draft_tokens [num_rows] int32; the bonus row's entry is ignored; an id
+ *              outside [0, V) is never accepted (the row then samples p)
+ *   draft_probs [num_rows, ld_q] fp32 draft distributions, only gathered; may
+ *              be NULL only with SV_ALL_GREEDY
+ *   verify_cap [R] or NULL
+ *   accept_len [R]; out_tokens [num_rows]: row s_r + j holds draft j for
+ *              j < L, the sampled token at j = L, -1 after; next_token [R]: the
+ *              sampled (correction or bonus) token; row_flags [num_rows] or NULL.
+ * Returns SV_ERR_NULL when draft_probs is NULL without SV_ALL_GREEDY. */
+int32_t spec_verify_rejection_sample(const void* target_logits, sv_dtype dt, int64_t ld_logits,
+                                     int32_t vocab, const int32_t* qo_indptr,
+                                     int32_t num_requests, int32_t num_rows,
+                                     const int32_t* draft_tokens, const float* draft_probs,
+                                     int64_t ld_q, const int32_t* verify_cap,
+                                     const sv_sampling* sp, int32_t* accept_len,
+                                     int32_t* out_tokens, int32_t* next_token,
+                                     uint8_t* row_flags, void* workspace,
+                                     size_t workspace_bytes, sv_stream_t stream);
+
+/* Confidence planner (TensorRT-LLM PR #17056, first commit note: prefix
+ * survival is the cumulative product of per-position probabilities; the budget
+ * goes out by global survival rank with a value-independent tie-break).
+ * Confidences are clamped to [0,1] (NaN -> 0); S[r][j] = c[r][0]*...*c[r][j] in
+ * fp32, left to right; all (r, j) are ranked by (S desc, j asc, r asc) and the
+ * first min(budget, R*block) are verified.
+ *   confidence [R, ld_conf] fp32; verify_len [R] int32; qo_indptr [R+1] int32,
+ *   exclusive scan of verify_len + 1 (one bonus row per request), so
+ *   qo_indptr[R] = min(budget, R*block) + R is known on the host;
+ *   survival [R, block] fp32 or NULL.
+ * Requires R * block < 2^31. */
+int32_t spec_verify_plan_windows(const float* confidence, int64_t ld_conf, int32_t num_requests,
+                                 int32_t block, int32_t budget, int32_t* verify_len,
+                                 int32_t* qo_indptr, float* survival, void* workspace,
+                                 size_t workspace_bytes, sv_stream_t stream);
+
+/* Accepted prefix from per-row accept bytes (greedy accept with precomputed
+ * argmax ids, DFLASH-through-DSpark commit note): accept_len[r] = first j <
+ * min(gamma_r, verify_cap[r]) with accepted[s_r + j] == 0, else that bound. */
+int32_t spec_verify_accept_prefix(const uint8_t* accepted, const int32_t* qo_indptr,
+                                  int32_t num_requests, const int32_t* verify_cap,
+                                  int32_t* accept_len, sv_stream_t stream);
+
+/* Diagnostics. */
+const char* spec_verify_status_string(int32_t code);
+const char* spec_verify_last_error(void);
+
+/* Per-kernel timing for measurement: while enabled, every launch of the
+ * library records a pair of HIP events on the call's stream; read() waits for
+ * them and returns, per kernel id, the launch count and the summed
+ * milliseconds since the last reset.  Kernel ids: 0 row pass, 1 request
+ * finalize, 2 target-probs writer, 3 planner, 4 accept prefix. */
+int32_t spec_verify_profile_enable(int32_t on);
+int32_t spec_verify_profile_read(int32_t kernel_id, int64_t* launches, double* total_ms);
+int32_t spec_verify_profile_reset(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

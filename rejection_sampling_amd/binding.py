@@ -1,0 +1,247 @@
+"""Thin ctypes binding of libspecverify.so (include/spec_verify.h).
+
+Argument marshalling only: torch tensors are checked for device, dtype and
+layout and passed as raw pointers with the current HIP stream.  Every step of
+the verify path runs in the library's HIP kernels; there is no host or torch
+fallback.  Importing this module on a machine without the built library, or
+calling it without a GPU, raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libspecverify.so")
+
+SV_F32, SV_BF16 = 0, 1
+SV_ALL_GREEDY = 1
+ROW_ACCEPT, ROW_SAMPLED, ROW_RESID_EMPTY = 1, 2, 32
+KERNEL_IDS = {"row_pass": 0, "finalize": 1, "build_out": 2, "planner": 3, "accept_prefix": 4}
+
+EXPORTS = [
+    "spec_verify_workspace_bytes", "spec_verify_build_target_probs",
+    "spec_verify_rejection_sample", "spec_verify_plan_windows", "spec_verify_accept_prefix",
+    "spec_verify_status_string", "spec_verify_last_error", "spec_verify_profile_enable",
+    "spec_verify_profile_read", "spec_verify_profile_reset",
+]
+
+
+class Sampling(ctypes.Structure):
+    _fields_ = [("temperature", ctypes.c_void_p), ("top_k", ctypes.c_void_p),
+                ("top_p", ctypes.c_void_p), ("request_id", ctypes.c_void_p),
+                ("position0", ctypes.c_void_p), ("seed", ctypes.c_uint64),
+                ("flags", ctypes.c_uint32)]
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load the library (no GPU needed to load it)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built: run `python -m rejection_sampling_amd.build` "
+                           "or __graft_entry__.build()")
+    L = ctypes.CDLL(path)
+    P, i32, i64, u64, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64,
+                            ctypes.c_size_t)
+    L.spec_verify_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    L.spec_verify_workspace_bytes.restype = sz
+    L.spec_verify_build_target_probs.argtypes = [P, i32, i64, i32, i32, P, i32, P, P, i64, P, P,
+                                                 P, P, P, i32, P, sz, P]
+    L.spec_verify_build_target_probs.restype = i32
+    L.spec_verify_rejection_sample.argtypes = [P, i32, i64, i32, P, i32, i32, P, P, i64, P, P, P,
+                                               P, P, P, P, sz, P]
+    L.spec_verify_rejection_sample.restype = i32
+    L.spec_verify_plan_windows.argtypes = [P, i64, i32, i32, i32, P, P, P, P, sz, P]
+    L.spec_verify_plan_windows.restype = i32
+    L.spec_verify_accept_prefix.argtypes = [P, P, i32, P, P, P]
+    L.spec_verify_accept_prefix.restype = i32
+    L.spec_verify_status_string.argtypes = [i32]
+    L.spec_verify_status_string.restype = ctypes.c_char_p
+    L.spec_verify_last_error.argtypes = []
+    L.spec_verify_last_error.restype = ctypes.c_char_p
+    L.spec_verify_profile_enable.argtypes = [i32]
+    L.spec_verify_profile_enable.restype = i32
+    L.spec_verify_profile_read.argtypes = [i32, P, P]
+    L.spec_verify_profile_read.restype = i32
+    L.spec_verify_profile_reset.argtypes = []
+    L.spec_verify_profile_reset.restype = i32
+    _lib = L
+    return L
+
+
+class SpecVerifyError(RuntimeError):
+    pass
+
+
+def _check(rc: int):
+    if rc != 0:
+        L = load()
+        raise SpecVerifyError(f"{L.spec_verify_status_string(rc).decode()} ({rc}): "
+                              f"{L.spec_verify_last_error().decode()}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _dev(t: Optional[torch.Tensor], dtype, name):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _logits(t: torch.Tensor, name="logits"):
+    if not t.is_cuda or t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be a 2-D device tensor with unit column stride")
+    if t.dtype == torch.bfloat16:
+        return SV_BF16
+    if t.dtype == torch.float32:
+        return SV_F32
+    raise ValueError(f"{name} must be bfloat16 or float32")
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+_ws_cache = {}
+
+
+def workspace(num_rows: int, vocab: int, num_requests: int, block: int = 0,
+              device=None) -> torch.Tensor:
+    """A cached device workspace of at least the queried size."""
+    n = int(load().spec_verify_workspace_bytes(num_rows, vocab, num_requests, block))
+    dev = torch.device(device or "cuda")
+    cur = _ws_cache.get(dev)
+    if cur is None or cur.numel() < n:
+        cur = torch.empty(max(n, 1 << 20), dtype=torch.uint8, device=dev)
+        _ws_cache[dev] = cur
+    return cur
+
+
+class Params:
+    """Per-request sampling values as device tensors (kept alive with the call)."""
+
+    def __init__(self, temperature, top_k=None, top_p=None, request_id=None, position0=None,
+                 seed: int = 0, all_greedy: bool = False):
+        self.T = _dev(temperature, torch.float32, "temperature")
+        self.k = _dev(top_k, torch.int32, "top_k")
+        self.P = _dev(top_p, torch.float32, "top_p")
+        # request ids and positions are uint32 in the ABI; int32 tensors carry
+        # the same bits
+        self.rid = _dev(request_id, torch.int32, "request_id")
+        self.pos0 = _dev(position0, torch.int32, "position0")
+        self.s = Sampling(_ptr(self.T), _ptr(self.k), _ptr(self.P), _ptr(self.rid),
+                          _ptr(self.pos0), int(seed) & ((1 << 64) - 1),
+                          SV_ALL_GREEDY if all_greedy else 0)
+
+
+def build_target_probs(logits: torch.Tensor, qo_indptr: torch.Tensor, params: Params,
+                       want_probs: bool = False, kmax: int = 0):
+    dt = _logits(logits)
+    rows, V = logits.shape
+    qo = _dev(qo_indptr, torch.int32, "qo_indptr")
+    R = qo.numel() - 1
+    dev = logits.device
+    out = {
+        "row_max": torch.empty(rows, dtype=torch.float32, device=dev),
+        "row_argmax": torch.empty(rows, dtype=torch.int32, device=dev),
+        "row_lse": torch.empty(rows, dtype=torch.float32, device=dev),
+        "kept_count": torch.empty(rows, dtype=torch.int32, device=dev),
+        "kept_idx": torch.empty((rows, kmax), dtype=torch.int32, device=dev) if kmax else None,
+        "probs": torch.empty((rows, V), dtype=torch.float32, device=dev) if want_probs else None,
+    }
+    ws = workspace(rows, V, R, 0, dev)
+    rc = load().spec_verify_build_target_probs(
+        _ptr(logits), dt, logits.stride(0), rows, V, _ptr(qo), R, ctypes.byref(params.s),
+        _ptr(out["probs"]), V, _ptr(out["row_max"]), _ptr(out["row_argmax"]),
+        _ptr(out["row_lse"]), _ptr(out["kept_count"]), _ptr(out["kept_idx"]), kmax, _ptr(ws),
+        ws.numel(), _stream())
+    _check(rc)
+    return out
+
+
+def rejection_sample(logits: torch.Tensor, qo_indptr: torch.Tensor, draft_tokens: torch.Tensor,
+                     draft_probs: Optional[torch.Tensor], params: Params,
+                     verify_cap: Optional[torch.Tensor] = None, out=None):
+    dt = _logits(logits)
+    rows, V = logits.shape
+    qo = _dev(qo_indptr, torch.int32, "qo_indptr")
+    R = qo.numel() - 1
+    dev = logits.device
+    d = _dev(draft_tokens, torch.int32, "draft_tokens")
+    if draft_probs is not None:
+        if draft_probs.dtype != torch.float32 or not draft_probs.is_cuda or \
+                draft_probs.stride(1) != 1:
+            raise ValueError("draft_probs must be a 2-D fp32 device tensor")
+    cap = _dev(verify_cap, torch.int32, "verify_cap")
+    if out is None:
+        out = {
+            "accept_len": torch.empty(R, dtype=torch.int32, device=dev),
+            "out_tokens": torch.empty(rows, dtype=torch.int32, device=dev),
+            "next_token": torch.empty(R, dtype=torch.int32, device=dev),
+            "row_flags": torch.empty(rows, dtype=torch.uint8, device=dev),
+        }
+    ws = workspace(rows, V, R, 0, dev)
+    ldq = draft_probs.stride(0) if draft_probs is not None else V
+    rc = load().spec_verify_rejection_sample(
+        _ptr(logits), dt, logits.stride(0), V, _ptr(qo), R, rows, _ptr(d), _ptr(draft_probs), ldq,
+        _ptr(cap), ctypes.byref(params.s), _ptr(out["accept_len"]), _ptr(out["out_tokens"]),
+        _ptr(out["next_token"]), _ptr(out["row_flags"]), _ptr(ws), ws.numel(), _stream())
+    _check(rc)
+    return out
+
+
+def plan_windows(confidence: torch.Tensor, budget: int, want_survival: bool = True):
+    conf = _dev(confidence, torch.float32, "confidence")
+    R, B = conf.shape
+    dev = conf.device
+    vl = torch.empty(R, dtype=torch.int32, device=dev)
+    qo = torch.empty(R + 1, dtype=torch.int32, device=dev)
+    surv = torch.empty((R, B), dtype=torch.float32, device=dev) if want_survival else None
+    ws = workspace(0, 1, R, B, dev)
+    rc = load().spec_verify_plan_windows(_ptr(conf), B, R, B, int(budget), _ptr(vl), _ptr(qo),
+                                         _ptr(surv), _ptr(ws), ws.numel(), _stream())
+    _check(rc)
+    return vl, qo, surv
+
+
+def accept_prefix(accepted: torch.Tensor, qo_indptr: torch.Tensor,
+                  verify_cap: Optional[torch.Tensor] = None):
+    acc = _dev(accepted, torch.uint8, "accepted")
+    qo = _dev(qo_indptr, torch.int32, "qo_indptr")
+    cap = _dev(verify_cap, torch.int32, "verify_cap")
+    R = qo.numel() - 1
+    out = torch.empty(R, dtype=torch.int32, device=qo.device)
+    rc = load().spec_verify_accept_prefix(_ptr(acc), _ptr(qo), R, _ptr(cap), _ptr(out), _stream())
+    _check(rc)
+    return out
+
+
+def profile_enable(on: bool = True):
+    _check(load().spec_verify_profile_enable(1 if on else 0))
+
+
+def profile_reset():
+    _check(load().spec_verify_profile_reset())
+
+
+def profile_read(kernel: str):
+    n = ctypes.c_int64(0)
+    ms = ctypes.c_double(0.0)
+    _check(load().spec_verify_profile_read(KERNEL_IDS[kernel], ctypes.byref(n), ctypes.byref(ms)))
+    return int(n.value), float(ms.value)

@@ -1,0 +1,52 @@
+"""Build libspecverify.so for gfx950 in-tree with hipcc.
+
+The library is the C ABI declared in include/spec_verify.h; its sources are
+rejection_sampling_amd/csrc/*.hip.  Packed fp32 instructions are disabled
+(-packed-fp32-ops) and fp32 denormals are kept, so survival products and
+weights are IEEE single precision throughout.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libspecverify.so")
+SOURCES = ["sv_api.hip", "sv_verify.hip", "sv_plan.hip"]
+ARCH = os.environ.get("SV_OFFLOAD_ARCH", "gfx950")
+
+
+def hipcc() -> str:
+    for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found")
+
+
+def flags():
+    return [
+        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+        "-fno-gpu-flush-denormals-to-zero", "-ffp-contract=off",
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-Wno-unused-command-line-argument",
+        "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+    ]
+
+
+def build(verbose: bool = False) -> str:
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), *flags(), "-o", tmp, *srcs]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.check_call(cmd, cwd=HERE)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

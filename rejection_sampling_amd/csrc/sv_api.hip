@@ -1,0 +1,332 @@
+// sv_api.hip -- host side of libspecverify: argument checks, workspace
+// carving, launches, status codes and optional per-kernel event timing.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/spec_verify.h"
+#include "sv_device.hpp"
+#include "sv_kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int32_t fail(int32_t code, const char* what) {
+  g_last_error = what;
+  return code;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Layout {
+  size_t rec, list, keys, total;
+};
+
+Layout layout(int64_t rows, int64_t R, int64_t block) {
+  Layout L;
+  L.rec = 0;
+  L.list = align256((size_t)rows * sizeof(sv::RowRec));
+  L.keys = L.list + align256((size_t)rows * sv::kListCap * sizeof(sv::ListEntry));
+  L.total = L.keys + align256((size_t)(R * block) * sizeof(uint64_t)) + 256;
+  return L;
+}
+
+// ---- optional event timing
+struct Prof {
+  std::mutex mu;
+  bool on = false;
+  struct Rec { int id; hipEvent_t a, b; };
+  std::vector<Rec> pending;
+  int64_t launches[8] = {};
+  double ms[8] = {};
+};
+Prof& prof() {
+  static Prof p;
+  return p;
+}
+
+struct ProfScope {
+  int id;
+  hipStream_t s;
+  hipEvent_t a = nullptr, b = nullptr;
+  bool active = false;
+  ProfScope(int id_, hipStream_t s_) : id(id_), s(s_) {
+    Prof& p = prof();
+    std::lock_guard<std::mutex> g(p.mu);
+    if (!p.on) return;
+    if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) return;
+    (void)hipEventRecord(a, s);
+    active = true;
+  }
+  ~ProfScope() {
+    if (!active) return;
+    (void)hipEventRecord(b, s);
+    Prof& p = prof();
+    std::lock_guard<std::mutex> g(p.mu);
+    p.pending.push_back({id, a, b});
+  }
+};
+
+int32_t check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    g_last_error = std::string(what) + ": " + hipGetErrorString(e);
+    return SV_ERR_HIP;
+  }
+  return SV_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* spec_verify_status_string(int32_t code) {
+  switch (code) {
+    case SV_OK: return "ok";
+    case SV_ERR_NULL: return "null pointer";
+    case SV_ERR_SHAPE: return "bad size or leading dimension";
+    case SV_ERR_DTYPE: return "bad dtype or alignment";
+    case SV_ERR_WORKSPACE: return "workspace too small";
+    case SV_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* spec_verify_last_error(void) { return g_last_error.c_str(); }
+
+size_t spec_verify_workspace_bytes(int32_t num_rows, int32_t vocab, int32_t num_requests,
+                                   int32_t block) {
+  (void)vocab;
+  if (num_rows < 0) num_rows = 0;
+  if (num_requests < 0) num_requests = 0;
+  if (block < 0) block = 0;
+  return layout(num_rows, num_requests, block).total;
+}
+
+static int32_t check_common(const void* logits, sv_dtype dt, int64_t ld, int32_t rows, int32_t V,
+                            const int32_t* qo, int32_t R, const sv_sampling* sp) {
+  if (!sp) return fail(SV_ERR_NULL, "sampling parameters are NULL");
+  if (dt != SV_F32 && dt != SV_BF16) return fail(SV_ERR_DTYPE, "unknown logit dtype");
+  if (rows < 0 || R < 0) return fail(SV_ERR_SHAPE, "negative row or request count");
+  if (V <= 0) return fail(SV_ERR_SHAPE, "vocab must be positive");
+  if (ld < V) return fail(SV_ERR_SHAPE, "ld_logits < vocab");
+  if (R > 0 && !qo) return fail(SV_ERR_NULL, "qo_indptr is NULL");
+  if (rows > 0 && !logits) return fail(SV_ERR_NULL, "logits are NULL");
+  if (logits && !aligned(logits, dt == SV_BF16 ? 2 : 4))
+    return fail(SV_ERR_DTYPE, "logits pointer misaligned for its dtype");
+  if (rows > 0 && R == 0) return fail(SV_ERR_SHAPE, "rows without requests");
+  return SV_OK;
+}
+
+static sv::VerifyArgs base_args(const void* logits, sv_dtype dt, int64_t ld, int32_t V,
+                                const int32_t* qo, int32_t R, int32_t rows,
+                                const sv_sampling* sp, void* ws) {
+  sv::VerifyArgs A;
+  std::memset(&A, 0, sizeof(A));
+  A.logits = logits;
+  A.ld_logits = ld;
+  A.vocab = V;
+  A.dtype = dt == SV_BF16 ? 1 : 0;
+  A.qo = qo;
+  A.num_requests = R;
+  A.num_rows = rows;
+  A.temperature = sp->temperature;
+  A.top_k = sp->top_k;
+  A.top_p = sp->top_p;
+  A.request_id = sp->request_id;
+  A.position0 = sp->position0;
+  A.seed = sp->seed;
+  Layout L = layout(rows, R, 0);
+  A.rec = (sv::RowRec*)((char*)ws + L.rec);
+  A.list = (sv::ListEntry*)((char*)ws + L.list);
+  return A;
+}
+
+int32_t spec_verify_build_target_probs(const void* logits, sv_dtype dt, int64_t ld_logits,
+                                       int32_t num_rows, int32_t vocab,
+                                       const int32_t* qo_indptr, int32_t num_requests,
+                                       const sv_sampling* sp, float* probs, int64_t ld_probs,
+                                       float* row_max, int32_t* row_argmax, float* row_lse,
+                                       int32_t* kept_count, int32_t* kept_idx, int32_t kmax,
+                                       void* workspace, size_t workspace_bytes,
+                                       sv_stream_t stream) {
+  int32_t rc = check_common(logits, dt, ld_logits, num_rows, vocab, qo_indptr, num_requests, sp);
+  if (rc) return rc;
+  if (probs && ld_probs < vocab) return fail(SV_ERR_SHAPE, "ld_probs < vocab");
+  if (kmax < 0 || kmax > sv::kListCap) return fail(SV_ERR_SHAPE, "kmax must be in [0, 1024]");
+  if (kept_idx && kmax == 0) return fail(SV_ERR_SHAPE, "kept_idx needs kmax > 0");
+  if (num_rows == 0) return SV_OK;
+  if (!workspace) return fail(SV_ERR_WORKSPACE, "workspace is NULL");
+  if (workspace_bytes < spec_verify_workspace_bytes(num_rows, vocab, num_requests, 0))
+    return fail(SV_ERR_WORKSPACE, "workspace smaller than spec_verify_workspace_bytes()");
+  if (!aligned(workspace, 256)) return fail(SV_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  sv::VerifyArgs A = base_args(logits, dt, ld_logits, vocab, qo_indptr, num_requests, num_rows,
+                               sp, workspace);
+  A.build = 1;
+  {
+    ProfScope ps(0, s);
+    hipLaunchKernelGGL(sv::row_pass_kernel, dim3(num_rows), dim3(sv::kRowBlock), 0, s, A);
+  }
+  if ((rc = check_launch("row pass"))) return rc;
+  sv::BuildOutArgs B;
+  B.probs = probs;
+  B.ld_probs = ld_probs;
+  B.row_max = row_max;
+  B.row_argmax = row_argmax;
+  B.row_lse = row_lse;
+  B.kept_count = kept_count;
+  B.kept_idx = kept_idx;
+  B.kmax = kept_idx ? kmax : 0;
+  {
+    ProfScope ps(2, s);
+    hipLaunchKernelGGL(sv::build_out_kernel, dim3(num_rows), dim3(sv::kRowBlock), 0, s, A, B);
+  }
+  return check_launch("build outputs");
+}
+
+int32_t spec_verify_rejection_sample(const void* target_logits, sv_dtype dt, int64_t ld_logits,
+                                     int32_t vocab, const int32_t* qo_indptr,
+                                     int32_t num_requests, int32_t num_rows,
+                                     const int32_t* draft_tokens, const float* draft_probs,
+                                     int64_t ld_q, const int32_t* verify_cap,
+                                     const sv_sampling* sp, int32_t* accept_len,
+                                     int32_t* out_tokens, int32_t* next_token,
+                                     uint8_t* row_flags, void* workspace,
+                                     size_t workspace_bytes, sv_stream_t stream) {
+  int32_t rc = check_common(target_logits, dt, ld_logits, num_rows, vocab, qo_indptr,
+                            num_requests, sp);
+  if (rc) return rc;
+  if (num_rows > 0 && !draft_tokens) return fail(SV_ERR_NULL, "draft_tokens are NULL");
+  if (num_requests > 0 && (!accept_len || !next_token))
+    return fail(SV_ERR_NULL, "accept_len / next_token are NULL");
+  if (num_rows > 0 && !out_tokens) return fail(SV_ERR_NULL, "out_tokens are NULL");
+  if (!draft_probs && !(sp->flags & SV_ALL_GREEDY))
+    return fail(SV_ERR_NULL, "draft_probs is NULL without SV_ALL_GREEDY");
+  if (draft_probs && ld_q < vocab) return fail(SV_ERR_SHAPE, "ld_q < vocab");
+  if (draft_probs && !aligned(draft_probs, 4)) return fail(SV_ERR_DTYPE, "draft_probs misaligned");
+  if (num_requests == 0) return SV_OK;
+  if (!workspace) return fail(SV_ERR_WORKSPACE, "workspace is NULL");
+  if (workspace_bytes < spec_verify_workspace_bytes(num_rows, vocab, num_requests, 0))
+    return fail(SV_ERR_WORKSPACE, "workspace smaller than spec_verify_workspace_bytes()");
+  if (!aligned(workspace, 256)) return fail(SV_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  sv::VerifyArgs A = base_args(target_logits, dt, ld_logits, vocab, qo_indptr, num_requests,
+                               num_rows, sp, workspace);
+  A.build = 0;
+  A.draft_tokens = draft_tokens;
+  A.draft_probs = draft_probs;
+  A.ld_q = ld_q;
+  A.verify_cap = verify_cap;
+  A.accept_len = accept_len;
+  A.out_tokens = out_tokens;
+  A.next_token = next_token;
+  A.row_flags = row_flags;
+  if (!draft_probs) A.temperature = nullptr;  // SV_ALL_GREEDY: every request greedy
+  if (num_rows > 0) {
+    ProfScope ps(0, s);
+    hipLaunchKernelGGL(sv::row_pass_kernel, dim3(num_rows), dim3(sv::kRowBlock), 0, s, A);
+  }
+  if ((rc = check_launch("row pass"))) return rc;
+  {
+    ProfScope ps(1, s);
+    hipLaunchKernelGGL(sv::finalize_kernel, dim3(num_requests), dim3(sv::kRowBlock), 0, s, A);
+  }
+  return check_launch("finalize");
+}
+
+int32_t spec_verify_plan_windows(const float* confidence, int64_t ld_conf, int32_t num_requests,
+                                 int32_t block, int32_t budget, int32_t* verify_len,
+                                 int32_t* qo_indptr, float* survival, void* workspace,
+                                 size_t workspace_bytes, sv_stream_t stream) {
+  if (num_requests < 0 || block < 0) return fail(SV_ERR_SHAPE, "negative size");
+  if ((int64_t)num_requests * (int64_t)block >= (int64_t)1 << 31)
+    return fail(SV_ERR_SHAPE, "num_requests * block must be < 2^31");
+  if (!qo_indptr) return fail(SV_ERR_NULL, "qo_indptr is NULL");
+  if (num_requests > 0 && (!verify_len || (block > 0 && !confidence)))
+    return fail(SV_ERR_NULL, "confidence / verify_len are NULL");
+  if (num_requests > 0 && ld_conf < block) return fail(SV_ERR_SHAPE, "ld_conf < block");
+  const Layout L = layout(0, num_requests, block);
+  if (!workspace) return fail(SV_ERR_WORKSPACE, "workspace is NULL");
+  if (workspace_bytes < L.total) return fail(SV_ERR_WORKSPACE, "workspace too small");
+  if (!aligned(workspace, 256)) return fail(SV_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  sv::PlanArgs A;
+  A.conf = confidence;
+  A.ld_conf = ld_conf;
+  A.num_requests = num_requests;
+  A.block = block;
+  A.budget = budget;
+  A.verify_len = verify_len;
+  A.qo_indptr = qo_indptr;
+  A.survival = survival;
+  A.keys = (uint64_t*)((char*)workspace + L.keys);
+  {
+    ProfScope ps(3, s);
+    hipLaunchKernelGGL(sv::plan_kernel, dim3(1), dim3(sv::kPlanBlock), 0, s, A);
+  }
+  return check_launch("planner");
+}
+
+int32_t spec_verify_accept_prefix(const uint8_t* accepted, const int32_t* qo_indptr,
+                                  int32_t num_requests, const int32_t* verify_cap,
+                                  int32_t* accept_len, sv_stream_t stream) {
+  if (num_requests < 0) return fail(SV_ERR_SHAPE, "negative request count");
+  if (num_requests == 0) return SV_OK;
+  if (!accepted || !qo_indptr || !accept_len) return fail(SV_ERR_NULL, "null pointer");
+  hipStream_t s = (hipStream_t)stream;
+  {
+    ProfScope ps(4, s);
+    hipLaunchKernelGGL(sv::accept_prefix_kernel, dim3((num_requests + 3) / 4), dim3(256), 0, s,
+                       accepted, qo_indptr, num_requests, verify_cap, accept_len);
+  }
+  return check_launch("accept prefix");
+}
+
+int32_t spec_verify_profile_enable(int32_t on) {
+  Prof& p = prof();
+  std::lock_guard<std::mutex> g(p.mu);
+  p.on = on != 0;
+  return SV_OK;
+}
+
+int32_t spec_verify_profile_reset(void) {
+  Prof& p = prof();
+  std::lock_guard<std::mutex> g(p.mu);
+  for (auto& r : p.pending) {
+    (void)hipEventSynchronize(r.b);
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+  }
+  p.pending.clear();
+  for (int k = 0; k < 8; ++k) { p.launches[k] = 0; p.ms[k] = 0.0; }
+  return SV_OK;
+}
+
+int32_t spec_verify_profile_read(int32_t kernel_id, int64_t* launches, double* total_ms) {
+  if (kernel_id < 0 || kernel_id >= 8) return fail(SV_ERR_SHAPE, "kernel id out of range");
+  Prof& p = prof();
+  std::lock_guard<std::mutex> g(p.mu);
+  for (auto& r : p.pending) {
+    if (hipEventSynchronize(r.b) != hipSuccess) return fail(SV_ERR_HIP, "event synchronize");
+    float ms = 0.0f;
+    (void)hipEventElapsedTime(&ms, r.a, r.b);
+    p.launches[r.id] += 1;
+    p.ms[r.id] += ms;
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+  }
+  p.pending.clear();
+  if (launches) *launches = p.launches[kernel_id];
+  if (total_ms) *total_ms = p.ms[kernel_id];
+  return SV_OK;
+}
+
+}  // extern "C"

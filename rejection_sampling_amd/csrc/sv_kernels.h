@@ -1,0 +1,76 @@
+// sv_kernels.h -- kernel argument blocks and launch entry points shared by the
+// kernel translation units and the host library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sv {
+
+struct RowRec;
+struct ListEntry;
+
+struct VerifyArgs {
+  const void* logits;
+  int64_t ld_logits;
+  int32_t vocab;
+  int32_t dtype;          // 0 fp32, 1 bf16
+  const int32_t* qo;
+  int32_t num_requests;
+  int32_t num_rows;
+  const int32_t* draft_tokens;
+  const float* draft_probs;
+  int64_t ld_q;
+  const int32_t* verify_cap;
+  const float* temperature;
+  const int32_t* top_k;
+  const float* top_p;
+  const uint32_t* request_id;
+  const uint32_t* position0;
+  uint64_t seed;
+  int32_t build;          // 1: target-probs build (every row, lse), 0: verify
+  RowRec* rec;            // [num_rows]
+  ListEntry* list;        // [num_rows, kListCap]
+  int32_t* accept_len;
+  int32_t* out_tokens;
+  int32_t* next_token;
+  uint8_t* row_flags;
+};
+
+struct BuildOutArgs {
+  float* probs;
+  int64_t ld_probs;
+  float* row_max;
+  int32_t* row_argmax;
+  float* row_lse;
+  int32_t* kept_count;
+  int32_t* kept_idx;
+  int32_t kmax;
+};
+
+struct PlanArgs {
+  const float* conf;
+  int64_t ld_conf;
+  int32_t num_requests;
+  int32_t block;
+  int32_t budget;
+  int32_t* verify_len;
+  int32_t* qo_indptr;
+  float* survival;
+  uint64_t* keys;        // workspace [R * block]
+};
+
+__global__ void row_pass_kernel(VerifyArgs A);
+__global__ void finalize_kernel(VerifyArgs A);
+__global__ void build_out_kernel(VerifyArgs A, BuildOutArgs B);
+__global__ void plan_kernel(PlanArgs A);
+__global__ void accept_prefix_kernel(const uint8_t* accepted, const int32_t* qo, int32_t R,
+                                     const int32_t* verify_cap, int32_t* accept_len);
+
+// sizes shared with the host
+constexpr int kRowBlock = 256;
+constexpr int kPlanBlock = 1024;
+constexpr size_t kRowRecBytes = 56;
+constexpr size_t kListBytesPerRow = 1024 * 8;
+
+}  // namespace sv

@@ -1,0 +1,837 @@
+// sv_verify.hip -- verify-step kernels for gfx950.
+//
+//   row_pass_kernel   one workgroup per packed row: the streaming pass over the
+//                     logits, the kept set N of the row (top-k on raw logits,
+//                     temperature on the kept values only, then top-p, as the
+//                     build_speculative_verify_target_probs note of "Adaptive
+//                     verification for DFLASH" describes), p(d) and the ratio
+//                     test of the row's draft token (Leviathan et al.; greedy:
+//                     argmax match, consolidation study section 2).
+//   finalize_kernel   one workgroup per request: the accepted prefix (first
+//                     rejected row, capped by verify_cap), then one exponential
+//                     race on the single sampled row -- residual max(0, p - q)
+//                     after a rejection, p after a full accept.
+//   build_out_kernel  one workgroup per row: the outputs of the target-probs
+//                     build (max, argmax, lse, kept ids, dense p).
+#include <type_traits>
+
+#include "sv_device.hpp"
+#include "sv_rowpass.hpp"
+#include "sv_kernels.h"
+
+namespace sv {
+
+// ------------------------------------------------------------ exact path
+struct ExactOut {
+  uint32_t bkey;   // order key (32-bit) of the boundary value of N
+  int nb;          // ties at bkey kept
+  int nkeep;
+  double zk, zn;   // masses relative to exp(m/T)
+  int argmax;
+  int tie_d;       // ties of the draft value with a smaller id
+};
+
+__device__ __forceinline__ uint32_t key_of_prefix(uint32_t prefix, bool bf16) {
+  if (!bf16) return prefix;
+  // top 16 bits are the bf16 order key; rebuild the value, then its fp32 key
+  const uint32_t k16 = prefix >> 16;
+  const uint32_t u16 = (k16 & 0x8000u) ? (k16 & 0x7FFFu) : (~k16 & 0xFFFFu);
+  return fkey(__uint_as_float(u16 << 16));
+}
+
+// Walk 256 bins from the top: the digit d* where above + sum(d > d*) < target
+// <= above + sum(d >= d*).  Wave 0 computes; results land in sh.
+__device__ inline void walk_bins(const double* val, double above, double target, RowShared& sh,
+                                 double* out_above) {
+  if (wave_id() == 0) {
+    const int l = lane_id();
+    const double h0 = val[255 - 4 * l], h1 = val[254 - 4 * l];
+    const double h2 = val[253 - 4 * l], h3 = val[252 - 4 * l];
+    const double local = (h0 + h1) + (h2 + h3);
+    const double incl = wave_inclusive_sum(local);
+    const double excl = incl - local;
+    const double top = __shfl(incl, 63, 64);
+    bool here = above + excl < target && target <= above + incl;
+    uint64_t mk = __ballot(here);
+    // target beyond the total (rounding): take the last non-empty digit
+    if (mk == 0) mk = __ballot(above + excl < above + top && l == 63) | 0;
+    int src = mk ? __ffsll((unsigned long long)mk) - 1 : 63;
+    if (l == src) {
+      double c = above + excl;
+      int d;
+      if (c + h0 >= target || (h1 == 0 && h2 == 0 && h3 == 0)) d = 255 - 4 * l;
+      else if ((c += h0) + h1 >= target || (h2 == 0 && h3 == 0)) d = 254 - 4 * l;
+      else if ((c += h1) + h2 >= target || h3 == 0) d = 253 - 4 * l;
+      else { c += h2; d = 252 - 4 * l; }
+      sh.sel_digit = d;
+      sh.zn_shared = c;
+    }
+  }
+  __syncthreads();
+  *out_above = sh.zn_shared;
+}
+
+template <int DT>
+__device__ void exact_kept_set(const void* row, int V, float m, float T, int k_eff, float P,
+                               int d, float xd, RowShared& sh, ExactOut& o) {
+  constexpr bool kBf = DT == 1;
+  const float c = kLog2e / T;
+  int lg = 0;
+  while ((1ll << lg) < (long long)V + 1) ++lg;
+  const double scale = ldexp(1.0, 62 - lg);
+  uint64_t* mass = sh.buf;             // 256 x u64
+  double* vals = (double*)(sh.buf + 256);  // 256 x double
+  const uint32_t keyd = d >= 0 ? fkey(xd) : 0u;
+  const int top_shift = 24, low_shift = kBf ? 16 : 0;
+
+  int amin = 0x7FFFFFFF, tied = 0;
+  bool first = true;
+
+  // one histogram pass over elements with key >= klo and (key & pmask) == prefix
+  auto pass = [&](uint32_t prefix, uint32_t pmask, int shift, uint32_t klo) {
+    for (int b = threadIdx.x; b < 256; b += kBlock) { sh.hist[b] = 0u; mass[b] = 0ull; }
+    __syncthreads();
+    const bool fst = first;
+    for_each_element<DT>(row, V, [&](float x, int i) {
+      const uint32_t key = fkey(x);
+      if (fst) {
+        if (x == m && i < amin) amin = i;
+        if (d >= 0 && i < d && key == keyd) ++tied;
+      }
+      if (key < klo || (key & pmask) != prefix) return;
+      const uint32_t dg = (key >> shift) & 255u;
+      atomicAdd(&sh.hist[dg], 1u);
+      const float w = exp2f((x - m) * c);
+      atomicAdd((unsigned long long*)&mass[dg], (unsigned long long)((double)w * scale));
+    });
+    first = false;
+    __syncthreads();
+  };
+
+  // ---- top-k phase (count target)
+  uint32_t bk = 0;          // 32-bit key of the k-th element (0: top-k off)
+  int nbk = 0, cnt_bk = 0;
+  double zk = 0.0;          // fixed-point units
+  const bool topk_on = k_eff < V;
+  if (topk_on) {
+    uint32_t prefix = 0, pmask = 0;
+    double cnt_above = 0.0, mass_above = 0.0;
+    for (int shift = top_shift; shift >= low_shift; shift -= 8) {
+      pass(prefix, pmask, shift, 0u);
+      for (int b = threadIdx.x; b < 256; b += kBlock) vals[b] = (double)sh.hist[b];
+      __syncthreads();
+      double above;
+      walk_bins(vals, cnt_above, (double)k_eff, sh, &above);
+      const int dg = sh.sel_digit;
+      // mass of the digits strictly above dg
+      double mab = 0.0;
+      for (int b = threadIdx.x; b < 256; b += kBlock) vals[b] = b > dg ? (double)mass[b] : 0.0;
+      __syncthreads();
+      mab = block_sum_d(threadIdx.x < 256 ? vals[threadIdx.x] : 0.0, sh.dscr);
+      cnt_above = above;
+      mass_above += mab;
+      cnt_bk = (int)sh.hist[dg];
+      prefix |= (uint32_t)dg << shift;
+      pmask |= 0xFFu << shift;
+      __syncthreads();
+    }
+    bk = key_of_prefix(prefix, kBf);
+    nbk = k_eff - (int)cnt_above;
+    const float wb = exp2f((key_to_float(bk) - m) * c);
+    zk = mass_above + (double)nbk * (double)(unsigned long long)((double)wb * scale);
+    o.bkey = bk;
+    o.nb = nbk;
+    o.nkeep = k_eff;
+  }
+
+  // ---- top-p phase (mass target), restricted to K
+  const bool topp_on = P < 1.0f;
+  if (topp_on) {
+    uint32_t prefix = 0, pmask = 0;
+    double cnt_above = 0.0, mass_above = 0.0;
+    const float wbk = topk_on ? exp2f((key_to_float(bk) - m) * c) : 0.0f;
+    const double fx_bk = (double)(unsigned long long)((double)wbk * scale);
+    const int excess = topk_on ? cnt_bk - nbk : 0;
+    double target = -1.0;
+    for (int shift = top_shift; shift >= low_shift; shift -= 8) {
+      pass(prefix, pmask, shift, topk_on ? bk : 0u);
+      // remove the tied entries at bk that are outside K
+      const bool bk_here = topk_on && (bk & pmask) == prefix;
+      const int dbk = (int)((bk >> shift) & 255u);
+      for (int b = threadIdx.x; b < 256; b += kBlock) {
+        double mv = (double)mass[b];
+        if (bk_here && b == dbk) mv -= (double)excess * fx_bk;
+        vals[b] = mv;
+      }
+      __syncthreads();
+      if (target < 0.0) {
+        if (!topk_on) zk = block_sum_d(threadIdx.x < 256 ? vals[threadIdx.x] : 0.0, sh.dscr);
+        target = (double)P * zk;
+      }
+      double above;
+      walk_bins(vals, mass_above, target, sh, &above);
+      const int dg = sh.sel_digit;
+      double cab = 0.0;
+      {
+        const int b = threadIdx.x;
+        double cv = 0.0;
+        if (b < 256 && b > dg) {
+          cv = (double)sh.hist[b];
+          if (bk_here && b == dbk) cv -= (double)excess;
+        }
+        cab = block_sum_d(cv, sh.dscr);
+      }
+      cnt_above += cab;
+      mass_above = above;
+      prefix |= (uint32_t)dg << shift;
+      pmask |= 0xFFu << shift;
+      __syncthreads();
+    }
+    const uint32_t bp = key_of_prefix(prefix, kBf);
+    int avail;
+    {
+      // ties at bp inside K
+      uint32_t hb = sh.hist[(bp >> low_shift) & 255u];
+      avail = (int)hb;
+      if (topk_on && bp == bk) avail = nbk;
+    }
+    const float wbp = exp2f((key_to_float(bp) - m) * c);
+    const double fw = (double)(unsigned long long)((double)wbp * scale);
+    double need = fw > 0.0 ? ceil((target - mass_above) / fw) : 1.0;
+    int nb = need < 1.0 ? 1 : (need > (double)avail ? avail : (int)need);
+    if (nb < 1) nb = 1;
+    o.bkey = bp;
+    o.nb = nb;
+    o.nkeep = (int)cnt_above + nb;
+    o.zn = (mass_above + (double)nb * fw) / scale;
+  } else {
+    o.zn = zk / scale;
+  }
+  o.zk = zk / scale;
+
+  if (first) {
+    // no histogram pass ran (cannot happen: callers need top-k or top-p)
+    for_each_element<DT>(row, V, [&](float x, int i) {
+      if (x == m && i < amin) amin = i;
+      if (d >= 0 && i < d && fkey(x) == keyd) ++tied;
+    });
+  }
+  // argmax and tie count: block reductions
+  {
+    const uint64_t e = ((uint64_t)(uint32_t)(0x7FFFFFFF - amin));
+    const uint64_t best = block_max_u64(e, sh.uscr);
+    o.argmax = 0x7FFFFFFF - (int)(uint32_t)best;
+    o.tie_d = block_sum_i(tied, sh.iscr);
+  }
+}
+
+// -------------------------------------------------------- row pass kernel
+template <int DT>
+__device__ __forceinline__ void row_pass(const VerifyArgs& A, RowShared& sh) {
+  const int i = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int V = A.vocab;
+  const int r = row_to_request(A.qo, A.num_requests, i);
+  const int s = A.qo[r], e = A.qo[r + 1];
+  const int j = i - s;
+  const int gamma = e - s - 1;
+  int cap_eff = gamma;
+  if (A.verify_cap) {
+    int cv = A.verify_cap[r];
+    cap_eff = cv < 0 ? 0 : (cv > gamma ? gamma : cv);
+  }
+  RowRec* rec = A.rec + i;
+  const bool tested = !A.build && j < cap_eff;
+  const bool used = A.build || j <= cap_eff;
+  if (!used) {
+    if (tid == 0) {
+      RowRec z = {};
+      z.mode = kModeSkip;
+      *rec = z;
+    }
+    return;
+  }
+  const float T = A.temperature ? A.temperature[r] : 0.0f;
+  const bool greedy = !(T > 0.0f);
+  int k = A.top_k ? A.top_k[r] : 0;
+  const float P = A.top_p ? A.top_p[r] : 1.0f;
+  int k_eff = (k > 0 && k < V) ? k : V;
+  bool topp_on = P < 1.0f;
+  if (!(P > 0.0f) && !(P != P)) {  // P <= 0: keep only the top token
+    k_eff = 1;
+    topp_on = false;
+  }
+  const float teff = greedy ? 1.0f : T;
+  const float c = kLog2e / teff;
+  const void* row = (const char*)A.logits + (size_t)i * (size_t)A.ld_logits * (DT == 1 ? 2 : 4);
+  const int d = tested ? A.draft_tokens[i] : -1;
+  const bool d_ok = d >= 0 && d < V;
+  const uint32_t rid = A.request_id ? A.request_id[r] : (uint32_t)r;
+  const uint32_t pos0 = A.position0 ? A.position0[r] : 0u;
+
+  RowRec out = {};
+  out.lse = 0.0f;
+  out.pd = 0.0f;
+  const bool need_sum_build = A.build != 0;
+  StreamAcc acc;
+
+  // ------------------------------------------------ greedy rows
+  if (greedy) {
+    if (need_sum_build) stream_row<DT, false, true, true>(row, V, c, 1, sh, acc);
+    else stream_row<DT, false, false, true>(row, V, c, 1, sh, acc);
+    const float m = block_max_f(acc.mx, sh.fscr);
+    const uint64_t cand = acc.mx == m ? (uint64_t)(uint32_t)(0x7FFFFFFF - acc.bi) : 0ull;
+    const int a = 0x7FFFFFFF - (int)(uint32_t)block_max_u64(cand, sh.uscr);
+    if (need_sum_build) {
+      const double part = acc.s * (double)exp2f((acc.sref - m) * c);
+      const double Z = block_sum_d(part, sh.dscr);
+      out.lse = (float)((double)m / (double)teff + log(Z));
+    }
+    out.m = m;
+    out.a = a;
+    out.mode = kModeGreedy;
+    out.nkeep = 1;
+    out.zn = out.zk = 1.0;
+    if (tested) {
+      out.flags |= kRecTested;
+      if (!d_ok) out.flags |= kRecBadDraft;
+      if (d == a) out.flags |= kRecAccept;
+      out.pd = d == a ? 1.0f : 0.0f;
+    }
+    if (tid == 0) *rec = out;
+    return;
+  }
+
+  // ------------------------------------------------ sampled rows
+  const bool all_mode = k_eff == V && !topp_on;
+  const bool buf_mode = !all_mode && (k_eff <= kTopkFast || (k_eff == V && topp_on));
+  const int keep = k_eff < V ? k_eff : kKeepTopP;
+  const bool need_sum = need_sum_build || all_mode || (k_eff == V && topp_on);
+  if (all_mode) {
+    stream_row<DT, false, true, true>(row, V, c, 1, sh, acc);
+  } else if (buf_mode) {
+    if (need_sum) stream_row<DT, true, true, false>(row, V, c, keep, sh, acc);
+    else stream_row<DT, true, false, false>(row, V, c, keep, sh, acc);
+  } else {
+    if (need_sum) stream_row<DT, false, true, false>(row, V, c, 1, sh, acc);
+    else stream_row<DT, false, false, false>(row, V, c, 1, sh, acc);
+  }
+  const float m = block_max_f(acc.mx, sh.fscr);
+  double Z = 0.0;
+  if (need_sum) {
+    const double part = acc.s * (double)exp2f((acc.sref - m) * c);
+    Z = block_sum_d(part, sh.dscr);
+    out.lse = (float)((double)m / (double)T + log(Z));
+  }
+  out.m = m;
+  const double Td = (double)T;
+  double pd = 0.0;
+  bool exact = !buf_mode && !all_mode;
+
+  if (all_mode) {
+    const uint64_t cand = acc.mx == m ? (uint64_t)(uint32_t)(0x7FFFFFFF - acc.bi) : 0ull;
+    out.a = 0x7FFFFFFF - (int)(uint32_t)block_max_u64(cand, sh.uscr);
+    out.mode = kModeAll;
+    out.nkeep = V;
+    out.zk = out.zn = Z;
+    if (d_ok) {
+      const float xd = Vec<DT>::load1(row, d);
+      pd = exp(((double)xd - (double)m) / Td) / Z;
+    }
+  } else if (buf_mode) {
+    __syncthreads();
+    int n = sh.count;
+    const bool ovf = sh.overflow != 0 || n > kCap;
+    if (ovf || n < keep && n < V) {
+      exact = true;
+    } else {
+      if (n > keep && k_eff < V) {
+        compact_top(sh, n, keep);
+        n = keep;
+      }
+      sort_desc(sh, n);
+      // fp64 weights and prefix masses over contiguous per-thread chunks
+      const int ch = (n + kBlock - 1) / kBlock;
+      const int t0 = tid * ch;
+      double loc = 0.0;
+      for (int t = t0; t < t0 + ch && t < n; ++t)
+        loc += exp(((double)entry_val(sh.buf[t]) - (double)m) / Td);
+      double total;
+      const double base = block_exclusive_sum_d(loc, sh.dscr, &total);
+      const double zk = k_eff < V ? total : Z;
+      const double target = topp_on ? (double)P * zk : 2.0 * total + 1.0;
+      // kept count: entries whose exclusive prefix mass is below the target
+      int kept_loc = 0;
+      double run = base;
+      for (int t = t0; t < t0 + ch && t < n; ++t) {
+        const double w = exp(((double)entry_val(sh.buf[t]) - (double)m) / Td);
+        if (run < target) ++kept_loc;
+        run += w;
+      }
+      int nkeep = block_sum_i(kept_loc, sh.iscr);
+      if (nkeep < 1) nkeep = 1;
+      if (topp_on && k_eff == V && total < target) {
+        exact = true;  // the buffer does not reach the top-p mass
+      } else {
+        // Z_N = prefix mass through entry nkeep-1
+        if (tid == 0) { sh.zn_shared = 0.0; sh.found = -1; }
+        __syncthreads();
+        run = base;
+        for (int t = t0; t < t0 + ch && t < n; ++t) {
+          const double w = exp(((double)entry_val(sh.buf[t]) - (double)m) / Td);
+          run += w;
+          if (t == nkeep - 1) sh.zn_shared = run;
+          if (d_ok && t < nkeep && entry_idx(sh.buf[t]) == d) sh.found = t;
+        }
+        __syncthreads();
+        const double zn = sh.zn_shared;
+        const int fd = sh.found;
+        out.a = entry_idx(sh.buf[0]);
+        out.zk = zk;
+        out.zn = zn;
+        out.nkeep = nkeep;
+        if (fd >= 0) pd = exp(((double)entry_val(sh.buf[fd]) - (double)m) / Td) / zn;
+        if (nkeep <= kListCap) {
+          out.mode = kModeList;
+          ListEntry* L = A.list + (size_t)i * kListCap;
+          for (int t = tid; t < nkeep; t += kBlock) {
+            const uint64_t v = sh.buf[t];
+            ListEntry le;
+            le.idx = entry_idx(v);
+            le.x = entry_val(v);
+            L[t] = le;
+          }
+        } else {
+          out.mode = kModeRange;
+          const uint32_t bkey = (uint32_t)(sh.buf[nkeep - 1] >> 32);
+          int ties = 0;
+          for (int t = tid; t < nkeep; t += kBlock) ties += ((uint32_t)(sh.buf[t] >> 32) == bkey);
+          out.bkey = bkey;
+          out.nb = block_sum_i(ties, sh.iscr);
+        }
+      }
+    }
+  }
+
+  if (exact) {
+    // resolved by resolve_pending(): the multi-pass exact path needs more
+    // registers than the streaming kernel should carry
+    out.mode = kModePending;
+    if (tid == 0) *rec = out;
+    return;
+  }
+
+  if (tested) {
+    out.flags |= kRecTested;
+    out.pd = (float)pd;
+    if (!d_ok) {
+      out.flags |= kRecBadDraft;
+    } else {
+      const double q = (double)A.draft_probs[(size_t)i * (size_t)A.ld_q + d];
+      const double ratio = q > 0.0 ? fmin(1.0, pd / q) : (pd > 0.0 ? 1.0 : 0.0);
+      const double u = accept_uniform(A.seed, rid, pos0 + (uint32_t)j);
+      if (u < ratio) out.flags |= kRecAccept;
+    }
+  }
+  if (tid == 0) *rec = out;
+}
+
+__global__ __launch_bounds__(kBlock) void row_pass_kernel(VerifyArgs A) {
+  __shared__ RowShared sh;
+  if (A.dtype == 1) row_pass<1>(A, sh);
+  else row_pass<0>(A, sh);
+}
+
+// ------------------------------------------------------ pending rows
+// Exact kept set of a row the streaming pass could not settle (candidate
+// overflow, a top-p mass beyond the buffer, or top-k above the buffer), then
+// p(d) and the ratio test of its draft.  Rewrites the row record.
+template <int DT>
+__device__ void resolve_pending(const VerifyArgs& A, int i, int r, int j, bool tested,
+                                RowShared& sh) {
+  RowRec out = A.rec[i];
+  const int V = A.vocab;
+  const float T = A.temperature ? A.temperature[r] : 0.0f;
+  const int k = A.top_k ? A.top_k[r] : 0;
+  const float P = A.top_p ? A.top_p[r] : 1.0f;
+  int k_eff = (k > 0 && k < V) ? k : V;
+  bool topp_on = P < 1.0f;
+  if (!(P > 0.0f) && !(P != P)) {
+    k_eff = 1;
+    topp_on = false;
+  }
+  const void* row = (const char*)A.logits + (size_t)i * (size_t)A.ld_logits * (DT == 1 ? 2 : 4);
+  const int d = tested ? A.draft_tokens[i] : -1;
+  const bool d_ok = d >= 0 && d < V;
+  const float xd = d_ok ? Vec<DT>::load1(row, d) : 0.0f;
+  ExactOut eo;
+  exact_kept_set<DT>(row, V, out.m, T, k_eff, topp_on ? P : 1.0f, d_ok ? d : -1, xd, sh, eo);
+  out.mode = kModeRange;
+  out.a = eo.argmax;
+  out.bkey = eo.bkey;
+  out.nb = eo.nb;
+  out.nkeep = eo.nkeep;
+  out.zk = eo.zk;
+  out.zn = eo.zn;
+  out.flags |= kRecExact;
+  double pd = 0.0;
+  if (d_ok) {
+    const uint32_t kd = fkey(xd);
+    const bool in = kd > eo.bkey || (kd == eo.bkey && eo.tie_d < eo.nb);
+    pd = in ? exp(((double)xd - (double)out.m) / (double)T) / eo.zn : 0.0;
+  }
+  if (tested) {
+    out.flags |= kRecTested;
+    out.pd = (float)pd;
+    if (!d_ok) {
+      out.flags |= kRecBadDraft;
+    } else {
+      const uint32_t rid = A.request_id ? A.request_id[r] : (uint32_t)r;
+      const uint32_t pos0 = A.position0 ? A.position0[r] : 0u;
+      const double q = (double)A.draft_probs[(size_t)i * (size_t)A.ld_q + d];
+      const double ratio = q > 0.0 ? fmin(1.0, pd / q) : (pd > 0.0 ? 1.0 : 0.0);
+      const double u = accept_uniform(A.seed, rid, pos0 + (uint32_t)j);
+      if (u < ratio) out.flags |= kRecAccept;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) A.rec[i] = out;
+  __threadfence_block();
+  __syncthreads();
+}
+
+// ----------------------------------------------------------------- races
+// Exponential race: winner = argmax over weight_v / E_v, E_v = -ln U_v; ties
+// go to the lower id.  Reduces (key, id) pairs across the block.
+struct RaceBest {
+  double key;
+  int id;
+};
+__device__ __forceinline__ bool race_better(double k1, int i1, double k2, int i2) {
+  return k1 > k2 || (k1 == k2 && i1 < i2);
+}
+__device__ inline RaceBest block_race_best(RaceBest b, RowShared& sh) {
+#pragma unroll
+  for (int dd = 32; dd >= 1; dd >>= 1) {
+    const double ok = __shfl_xor(b.key, dd, 64);
+    const int oi = __shfl_xor(b.id, dd, 64);
+    if (race_better(ok, oi, b.key, b.id)) { b.key = ok; b.id = oi; }
+  }
+  __syncthreads();
+  if (lane_id() == 0) {
+    sh.dscr[wave_id()] = b.key;
+    sh.iscr[wave_id()] = b.id;
+  }
+  __syncthreads();
+  RaceBest r = {sh.dscr[0], sh.iscr[0]};
+  for (int w = 1; w < kWaves; ++w)
+    if (race_better(sh.dscr[w], sh.iscr[w], r.key, r.id)) { r.key = sh.dscr[w]; r.id = sh.iscr[w]; }
+  __syncthreads();
+  return r;
+}
+
+__device__ __forceinline__ double race_e(uint64_t seed, uint32_t rid, uint32_t pos, uint32_t v) {
+  return -log(race_uniform(seed, rid, pos, 1u, v));
+}
+
+// fp32 screening bound for the stream race: |log2 key_32 - log2 key| < kEta.
+constexpr float kEta = 0.0078125f;     // 2^-7, in log2 units
+constexpr float kRelP = 1.0e-4f;       // relative error bound of p_32
+constexpr int kSlots = 8;              // candidate slots per thread
+
+__device__ __forceinline__ float race_log2e32(uint64_t seed, uint32_t rid, uint32_t pos,
+                                              uint32_t v) {
+  const uint32_t w = race_word(seed, rid, pos, 1u, v);
+  const float U = (float)(2u * (w >> 9) + 1u) * 0x1.0p-24f;
+  const float E = U > 0.5f ? -log1pf(-(1.0f - U)) : -logf(U);
+  return log2f(E);
+}
+
+// Race over the whole row (kModeAll / kModeRange), weights p (residual=false)
+// or max(0, p - q).  Returns id (-1 when every weight is zero).
+template <int DT>
+__device__ int stream_race(const void* row, int V, const RowRec& rr, float T, const float* qrow,
+                           bool residual, uint64_t seed, uint32_t rid, uint32_t pos,
+                           RowShared& sh) {
+  const float c = kLog2e / T;
+  const double Td = T;
+  const float l2zn = (float)log2(rr.zn);
+  const bool range = rr.mode == kModeRange;
+  const uint32_t bkey = rr.bkey;
+  const int nb = rr.nb;
+  int* slot_id = (int*)sh.buf;                       // [kBlock * kSlots]
+  float* slot_up = (float*)(slot_id + kBlock * kSlots);
+  int nslot = 0;
+  float best_lo = -INFINITY;
+  const int tid = threadIdx.x;
+  auto visit = [&](float x, int v, int rank) {
+    const uint32_t key = fkey(x);
+    const bool in = !range || key > bkey || (key == bkey && rank < nb);
+    if (!in) return;
+    const float y = (x - rr.m) * c;          // log2 of the weight relative to the max
+    float lo, up;
+    if (!residual) {
+      if (!(y > -1.0e30f)) return;
+      const float l2e = race_log2e32(seed, rid, pos, (uint32_t)v);
+      const float kap = y - l2e;
+      lo = kap - kEta;
+      up = kap + kEta;
+    } else {
+      const float p32 = exp2f(y - l2zn);
+      const float q = qrow[v];
+      const float rhi = p32 * (1.0f + kRelP) - q;
+      if (!(rhi > 0.0f)) return;
+      const float rlo = p32 * (1.0f - kRelP) - q;
+      const float l2e = race_log2e32(seed, rid, pos, (uint32_t)v);
+      up = log2f(rhi) - l2e + kEta;
+      lo = rlo > 0.0f ? log2f(rlo) - l2e - kEta : -INFINITY;
+    }
+    if (up >= best_lo) {
+      if (nslot == kSlots) {
+        // drop slots that can no longer win
+        const float bl = fmaxf(best_lo, lo);
+        int w = 0;
+        for (int s2 = 0; s2 < kSlots; ++s2) {
+          const int sid = slot_id[tid * kSlots + s2];
+          const float su = slot_up[tid * kSlots + s2];
+          if (su >= bl) {
+            slot_id[tid * kSlots + w] = sid;
+            slot_up[tid * kSlots + w] = su;
+            ++w;
+          }
+        }
+        nslot = w;
+      }
+      if (nslot < kSlots) {
+        slot_id[tid * kSlots + nslot] = v;
+        slot_up[tid * kSlots + nslot] = up;
+        ++nslot;
+      } else {
+        // more than kSlots candidates within the screening band of each other:
+        // replace the smallest upper bound
+        int ws = 0;
+        for (int s2 = 1; s2 < kSlots; ++s2)
+          if (slot_up[tid * kSlots + s2] < slot_up[tid * kSlots + ws]) ws = s2;
+        if (slot_up[tid * kSlots + ws] < up) {
+          slot_id[tid * kSlots + ws] = v;
+          slot_up[tid * kSlots + ws] = up;
+        }
+      }
+    }
+    best_lo = fmaxf(best_lo, lo);
+  };
+  if (range) {
+    for_each_element_ranked<DT>(row, V, [&](float x) { return fkey(x) == bkey; }, visit, sh);
+  } else {
+    for_each_element<DT>(row, V, [&](float x, int v) { visit(x, v, 0); });
+  }
+  // block-wide best lower bound, then exact fp64 keys of the slots above it
+  const float B = block_max_f(best_lo, sh.fscr);
+  RaceBest b = {-1.0, 0x7FFFFFFF};
+  for (int s2 = 0; s2 < nslot; ++s2) {
+    if (slot_up[tid * kSlots + s2] < B) continue;
+    const int v = slot_id[tid * kSlots + s2];
+    const double x = (double)Vec<DT>::load1(row, v);
+    double wgt = exp((x - (double)rr.m) / Td) / rr.zn;
+    if (residual) wgt = wgt - (double)qrow[v];
+    if (!(wgt > 0.0)) continue;
+    const double key = wgt / race_e(seed, rid, pos, (uint32_t)v);
+    if (race_better(key, v, b.key, b.id)) { b.key = key; b.id = v; }
+  }
+  __syncthreads();
+  RaceBest w = block_race_best(b, sh);
+  return w.key > 0.0 ? w.id : -1;
+}
+
+// Race over an explicit kept list (kModeList), fp64 throughout.
+__device__ int list_race(const ListEntry* L, const RowRec& rr, float T, const float* qrow,
+                         bool residual, uint64_t seed, uint32_t rid, uint32_t pos, RowShared& sh) {
+  const double Td = T;
+  RaceBest b = {-1.0, 0x7FFFFFFF};
+  for (int t = threadIdx.x; t < rr.nkeep; t += kBlock) {
+    const ListEntry le = L[t];
+    double wgt = exp(((double)le.x - (double)rr.m) / Td) / rr.zn;
+    if (residual) wgt = wgt - (double)qrow[le.idx];
+    if (!(wgt > 0.0)) continue;
+    const double key = wgt / race_e(seed, rid, pos, (uint32_t)le.idx);
+    if (race_better(key, le.idx, b.key, b.id)) { b.key = key; b.id = le.idx; }
+  }
+  RaceBest w = block_race_best(b, sh);
+  return w.key > 0.0 ? w.id : -1;
+}
+
+// ------------------------------------------------------- finalize kernel
+template <int DT>
+__device__ void finalize(const VerifyArgs& A, RowShared& sh) {
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int s = A.qo[r], e = A.qo[r + 1];
+  const int nr = e - s;
+  if (nr <= 0) {
+    if (tid == 0) {
+      A.accept_len[r] = 0;
+      A.next_token[r] = -1;
+    }
+    return;
+  }
+  const int gamma = nr - 1;
+  int cap_eff = gamma;
+  if (A.verify_cap) {
+    int cv = A.verify_cap[r];
+    cap_eff = cv < 0 ? 0 : (cv > gamma ? gamma : cv);
+  }
+  // rows of this request the streaming pass left to the exact path
+  for (int j = 0; j <= cap_eff; ++j) {
+    if (A.rec[s + j].mode == kModePending) resolve_pending<DT>(A, s + j, r, j, j < cap_eff, sh);
+  }
+  // accepted prefix: first row j < cap_eff whose test rejected (wave 0 ballots)
+  if (wave_id() == 0) {
+    int L = cap_eff;
+    for (int j0 = 0; j0 < cap_eff; j0 += 64) {
+      const int j = j0 + lane_id();
+      const bool rej = j < cap_eff && !(A.rec[s + j].flags & kRecAccept);
+      const uint64_t mk = __ballot(rej);
+      if (mk) {
+        L = j0 + __ffsll((unsigned long long)mk) - 1;
+        break;
+      }
+    }
+    if (lane_id() == 0) sh.found = L;
+  }
+  __syncthreads();
+  const int L = sh.found;
+  const int is = s + L;
+  const RowRec rr = A.rec[is];
+  const bool rejected = L < cap_eff;
+  const bool bad = rejected && (rr.flags & kRecBadDraft);
+  const float T = A.temperature ? A.temperature[r] : 0.0f;
+  const uint32_t rid = A.request_id ? A.request_id[r] : (uint32_t)r;
+  const uint32_t pos = (A.position0 ? A.position0[r] : 0u) + (uint32_t)L;
+  int sample;
+  bool resid_empty = false;
+  if (rr.mode == kModeGreedy) {
+    sample = rr.a;
+  } else {
+    const void* row = (const char*)A.logits + (size_t)is * (size_t)A.ld_logits * (DT == 1 ? 2 : 4);
+    const float* qrow = A.draft_probs ? A.draft_probs + (size_t)is * (size_t)A.ld_q : nullptr;
+    const bool residual = rejected && !bad;
+    if (rr.mode == kModeList) {
+      const ListEntry* Lst = A.list + (size_t)is * kListCap;
+      sample = list_race(Lst, rr, T, qrow, residual, A.seed, rid, pos, sh);
+      if (residual && sample < 0) {
+        resid_empty = true;
+        sample = list_race(Lst, rr, T, qrow, false, A.seed, rid, pos, sh);
+      }
+    } else {
+      sample = stream_race<DT>(row, A.vocab, rr, T, qrow, residual, A.seed, rid, pos, sh);
+      if (residual && sample < 0) {
+        resid_empty = true;
+        sample = stream_race<DT>(row, A.vocab, rr, T, qrow, false, A.seed, rid, pos, sh);
+      }
+    }
+  }
+  for (int j = tid; j < nr; j += kBlock) {
+    const int i = s + j;
+    A.out_tokens[i] = j < L ? A.draft_tokens[i] : (j == L ? sample : -1);
+    if (A.row_flags) {
+      uint8_t f = 0;
+      if (j < cap_eff && (A.rec[i].flags & kRecAccept)) f |= 1;
+      if (j == L) f |= 2;
+      if (j == L && resid_empty) f |= 32;
+      A.row_flags[i] = f;
+    }
+  }
+  if (tid == 0) {
+    A.accept_len[r] = L;
+    A.next_token[r] = sample;
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void finalize_kernel(VerifyArgs A) {
+  __shared__ RowShared sh;
+  if (A.dtype == 1) finalize<1>(A, sh);
+  else finalize<0>(A, sh);
+}
+
+// ---------------------------------------------------- build outputs kernel
+template <int DT>
+__device__ void build_out(const VerifyArgs& A, const BuildOutArgs& B, RowShared& sh) {
+  const int i = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int V = A.vocab;
+  const int r = row_to_request(A.qo, A.num_requests, i);
+  if (A.rec[i].mode == kModePending) resolve_pending<DT>(A, i, r, i - A.qo[r], false, sh);
+  const RowRec rr = A.rec[i];
+  const float T = A.temperature ? A.temperature[r] : 0.0f;
+  const void* row = (const char*)A.logits + (size_t)i * (size_t)A.ld_logits * (DT == 1 ? 2 : 4);
+  if (tid == 0) {
+    if (B.row_max) B.row_max[i] = rr.m;
+    if (B.row_argmax) B.row_argmax[i] = rr.a;
+    if (B.row_lse) B.row_lse[i] = rr.lse;
+    if (B.kept_count) B.kept_count[i] = rr.nkeep;
+  }
+  // kept ids in order
+  if (B.kept_idx && B.kmax > 0) {
+    int32_t* out = B.kept_idx + (size_t)i * B.kmax;
+    const int nk = rr.nkeep < B.kmax ? rr.nkeep : B.kmax;
+    if (rr.mode == kModeGreedy) {
+      for (int t = tid; t < B.kmax; t += kBlock) out[t] = t == 0 ? rr.a : -1;
+    } else if (rr.mode == kModeList) {
+      const ListEntry* L = A.list + (size_t)i * kListCap;
+      for (int t = tid; t < B.kmax; t += kBlock) out[t] = t < nk ? L[t].idx : -1;
+    } else {
+      // the first nk kept ids are the best nk of the row: stream once more
+      const float c = kLog2e / T;
+      StreamAcc acc;
+      stream_row<DT, true, false, false>(row, V, c, nk, sh, acc);
+      __syncthreads();
+      int n = sh.count;
+      if (n > nk) {
+        compact_top(sh, n, nk);
+        n = nk;
+      }
+      sort_desc(sh, n);
+      for (int t = tid; t < B.kmax; t += kBlock) out[t] = t < nk && t < n ? entry_idx(sh.buf[t]) : -1;
+      __syncthreads();
+    }
+  }
+  // dense probabilities
+  if (B.probs) {
+    float* prow = B.probs + (size_t)i * (size_t)B.ld_probs;
+    const double Td = T;
+    if (rr.mode == kModeGreedy) {
+      for (int v = tid; v < V; v += kBlock) prow[v] = v == rr.a ? 1.0f : 0.0f;
+    } else if (rr.mode == kModeList) {
+      for (int v = tid; v < V; v += kBlock) prow[v] = 0.0f;
+      __syncthreads();
+      const ListEntry* L = A.list + (size_t)i * kListCap;
+      for (int t = tid; t < rr.nkeep; t += kBlock) {
+        const ListEntry le = L[t];
+        prow[le.idx] = (float)(exp(((double)le.x - (double)rr.m) / Td) / rr.zn);
+      }
+    } else if (rr.mode == kModeAll) {
+      for_each_element<DT>(row, V, [&](float x, int v) {
+        prow[v] = (float)(exp(((double)x - (double)rr.m) / Td) / rr.zn);
+      });
+    } else {
+      const uint32_t bkey = rr.bkey;
+      const int nb = rr.nb;
+      for_each_element_ranked<DT>(
+          row, V, [&](float x) { return fkey(x) == bkey; },
+          [&](float x, int v, int rank) {
+            const uint32_t key = fkey(x);
+            const bool in = key > bkey || (key == bkey && rank < nb);
+            prow[v] = in ? (float)(exp(((double)x - (double)rr.m) / Td) / rr.zn) : 0.0f;
+          },
+          sh);
+    }
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void build_out_kernel(VerifyArgs A, BuildOutArgs B) {
+  __shared__ RowShared sh;
+  if (A.dtype == 1) build_out<1>(A, B, sh);
+  else build_out<0>(A, B, sh);
+}
+
+}  // namespace sv

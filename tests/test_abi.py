@@ -1,0 +1,100 @@
+"""The C-ABI library builds, loads without a GPU, exports every symbol the
+header declares, and rejects host-detectable misuse with status codes (no
+kernel is launched on those paths)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spec_verify.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from rejection_sampling_amd import binding, build
+    if not os.path.exists(binding.LIB_PATH):
+        build.build()
+    return binding.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(spec_verify_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_four_calls():
+    names = declared_functions()
+    for n in ("spec_verify_build_target_probs", "spec_verify_rejection_sample",
+              "spec_verify_plan_windows", "spec_verify_accept_prefix"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_binding_lists_every_export(lib):
+    from rejection_sampling_amd import binding
+    assert sorted(binding.EXPORTS) == declared_functions()
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -4, -5):
+        assert lib.spec_verify_status_string(code)
+
+
+def test_host_validation_without_gpu(lib):
+    """Bad arguments are refused before anything touches the device."""
+    from rejection_sampling_amd.binding import Sampling
+    sp = Sampling(None, None, None, None, None, 0, 0)
+    fake = ctypes.c_void_p(0x10000)   # never dereferenced: validation fails first
+    ws = ctypes.c_void_p(0x100000)
+    # ld < vocab
+    rc = lib.spec_verify_rejection_sample(fake, 1, 10, 20, fake, 1, 2, fake, fake, 20, None,
+                                          ctypes.byref(sp), fake, fake, fake, None, ws, 1 << 20,
+                                          None)
+    assert rc == -2
+    # unknown dtype
+    rc = lib.spec_verify_rejection_sample(fake, 7, 20, 20, fake, 1, 2, fake, fake, 20, None,
+                                          ctypes.byref(sp), fake, fake, fake, None, ws, 1 << 20,
+                                          None)
+    assert rc == -3
+    # draft_probs NULL without the all-greedy hint
+    rc = lib.spec_verify_rejection_sample(fake, 1, 20, 20, fake, 1, 2, fake, None, 20, None,
+                                          ctypes.byref(sp), fake, fake, fake, None, ws, 1 << 20,
+                                          None)
+    assert rc == -1
+    # workspace too small
+    rc = lib.spec_verify_rejection_sample(fake, 1, 20, 20, fake, 1, 2, fake, fake, 20, None,
+                                          ctypes.byref(sp), fake, fake, fake, None, ws, 16, None)
+    assert rc == -4
+    assert b"workspace" in lib.spec_verify_last_error()
+    # misaligned bf16 pointer
+    rc = lib.spec_verify_rejection_sample(ctypes.c_void_p(0x10001), 1, 20, 20, fake, 1, 2, fake,
+                                          fake, 20, None, ctypes.byref(sp), fake, fake, fake,
+                                          None, ws, 1 << 20, None)
+    assert rc == -3
+    # planner: R * block overflow, NULL qo
+    rc = lib.spec_verify_plan_windows(fake, 1 << 20, 1 << 20, 1 << 12, 5, fake, fake, None, ws,
+                                      1 << 20, None)
+    assert rc == -2
+    rc = lib.spec_verify_plan_windows(fake, 4, 2, 4, 5, fake, None, None, ws, 1 << 20, None)
+    assert rc == -1
+    # build: kmax above the list capacity
+    rc = lib.spec_verify_build_target_probs(fake, 1, 20, 2, 20, fake, 1, ctypes.byref(sp), None,
+                                            0, None, None, None, None, fake, 5000, ws, 1 << 20,
+                                            None)
+    assert rc == -2
+    # empty batches are no-ops
+    assert lib.spec_verify_accept_prefix(None, None, 0, None, None, None) == 0
+
+
+def test_workspace_query_grows_with_rows(lib):
+    a = lib.spec_verify_workspace_bytes(10, 1000, 2, 0)
+    b = lib.spec_verify_workspace_bytes(1000, 1000, 2, 0)
+    c = lib.spec_verify_workspace_bytes(10, 1000, 256, 16)
+    assert 0 < a < b and a < c and a % 256 == 0

@@ -1,0 +1,309 @@
+"""GPU parity of the verify step against the CPU oracle (through the C ABI).
+
+Small cases compare every row; the five workloads run at their full sizes on
+the GPU and are compared with the oracle on sampled requests (each computed
+by the oracle on its own: results are keyed by request id and position, so a
+request's result does not depend on its batch), plus properties that hold for
+every request.  Tolerances: integers bit-exact; probabilities 1e-5 relative;
+lse 1e-4 absolute; decision mismatches only on oracle-flagged near ties.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import svref
+from rejection_sampling_amd import workloads as W
+from tests.gpu_common import (compare_build, compare_verify, dev_f32, dev_i32, dev_logits,
+                              gpu_verify, make_drafts, oracle_verify, params_for, progress)
+
+pytestmark = pytest.mark.gpu
+
+THREADS = min(16, os.cpu_count() or 1)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from rejection_sampling_amd import binding
+    binding.load()   # fails loudly when the library is missing
+    yield
+
+
+# ------------------------------------------------------------ small cases
+GRID = [
+    # (T, k, P)
+    (0.0, 0, 1.0), (0.8, 0, 1.0), (0.8, 0, 0.9), (1.0, 20, 0.95), (0.7, 50, 0.9),
+    (1.3, 5, 1.0), (0.5, 1, 0.5), (1.0, 2000, 0.9), (1.1, 3000, 1.0), (0.9, 0, 0.0),
+    (1.2, 1024, 0.97), (0.6, 0, 0.5),
+]
+
+
+def _small(seed, V, dtype=W.BF16, R=24, sigma=3.0, peak=0.0):
+    g = np.random.default_rng(seed)
+    gam = g.integers(0, 8, size=R)
+    choice = g.integers(0, len(GRID), size=R)
+    T = np.array([GRID[c][0] for c in choice], np.float32)
+    k = np.array([GRID[c][1] for c in choice], np.int32)
+    P = np.array([GRID[c][2] for c in choice], np.float32)
+    return W.small_prob_workload(seed, R, gam, V, sigma=sigma, T=T, k=k, P=P, dtype=dtype,
+                                 peak=peak)
+
+
+def _run_small(w, verify_cap=None, label=""):
+    qo = w.qo_indptr()
+    q, d = make_drafts(w, qo, THREADS)
+    progress(f"{label}: rows={w.num_rows} V={w.vocab} dtype={w.dtype}")
+    gpu = gpu_verify(w, qo, d, q, verify_cap)
+    ref = oracle_verify(w, qo, d, q, verify_cap, threads=THREADS)
+    compare_verify(gpu, ref, qo, cap=verify_cap, label=label)
+    # structural properties
+    for r in range(w.num_requests):
+        s, e = qo[r], qo[r + 1]
+        L = gpu["accept_len"][r]
+        assert 0 <= L <= e - s - 1
+        assert gpu["out_tokens"][s + L] == gpu["next_token"][r]
+        assert np.all(gpu["out_tokens"][s + L + 1:e] == -1)
+        assert 0 <= gpu["next_token"][r] < w.vocab
+    return gpu, ref
+
+
+@pytest.mark.parametrize("V", [20007, 32000, 4099])
+def test_small_grid_bf16(V):
+    _run_small(_small(11 + V, V), label=f"bf16 grid V={V}")
+
+
+def test_small_grid_fp32():
+    _run_small(_small(5, 9001, dtype=W.F32), label="fp32 grid")
+
+
+def test_small_grid_peaked_bf16():
+    _run_small(_small(6, 50000, sigma=4.0, peak=8.0), label="peaked bf16 grid")
+
+
+def test_verify_cap():
+    w = _small(7, 12003)
+    g = np.random.default_rng(1)
+    cap = np.array([g.integers(-1, x + 2) for x in w.rows_per_request], np.int32)
+    _run_small(w, verify_cap=cap, label="verify_cap")
+
+
+def test_tiny_vocabularies():
+    for V in (1, 2, 3, 64, 255):
+        _run_small(_small(100 + V, V, R=16), label=f"tiny V={V}")
+
+
+def test_ties_and_quantized_logits():
+    """Integer-valued logits: massive ties at the top-k / top-p boundaries and
+    top-p rows whose mass lies beyond the candidate buffer (exact path)."""
+    w = _small(8, 20000, R=20)
+    g = np.random.default_rng(8)
+    x = g.integers(0, 8, size=w.logits.shape).astype(np.float32)
+    w.logits = W.bf16_bits(x)
+    w.draft_logits = W.bf16_bits(x + g.integers(0, 2, size=x.shape).astype(np.float32))
+    _run_small(w, label="quantized ties")
+
+
+def test_minus_inf_and_bad_drafts():
+    w = _small(9, 3000, dtype=W.F32, R=16)
+    x = W.bf16_to_f32(w.logits) if w.dtype == W.BF16 else w.logits
+    x = x.copy()
+    x[:, ::7] = -np.inf
+    w.logits = x
+    qo = w.qo_indptr()
+    q, d = make_drafts(w, qo, THREADS)
+    d = d.copy()
+    d[1::5] = -1
+    d[2::9] = w.vocab + 3
+    gpu = gpu_verify(w, qo, d, q)
+    ref = oracle_verify(w, qo, d, q, threads=THREADS)
+    compare_verify(gpu, ref, qo, label="-inf / bad drafts")
+
+
+def test_all_greedy_without_draft_probs():
+    w = W.workload1()
+    qo = w.qo_indptr()
+    am = svref.parallel_argmax(w.logits, qo)
+    d = np.where(w.replace_mask, w.replace_ids, am).astype(np.int32)
+    gpu = gpu_verify(w, qo, d, None, all_greedy=True)
+    ref = oracle_verify(w, qo, d, None)
+    for key in ("accept_len", "next_token", "out_tokens"):
+        assert np.array_equal(gpu[key], ref[key]), key
+
+
+# ------------------------------------------------------- build outputs
+@pytest.mark.parametrize("dtype", [W.BF16, W.F32])
+def test_build_target_probs(dtype):
+    w = _small(12, 10007, dtype=dtype, R=20)
+    qo = w.qo_indptr()
+    kmax = 64
+    progress(f"build_target_probs dtype={dtype}")
+    from rejection_sampling_amd import binding as B
+    out = B.build_target_probs(dev_logits(w.logits), dev_i32(qo), params_for(w), want_probs=True,
+                               kmax=kmax)
+    torch.cuda.synchronize()
+    gpu = {k: (v.cpu().numpy() if v is not None else None) for k, v in out.items()}
+    ref = svref.build_target_probs(w.logits, qo, w.temperature, w.top_k, w.top_p, w.request_id,
+                                   w.position0, w.seed, want_probs=True, kmax=kmax)
+    compare_build(gpu, ref, ref["row_flags"], qo, w.temperature, kmax, label="build")
+
+
+# ------------------------------------------------------------ workloads
+def test_workload1_greedy():
+    w = W.workload1()
+    qo = w.qo_indptr()
+    am = svref.parallel_argmax(w.logits, qo)
+    d = np.where(w.replace_mask, w.replace_ids, am).astype(np.int32)
+    q = np.zeros((w.num_rows, w.vocab), np.float32)
+    q[np.arange(w.num_rows), np.clip(d, 0, w.vocab - 1)] = 1.0
+    progress("workload 1 greedy 4x5 V=1024 fp32")
+    gpu = gpu_verify(w, qo, d, q)
+    ref = oracle_verify(w, qo, d, q)
+    for key in ("accept_len", "next_token", "out_tokens"):
+        assert np.array_equal(gpu[key], ref[key]), key
+    assert np.array_equal(gpu["row_flags"] & 3, ref["row_flags"] & 3)
+
+
+def test_workload2_full():
+    w = W.workload2()
+    qo = w.qo_indptr()
+    q, d = make_drafts(w, qo, THREADS)
+    progress("workload 2 16x6 V=32000")
+    gpu = gpu_verify(w, qo, d, q)
+    ref = oracle_verify(w, qo, d, q, threads=THREADS)
+    compare_verify(gpu, ref, qo, label="workload 2")
+
+
+def _big(w, qo, sample, label, cap=None):
+    progress(f"{label}: drafts by the oracle ({w.num_rows} rows)")
+    q, d = make_drafts(w, qo, THREADS)
+    progress(f"{label}: GPU verify")
+    gpu = gpu_verify(w, qo, d, q, cap)
+    progress(f"{label}: oracle on {len(sample)} sampled requests")
+    ref = oracle_verify(w, qo, d, q, cap, requests=sample, threads=THREADS)
+    mism, flags = compare_verify(gpu, ref, qo, requests=sample, cap=cap, label=label)
+    # properties of every request
+    R = w.num_requests
+    for r in range(R):
+        s, e = qo[r], qo[r + 1]
+        L = gpu["accept_len"][r]
+        assert 0 <= L <= e - s - 1
+        assert gpu["out_tokens"][s + L] == gpu["next_token"][r]
+        assert np.array_equal(gpu["out_tokens"][s:s + L], d[s:s + L])
+        assert np.all(gpu["out_tokens"][s + L + 1:e] == -1)
+        assert 0 <= gpu["next_token"][r] < w.vocab
+    progress(f"{label}: ok, mismatches={mism}, flags={flags}, "
+             f"mean accepted={gpu['accept_len'].mean():.3f}")
+    return gpu, q, d
+
+
+def test_workload3_full():
+    w = W.workload3()
+    qo = w.qo_indptr()
+    sample = np.random.default_rng(3).choice(w.num_requests, 24, replace=False)
+    _big(w, qo, sample, "workload 3 128x8 V=248320")
+
+
+def test_workload4_full():
+    w = W.workload4()
+    qo = w.qo_indptr()
+    g = np.random.default_rng(4)
+    greedy = np.nonzero(w.temperature == 0)[0]
+    classes = [np.nonzero((w.temperature > 0) & (w.top_k == k) & (w.top_p == p))[0]
+               for k in (0, 20, 50) for p in (np.float32(1.0), np.float32(0.9))]
+    sample = list(g.choice(greedy, 4, replace=False))
+    for c in classes:
+        sample += list(g.choice(c, min(4, len(c)), replace=False))
+    # the hottest top-k-off / top-p requests reach the exact path
+    hot = np.nonzero((w.top_k == 0) & (w.top_p < 1) & (w.temperature > 1.0))[0]
+    sample += list(hot[:4])
+    gpu, q, d = _big(w, qo, sorted(set(int(x) for x in sample)), "workload 4 512x8 V=129280")
+    # greedy requests of the whole batch: emitted token is the row argmax
+    x = W.bf16_to_f32(w.logits)
+    for r in greedy:
+        s = qo[r]
+        L = gpu["accept_len"][r]
+        assert gpu["next_token"][r] == int(np.argmax(x[s + L]))
+
+
+def test_workload5_planner_and_verify():
+    w = W.workload5()
+    from rejection_sampling_amd import binding as B
+    progress("workload 5 planner")
+    vl_g, qo_g, surv_g = B.plan_windows(dev_f32(w.confidence), w.budget)
+    torch.cuda.synchronize()
+    vl, qo, surv = svref.plan_windows(w.confidence, w.budget)
+    assert np.array_equal(vl_g.cpu().numpy(), vl)
+    assert np.array_equal(qo_g.cpu().numpy(), qo)
+    assert np.array_equal(surv_g.cpu().numpy().view(np.uint32), surv.view(np.uint32))
+    assert qo[-1] == w.num_rows
+    sample = np.random.default_rng(5).choice(w.num_requests, 24, replace=False)
+    _big(w, qo, sample, "workload 5 ragged 1792 rows V=248320")
+
+
+# -------------------------------------------------------------- planner
+@pytest.mark.parametrize("R,Bk", [(1, 1), (7, 3), (256, 16), (1000, 9)])
+def test_planner_matches_oracle(R, Bk):
+    from rejection_sampling_amd import binding as B
+    g = np.random.default_rng(R)
+    conf = g.random((R, Bk)).astype(np.float32)
+    conf[g.random((R, Bk)) < 0.02] = np.nan
+    conf[g.random((R, Bk)) < 0.02] = 1.5
+    for budget in (-3, 0, 1, R * Bk // 3, R * Bk - 1, R * Bk, R * Bk + 5):
+        vl_g, qo_g, surv_g = B.plan_windows(dev_f32(conf), budget)
+        vl, qo, surv = svref.plan_windows(conf, budget)
+        assert np.array_equal(vl_g.cpu().numpy(), vl), budget
+        assert np.array_equal(qo_g.cpu().numpy(), qo), budget
+        assert np.array_equal(surv_g.cpu().numpy().view(np.uint32), surv.view(np.uint32))
+    # all-equal confidences: pure index tie-break
+    conf = np.full((R, Bk), 0.5, np.float32)
+    vl_g, qo_g, _ = B.plan_windows(dev_f32(conf), (R * Bk) // 2 + 1)
+    vl, qo, _ = svref.plan_windows(conf, (R * Bk) // 2 + 1)
+    assert np.array_equal(vl_g.cpu().numpy(), vl)
+
+
+def test_accept_prefix_matches_oracle():
+    from rejection_sampling_amd import binding as B
+    g = np.random.default_rng(3)
+    R = 300
+    lens = g.integers(1, 80, size=R)
+    qo = np.zeros(R + 1, np.int32)
+    np.cumsum(lens, out=qo[1:])
+    acc = (g.random(qo[-1]) < 0.9).astype(np.uint8)
+    cap = g.integers(-2, 90, size=R).astype(np.int32)
+    for c in (None, cap):
+        got = B.accept_prefix(torch.from_numpy(acc).cuda(), dev_i32(qo),
+                              dev_i32(c) if c is not None else None).cpu().numpy()
+        assert np.array_equal(got, svref.accept_prefix(acc, qo, c))
+
+
+# -------------------------------------------------- distribution on GPU
+def test_gpu_first_token_chi_square():
+    """The GPU's first emitted token follows the target (chi-square, 10^6
+    trials of one request each, V = 64)."""
+    from scipy import stats
+    from rejection_sampling_amd import binding as B
+    g = np.random.default_rng(101)
+    V, n = 64, 1_000_000
+    x = g.normal(0, 1.5, size=(2, V)).astype(np.float32)
+    xd = (x + g.normal(0, 1.0, size=x.shape)).astype(np.float32)
+    q1 = svref.build_target_probs(xd, np.array([0, 2], np.int32), np.ones(1, np.float32),
+                                  want_probs=True)["probs"].astype(np.float32)
+    p0 = svref.build_target_probs(x[:1], np.array([0, 1], np.int32), np.ones(1, np.float32),
+                                  want_probs=True)["probs"][0]
+    qo = np.arange(n + 1, dtype=np.int32) * 2
+    rid = np.arange(n, dtype=np.uint32)
+    pos0 = np.zeros(n, np.uint32)
+    q = np.ascontiguousarray(np.broadcast_to(q1, (n, 2, V))).reshape(2 * n, V)
+    d = svref.sample_probs(q, qo, rid, pos0, 77, tag=2)
+    logits = torch.from_numpy(np.ascontiguousarray(np.broadcast_to(x, (n, 2, V))).reshape(2 * n, V)).cuda()
+    prm = B.Params(dev_f32(np.ones(n)), None, None, dev_i32(rid), dev_i32(pos0), 77)
+    progress("GPU chi-square 10^6 trials")
+    out = B.rejection_sample(logits, dev_i32(qo), dev_i32(d), dev_f32(q), prm)
+    first = out["out_tokens"].view(n, 2)[:, 0].cpu().numpy()
+    counts = np.bincount(first, minlength=V)
+    exp = n * p0
+    chi2 = ((counts - exp) ** 2 / exp).sum()
+    assert stats.chi2.sf(chi2, V - 1) > 0.01
