@@ -1,0 +1,226 @@
+#!/usr/bin/env python3
+"""Benchmark of the verify step on one MI355X.
+
+One step = one spec_verify_rejection_sample call (row pass + finalize) over
+1024 rows (128 requests x 8-token blocks) of a 248320-token vocabulary in
+bf16: temperature 1.0, top-k 20, top-p 0.95, full fp32 draft distributions
+(gathered, never streamed), residual resampling on rejection.  Inputs are
+synthetic and seeded, built on the GPU: target logits N(0, 4) with +8 at one
+seeded index per row, draft logits = target + N(0, 1), draft distributions
+built from the draft logits by the library itself, drafted tokens sampled
+from them.  Three logits sets rotate so the 256 MB Infinity Cache cannot
+serve a repeat.
+
+Prints one JSON line: whole-job rows/s; the roofline of the dominant kernel
+(the row pass: algorithmic bytes = rows x V x 2 per launch, over its mean
+launch time from HIP events recorded on the call's stream); and the CPU
+oracle timed on a bounded sample of the same workload on one host core.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0     # MI355X HBM3E, published
+R_REQ, BLOCK, VOCAB = 128, 8, 248320
+ROWS = R_REQ * BLOCK
+T, TOPK, TOPP = 1.0, 20, 0.95
+SEED = 3007
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "row_pass_traffic.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "rejection_sampling_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp", ".h")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per row-pass launch from the committed counter runs, or None
+    when the kernels changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def make_inputs(torch, B, nsets: int):
+    """nsets independent input sets (logits, draft distributions, drafts)."""
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(SEED)
+    rows = torch.arange(ROWS, device=dev)
+    qo = (torch.arange(R_REQ + 1, device=dev, dtype=torch.int32) * BLOCK).contiguous()
+    Tt = torch.full((R_REQ,), T, device=dev, dtype=torch.float32)
+    kt = torch.full((R_REQ,), TOPK, device=dev, dtype=torch.int32)
+    pt = torch.full((R_REQ,), TOPP, device=dev, dtype=torch.float32)
+    rid = torch.arange(R_REQ, device=dev, dtype=torch.int32)
+    pos0 = torch.randint(0, 4096, (R_REQ,), generator=g, device=dev, dtype=torch.int32)
+    params = B.Params(Tt, kt, pt, rid, pos0, SEED)
+    sets = []
+    for s in range(nsets):
+        x = torch.randn((ROWS, VOCAB), generator=g, device=dev, dtype=torch.float32) * 4.0
+        peak = torch.randint(0, VOCAB, (ROWS,), generator=g, device=dev)
+        x[rows, peak] += 8.0
+        logits = x.to(torch.bfloat16)
+        x += torch.randn((ROWS, VOCAB), generator=g, device=dev)
+        draft = x.to(torch.bfloat16)
+        del x
+        # draft distributions: the library's own target-probs build on the draft logits
+        q = B.build_target_probs(draft, qo, params, want_probs=True)["probs"]
+        del draft
+        drafts = torch.multinomial(q, 1, generator=g).view(-1).to(torch.int32).contiguous()
+        sets.append((logits, q, drafts))
+    torch.cuda.synchronize()
+    return sets, qo, params
+
+
+def cpu_baseline(n_requests: int):
+    """The CPU oracle as it stands, single-threaded on one host core, on a
+    bounded sample of the same workload (n_requests x 8 rows, V 248320)."""
+    import numpy as np
+    from oracle import svref
+    from rejection_sampling_amd import workloads as W
+    w = W.workload3(num_requests=n_requests)
+    qo = w.qo_indptr()
+    # inputs (untimed): draft distributions and drafted tokens by the oracle
+    q = svref.parallel_draft_probs(w.draft_logits, qo, w.temperature, w.top_k, w.top_p,
+                                   w.request_id, w.position0, w.seed)
+    d = svref.sample_probs(q, qo, w.request_id, w.position0, w.seed, tag=2)
+    try:  # the timed call runs pinned to one core
+        os.sched_setaffinity(0, {sorted(os.sched_getaffinity(0))[0]})
+    except (AttributeError, OSError):
+        pass
+    t0 = time.perf_counter()
+    svref.rejection_sample(w.logits, qo, d, q, w.temperature, w.top_k, w.top_p, w.request_id,
+                           w.position0, w.seed)
+    dt = time.perf_counter() - t0
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": round(w.num_rows / dt, 3), "unit": "rows/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n_requests} requests x {BLOCK} rows of the {ROWS} x {VOCAB} bf16 "
+                      f"workload (same recipe, generated on the host), one call, "
+                      f"{dt:.2f} s on 1 core of {os.cpu_count()} ({cpu})"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--sets", type=int, default=3, help="rotating logits buffer sets")
+    ap.add_argument("--cpu-requests", type=int, default=48,
+                    help="requests in the CPU-baseline sample (0 skips it)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 512 MiB device copy (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the verify step "
+              "shards by request with no exchange, see DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from rejection_sampling_amd import binding as B
+    B.load()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+
+    print(f"[bench] building inputs ({args.sets} logits sets)", file=sys.stderr, flush=True)
+    sets, qo, params = make_inputs(torch, B, args.sets)
+    out = {
+        "accept_len": torch.empty(R_REQ, dtype=torch.int32, device="cuda"),
+        "out_tokens": torch.empty(ROWS, dtype=torch.int32, device="cuda"),
+        "next_token": torch.empty(R_REQ, dtype=torch.int32, device="cuda"),
+        "row_flags": torch.empty(ROWS, dtype=torch.uint8, device="cuda"),
+    }
+
+    def step(i):
+        logits, q, drafts = sets[i % len(sets)]
+        B.rejection_sample(logits, qo, drafts, q, params, out=out)
+
+    if args.calibrate_copy:
+        a = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    B.profile_enable(True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    B.profile_reset()
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    n_rp, ms_rp = B.profile_read("row_pass")
+    n_fz, ms_fz = B.profile_read("finalize")
+    B.profile_enable(False)
+    ms_per_step = elapsed * 1e3 / args.steps
+    rows_per_s = ROWS / (ms_per_step * 1e-3)
+    alg_bytes = ROWS * VOCAB * 2
+    kern_ms = ms_rp / max(n_rp, 1)
+    achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
+    acc = out["accept_len"].float().mean().item()   # of the last step's set
+
+    cpu = cpu_baseline(args.cpu_requests) if args.cpu_requests > 0 else None
+    line = {
+        "metric": "verify rows/s and achieved HBM GB/s (% of peak) at 1024 rows x 248k vocab bf16",
+        "value": round(rows_per_s, 1),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "prob_128x8_v248320_bf16", "rows": ROWS, "requests": R_REQ,
+                   "vocab": VOCAB, "temperature": T, "top_k": TOPK, "top_p": TOPP,
+                   "draft_probs": "dense fp32, gathered", "logit_sets": args.sets},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": measured_traffic(),
+                     "kernel": "row_pass_kernel", "kernel_ms": round(kern_ms, 5),
+                     "algorithmic_bytes": alg_bytes,
+                     "finalize_ms": round(ms_fz / max(n_fz, 1), 5)},
+        "cpu_baseline": cpu,
+        "mean_accept_len": round(acc, 4),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -42,6 +42,7 @@ struct Prof {
   bool on = false;
   struct Rec { int id; hipEvent_t a, b; };
   std::vector<Rec> pending;
+  std::vector<hipEvent_t> pool;  // reused events (created once)
   int64_t launches[8] = {};
   double ms[8] = {};
 };
@@ -59,7 +60,14 @@ struct ProfScope {
     Prof& p = prof();
     std::lock_guard<std::mutex> g(p.mu);
     if (!p.on) return;
-    if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) return;
+    for (hipEvent_t* ev : {&a, &b}) {
+      if (!p.pool.empty()) {
+        *ev = p.pool.back();
+        p.pool.pop_back();
+      } else if (hipEventCreate(ev) != hipSuccess) {
+        return;
+      }
+    }
     (void)hipEventRecord(a, s);
     active = true;
   }
@@ -302,8 +310,8 @@ int32_t spec_verify_profile_reset(void) {
   std::lock_guard<std::mutex> g(p.mu);
   for (auto& r : p.pending) {
     (void)hipEventSynchronize(r.b);
-    (void)hipEventDestroy(r.a);
-    (void)hipEventDestroy(r.b);
+    p.pool.push_back(r.a);
+    p.pool.push_back(r.b);
   }
   p.pending.clear();
   for (int k = 0; k < 8; ++k) { p.launches[k] = 0; p.ms[k] = 0.0; }
@@ -320,8 +328,8 @@ int32_t spec_verify_profile_read(int32_t kernel_id, int64_t* launches, double* t
     (void)hipEventElapsedTime(&ms, r.a, r.b);
     p.launches[r.id] += 1;
     p.ms[r.id] += ms;
-    (void)hipEventDestroy(r.a);
-    (void)hipEventDestroy(r.b);
+    p.pool.push_back(r.a);
+    p.pool.push_back(r.b);
   }
   p.pending.clear();
   if (launches) *launches = p.launches[kernel_id];

@@ -8,13 +8,32 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+// Tuning knobs of the streaming row pass (defaults are the tuned values).
+#ifndef SV_BLOCK
+#define SV_BLOCK 256        // threads per row workgroup
+#endif
+#ifndef SV_UNROLL
+#define SV_UNROLL 4         // 16-byte vectors per thread per tile
+#endif
+#ifndef SV_PREFETCH
+#define SV_PREFETCH 1       // issue the next tile's loads before consuming this one
+#endif
+#ifndef SV_NT_LOADS
+#define SV_NT_LOADS 1       // non-temporal loads for the logits stream
+#endif
+#ifndef SV_CHECK_EVERY
+#define SV_CHECK_EVERY 1    // tiles between candidate-buffer checks after the ramp
+#endif
+
 namespace sv {
 
-constexpr int kBlock = 256;               // threads per row workgroup
+constexpr int kBlock = SV_BLOCK;          // threads per row workgroup
 constexpr int kWaves = kBlock / 64;
 constexpr int kCap = 4096;                // LDS candidate buffer (64-bit entries)
-constexpr int kKeepTopP = 1536;           // candidates kept for top-k-off rows
-constexpr int kTopkFast = 1024;           // largest k on the buffer path
+constexpr int kKeepTopP = 384;            // candidates kept per wave for top-k-off rows
+constexpr int kThreshTopP = 640;          // per-wave compaction limit for those rows
+constexpr int kTopPSortCap = 1024;        // certified candidates sorted for top-p
+constexpr int kTopkFast = 256;            // largest k on the buffer path
 constexpr int kListCap = 1024;            // kept-set entries stored per row
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -117,8 +136,12 @@ __device__ __forceinline__ float entry_val(uint64_t e) { return key_to_float((ui
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 // Streaming 16-byte load (non-temporal: the logits are read once).
 __device__ __forceinline__ uint4 load_stream(const uint4* p) {
+#if SV_NT_LOADS
   const u32x4_t v = __builtin_nontemporal_load((const u32x4_t*)p);
   return make_uint4(v.x, v.y, v.z, v.w);
+#else
+  return *p;
+#endif
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

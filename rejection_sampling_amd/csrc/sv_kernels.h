@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "sv_device.hpp"
+
 namespace sv {
 
 struct RowRec;
@@ -68,7 +70,7 @@ __global__ void accept_prefix_kernel(const uint8_t* accepted, const int32_t* qo,
                                      const int32_t* verify_cap, int32_t* accept_len);
 
 // sizes shared with the host
-constexpr int kRowBlock = 256;
+constexpr int kRowBlock = SV_BLOCK;
 constexpr int kPlanBlock = 1024;
 constexpr size_t kRowRecBytes = 56;
 constexpr size_t kListBytesPerRow = 1024 * 8;

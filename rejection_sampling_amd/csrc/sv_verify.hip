@@ -89,7 +89,7 @@ __device__ void exact_kept_set(const void* row, int V, float m, float T, int k_e
 
   // one histogram pass over elements with key >= klo and (key & pmask) == prefix
   auto pass = [&](uint32_t prefix, uint32_t pmask, int shift, uint32_t klo) {
-    for (int b = threadIdx.x; b < 256; b += kBlock) { sh.hist[b] = 0u; mass[b] = 0ull; }
+    for (int b = threadIdx.x; b < 256; b += kBlock) { sh.whist[0][b] = 0u; mass[b] = 0ull; }
     __syncthreads();
     const bool fst = first;
     for_each_element<DT>(row, V, [&](float x, int i) {
@@ -100,7 +100,7 @@ __device__ void exact_kept_set(const void* row, int V, float m, float T, int k_e
       }
       if (key < klo || (key & pmask) != prefix) return;
       const uint32_t dg = (key >> shift) & 255u;
-      atomicAdd(&sh.hist[dg], 1u);
+      atomicAdd(&sh.whist[0][dg], 1u);
       const float w = exp2f((x - m) * c);
       atomicAdd((unsigned long long*)&mass[dg], (unsigned long long)((double)w * scale));
     });
@@ -118,7 +118,7 @@ __device__ void exact_kept_set(const void* row, int V, float m, float T, int k_e
     double cnt_above = 0.0, mass_above = 0.0;
     for (int shift = top_shift; shift >= low_shift; shift -= 8) {
       pass(prefix, pmask, shift, 0u);
-      for (int b = threadIdx.x; b < 256; b += kBlock) vals[b] = (double)sh.hist[b];
+      for (int b = threadIdx.x; b < 256; b += kBlock) vals[b] = (double)sh.whist[0][b];
       __syncthreads();
       double above;
       walk_bins(vals, cnt_above, (double)k_eff, sh, &above);
@@ -130,7 +130,7 @@ __device__ void exact_kept_set(const void* row, int V, float m, float T, int k_e
       mab = block_sum_d(threadIdx.x < 256 ? vals[threadIdx.x] : 0.0, sh.dscr);
       cnt_above = above;
       mass_above += mab;
-      cnt_bk = (int)sh.hist[dg];
+      cnt_bk = (int)sh.whist[0][dg];
       prefix |= (uint32_t)dg << shift;
       pmask |= 0xFFu << shift;
       __syncthreads();
@@ -176,7 +176,7 @@ __device__ void exact_kept_set(const void* row, int V, float m, float T, int k_e
         const int b = threadIdx.x;
         double cv = 0.0;
         if (b < 256 && b > dg) {
-          cv = (double)sh.hist[b];
+          cv = (double)sh.whist[0][b];
           if (bk_here && b == dbk) cv -= (double)excess;
         }
         cab = block_sum_d(cv, sh.dscr);
@@ -191,7 +191,7 @@ __device__ void exact_kept_set(const void* row, int V, float m, float T, int k_e
     int avail;
     {
       // ties at bp inside K
-      uint32_t hb = sh.hist[(bp >> low_shift) & 255u];
+      uint32_t hb = sh.whist[0][(bp >> low_shift) & 255u];
       avail = (int)hb;
       if (topk_on && bp == bk) avail = nbk;
     }
@@ -275,15 +275,19 @@ __device__ __forceinline__ void row_pass(const VerifyArgs& A, RowShared& sh) {
   const bool need_sum_build = A.build != 0;
   StreamAcc acc;
 
+  if (tid == 0) sh.woverflow = 0;
+  if (tid < kWaves) sh.wtau[tid] = -__int_as_float(0x7F800000);
+  __syncthreads();
+
   // ------------------------------------------------ greedy rows
   if (greedy) {
-    if (need_sum_build) stream_row<DT, false, true, true>(row, V, c, 1, sh, acc);
-    else stream_row<DT, false, false, true>(row, V, c, 1, sh, acc);
+    if (need_sum_build) stream_row<DT, false, true, true>(row, V, c, 1, 1, 0, sh, acc);
+    else stream_row<DT, false, false, true>(row, V, c, 1, 1, 0, sh, acc);
     const float m = block_max_f(acc.mx, sh.fscr);
     const uint64_t cand = acc.mx == m ? (uint64_t)(uint32_t)(0x7FFFFFFF - acc.bi) : 0ull;
     const int a = 0x7FFFFFFF - (int)(uint32_t)block_max_u64(cand, sh.uscr);
     if (need_sum_build) {
-      const double part = acc.s * (double)exp2f((acc.sref - m) * c);
+      const double part = acc.s * exp2((double)(acc.mx - m) * (double)c);
       const double Z = block_sum_d(part, sh.dscr);
       out.lse = (float)((double)m / (double)teff + log(Z));
     }
@@ -304,22 +308,34 @@ __device__ __forceinline__ void row_pass(const VerifyArgs& A, RowShared& sh) {
 
   // ------------------------------------------------ sampled rows
   const bool all_mode = k_eff == V && !topp_on;
-  const bool buf_mode = !all_mode && (k_eff <= kTopkFast || (k_eff == V && topp_on));
-  const int keep = k_eff < V ? k_eff : kKeepTopP;
-  const bool need_sum = need_sum_build || all_mode || (k_eff == V && topp_on);
-  if (all_mode) {
-    stream_row<DT, false, true, true>(row, V, c, 1, sh, acc);
-  } else if (buf_mode) {
-    if (need_sum) stream_row<DT, true, true, false>(row, V, c, keep, sh, acc);
-    else stream_row<DT, true, false, false>(row, V, c, keep, sh, acc);
+  const bool topk_mode = k_eff < V && k_eff <= kTopkFast;
+  const bool topp_mode = k_eff == V && topp_on;
+  const bool buf_mode = topk_mode || topp_mode;
+  const bool need_sum = need_sum_build || all_mode || topp_mode;
+  int keep, thresh, ramp;
+  if (topk_mode) {
+    keep = k_eff;
+    thresh = 2 * keep < 128 ? 128 : (2 * keep > 512 ? 512 : 2 * keep);
+    ramp = keep > 64 ? 1 : 0;
   } else {
-    if (need_sum) stream_row<DT, false, true, false>(row, V, c, 1, sh, acc);
-    else stream_row<DT, false, false, false>(row, V, c, 1, sh, acc);
+    keep = kKeepTopP;
+    thresh = kThreshTopP;
+    ramp = 2;
+  }
+  if (all_mode) {
+    if (need_sum_build) stream_row<DT, false, true, true>(row, V, c, 1, 1, 0, sh, acc);
+    else stream_row<DT, false, true, false>(row, V, c, 1, 1, 0, sh, acc);
+  } else if (buf_mode) {
+    if (need_sum) stream_row<DT, true, true, false>(row, V, c, keep, thresh, ramp, sh, acc);
+    else stream_row<DT, true, false, false>(row, V, c, keep, thresh, ramp, sh, acc);
+  } else {
+    if (need_sum) stream_row<DT, false, true, false>(row, V, c, 1, 1, 0, sh, acc);
+    else stream_row<DT, false, false, false>(row, V, c, 1, 1, 0, sh, acc);
   }
   const float m = block_max_f(acc.mx, sh.fscr);
   double Z = 0.0;
   if (need_sum) {
-    const double part = acc.s * (double)exp2f((acc.sref - m) * c);
+    const double part = acc.s * exp2((double)(acc.mx - m) * (double)c);
     Z = block_sum_d(part, sh.dscr);
     out.lse = (float)((double)m / (double)T + log(Z));
   }
@@ -329,8 +345,12 @@ __device__ __forceinline__ void row_pass(const VerifyArgs& A, RowShared& sh) {
   bool exact = !buf_mode && !all_mode;
 
   if (all_mode) {
-    const uint64_t cand = acc.mx == m ? (uint64_t)(uint32_t)(0x7FFFFFFF - acc.bi) : 0ull;
-    out.a = 0x7FFFFFFF - (int)(uint32_t)block_max_u64(cand, sh.uscr);
+    if (need_sum_build) {
+      const uint64_t cand = acc.mx == m ? (uint64_t)(uint32_t)(0x7FFFFFFF - acc.bi) : 0ull;
+      out.a = 0x7FFFFFFF - (int)(uint32_t)block_max_u64(cand, sh.uscr);
+    } else {
+      out.a = -1;  // not needed on the verify path
+    }
     out.mode = kModeAll;
     out.nkeep = V;
     out.zk = out.zn = Z;
@@ -339,16 +359,34 @@ __device__ __forceinline__ void row_pass(const VerifyArgs& A, RowShared& sh) {
       pd = exp(((double)xd - (double)m) / Td) / Z;
     }
   } else if (buf_mode) {
-    __syncthreads();
-    int n = sh.count;
-    const bool ovf = sh.overflow != 0 || n > kCap;
-    if (ovf || n < keep && n < V) {
+    __syncthreads();  // segments, counts and thresholds final
+    int n = 0;
+    if (sh.woverflow) {
       exact = true;
     } else {
-      if (n > keep && k_eff < V) {
-        compact_top(sh, n, keep);
-        n = keep;
+      uint64_t theta = 0ull;  // certified prefix: entries >= the largest wave threshold
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) theta = sh.wtheta[w] > theta ? sh.wtheta[w] : theta;
+      n = merge_segments(sh);
+      if (topk_mode) {
+        if (n < k_eff) {
+          exact = true;  // fewer finite candidates than k
+        } else if (n > k_eff) {
+          compact_top(sh, n, k_eff);
+          n = k_eff;
+        }
+      } else {
+        int cert = 0;
+        for (int t = tid; t < n; t += kBlock) cert += sh.buf[t] >= theta ? 1 : 0;
+        cert = block_sum_i(cert, sh.iscr);
+        const int use = cert < kTopPSortCap ? cert : kTopPSortCap;
+        if (n > use) {
+          compact_top(sh, n, use);
+          n = use;
+        }
       }
+    }
+    if (!exact) {
       sort_desc(sh, n);
       // fp64 weights and prefix masses over contiguous per-thread chunks
       const int ch = (n + kBlock - 1) / kBlock;
@@ -358,7 +396,7 @@ __device__ __forceinline__ void row_pass(const VerifyArgs& A, RowShared& sh) {
         loc += exp(((double)entry_val(sh.buf[t]) - (double)m) / Td);
       double total;
       const double base = block_exclusive_sum_d(loc, sh.dscr, &total);
-      const double zk = k_eff < V ? total : Z;
+      const double zk = topk_mode ? total : Z;
       const double target = topp_on ? (double)P * zk : 2.0 * total + 1.0;
       // kept count: entries whose exclusive prefix mass is below the target
       int kept_loc = 0;
@@ -370,8 +408,8 @@ __device__ __forceinline__ void row_pass(const VerifyArgs& A, RowShared& sh) {
       }
       int nkeep = block_sum_i(kept_loc, sh.iscr);
       if (nkeep < 1) nkeep = 1;
-      if (topp_on && k_eff == V && total < target) {
-        exact = true;  // the buffer does not reach the top-p mass
+      if (topp_mode && total < target) {
+        exact = true;  // the certified candidates do not reach the top-p mass
       } else {
         // Z_N = prefix mass through entry nkeep-1
         if (tid == 0) { sh.zn_shared = 0.0; sh.found = -1; }
@@ -780,16 +818,31 @@ __device__ void build_out(const VerifyArgs& A, const BuildOutArgs& B, RowShared&
       const ListEntry* L = A.list + (size_t)i * kListCap;
       for (int t = tid; t < B.kmax; t += kBlock) out[t] = t < nk ? L[t].idx : -1;
     } else {
-      // the first nk kept ids are the best nk of the row: stream once more
-      const float c = kLog2e / T;
-      StreamAcc acc;
-      stream_row<DT, true, false, false>(row, V, c, nk, sh, acc);
-      __syncthreads();
-      int n = sh.count;
-      if (n > nk) {
-        compact_top(sh, n, nk);
-        n = nk;
+      // the first nk kept ids are the best nk of the row: find the count
+      // boundary exactly, then collect the elements at or above it in id order
+      uint32_t bkey = 0u;
+      int nb = 0x7FFFFFFF;
+      if (nk < V) {
+        ExactOut eo;
+        exact_kept_set<DT>(row, V, rr.m, T, nk, 1.0f, -1, 0.0f, sh, eo);
+        bkey = eo.bkey;
+        nb = eo.nb;
       }
+      if (tid == 0) sh.count = 0;
+      __syncthreads();
+      for_each_element_ranked<DT>(
+          row, V, [&](float x) { return fkey(x) == bkey; },
+          [&](float x, int v, int rank) {
+            const uint32_t key = fkey(x);
+            if (key > bkey || (key == bkey && rank < nb)) {
+              const int slot = atomicAdd(&sh.count, 1);
+              if (slot < kCap) sh.buf[slot] = make_entry(x, v);
+            }
+          },
+          sh);
+      __syncthreads();
+      int n = sh.count < kCap ? sh.count : kCap;
+      __syncthreads();
       sort_desc(sh, n);
       for (int t = tid; t < B.kmax; t += kBlock) out[t] = t < nk && t < n ? entry_idx(sh.buf[t]) : -1;
       __syncthreads();
