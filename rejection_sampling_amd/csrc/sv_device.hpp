@@ -34,6 +34,8 @@ constexpr int kKeepTopP = 384;            // candidates kept per wave for top-k-
 constexpr int kThreshTopP = 640;          // per-wave compaction limit for those rows
 constexpr int kTopPSortCap = 1024;        // certified candidates sorted for top-p
 constexpr int kTopkFast = 256;            // largest k on the buffer path
+constexpr int kTopkVec = 64;              // largest k on the vector-candidate path
+constexpr int kThreshVec = 128;           // per-wave compaction limit there (>= 2 kTopkVec)
 constexpr int kListCap = 1024;            // kept-set entries stored per row
 constexpr float kLog2e = 1.4426950408889634f;
 

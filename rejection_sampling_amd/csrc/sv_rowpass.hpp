@@ -27,6 +27,13 @@
 namespace sv {
 
 constexpr int kWaveCap = kCap / kWaves;   // entries per wave segment
+// Vector-candidate rows: per wave, kVecCap entries followed by their raw
+// 16-byte vectors, in a region of kVecStride entries.
+constexpr int kVecCap = 256;
+constexpr int kVecDatOff = kVecCap;
+constexpr int kVecStride = kVecCap + 2 * kVecCap;
+static_assert(kWaves * kVecStride <= kCap, "vector segments fit the buffer");
+static_assert(kThreshVec < kVecCap, "room for a tile of appends");
 
 struct RowShared {
   uint64_t buf[kCap];               // wave segments while streaming; merged area after
@@ -37,8 +44,8 @@ struct RowShared {
   float fscr[kWaves];
   int iscr[kWaves];
   int wcount[kWaves];               // final entries per wave segment
-  uint64_t wtheta[kWaves];          // worst kept entry per wave (0: never compacted)
-  float wtau[kWaves];               // published wave thresholds (-inf before any)
+  float wtau[kWaves];               // wave thresholds (published while streaming, final after)
+  float endx[16];                   // vector-candidate rows: head (0..7) and tail (8..15) elements
   int woverflow;
   int count;
   int sel_digit, sel_need, sel_exact, found;
@@ -80,8 +87,10 @@ __device__ __forceinline__ void wave_pick_digit(const uint32_t* hist, int need, 
 }
 
 // Wave-local: the `keep` best of seg[0, n) (n > keep), compacted in place to
-// seg[0, keep).  Returns the worst kept entry.  Only this wave takes part.
-__device__ __forceinline__ uint64_t wave_compact(uint64_t* seg, uint32_t* hist, int n, int keep) {
+// seg[0, keep), moving dat[] along when given.  Returns the worst kept entry.
+// Only this wave takes part.
+__device__ __forceinline__ uint64_t wave_compact(uint64_t* seg, uint32_t* hist, int n, int keep,
+                                                 uint4* dat = nullptr) {
   const int l = lane_id();
   uint64_t prefix = 0, pmask = 0;
   int need = keep;
@@ -110,48 +119,20 @@ __device__ __forceinline__ uint64_t wave_compact(uint64_t* seg, uint32_t* hist, 
     const int e = b0 + l;
     const uint64_t v = e < n ? seg[e] : 0ull;
     const bool k = e < n && (v & pmask) >= prefix;
+    uint4 dv = make_uint4(0u, 0u, 0u, 0u);
+    if (dat && k) dv = dat[e];
     const uint64_t km = __ballot(k);
     const int off = __popcll(km & ((1ull << l) - 1ull));
     wave_lds_sync();
     if (k) {
       seg[pos0 + off] = v;
+      if (dat) dat[pos0 + off] = dv;
       mn = v < mn ? v : mn;
     }
     pos0 += __popcll(km);
     wave_lds_sync();
   }
   return wave_min_u64(mn);
-}
-
-// Wave-local exact selection for keep <= 64: every entry's rank is counted
-// against the whole segment (broadcast LDS reads), four entries per lane at a
-// time; the `keep` best go to `tmp` at their rank and then back to the front
-// of the segment, sorted.  Returns the worst kept entry.
-__device__ __forceinline__ uint64_t wave_select_small(uint64_t* seg, uint64_t* tmp, int n,
-                                                      int keep) {
-  const int l = lane_id();
-  for (int j0 = 0; j0 < n; j0 += 256) {
-    uint64_t mine[4];
-    int rank[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = j0 + 64 * j + l;
-      mine[j] = e < n ? seg[e] : 0ull;
-      rank[j] = 0;
-    }
-    for (int u = 0; u < n; ++u) {
-      const uint64_t v = seg[u];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) rank[j] += v > mine[j] ? 1 : 0;
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (j0 + 64 * j + l < n && rank[j] < keep) tmp[rank[j]] = mine[j];
-  }
-  wave_lds_sync();
-  if (l < keep) seg[l] = tmp[l];
-  wave_lds_sync();
-  return seg[keep - 1];
 }
 
 // Block level: radix select over buf[0, n): (prefix, pmask) such that exactly
@@ -281,12 +262,16 @@ struct StreamAcc {
   double s;     // sum of weights relative to exp2(mx * c)  (SUM)
 };
 
+// Per-wave candidate state.  Invariant: every element the wave has seen and
+// not kept has value <= tau, and (when it is finite and the wave kept at least
+// `keep` finite entries) `keep` kept entries that are better in (value desc,
+// id asc) order.
 struct WaveBuf {
-  int count;       // entries in the wave segment (may pass kWaveCap: overflow)
-  float tau;       // own filter: value of theta_w (NaN admits everything), strict
-  float tsh;       // shared filter: best published wave threshold, non-strict
-  uint64_t theta;  // worst kept entry after a compaction (0 before any)
+  int count;     // entries in the wave segment (may pass kWaveCap: overflow)
+  float tau;     // own threshold: later elements must be strictly larger
+  float tsh;     // best threshold published by any wave, non-strict (-inf: none)
   int keep, thresh;
+  bool share;    // publish and read thresholds across the block's waves
 };
 
 template <int DT>
@@ -340,12 +325,22 @@ __device__ __forceinline__ void set_reference(StreamAcc& a, float mx, float c) {
   a.corr = exp2(-(double)err);
 }
 
-// Tree reductions over P = 1, 4 or 8 values.
+// Maximum that propagates NaN (one v_maximum3 per two inputs, no operand
+// canonicalisation).  Logits are finite or -inf; a NaN only blinds the
+// vector it sits in.
+__device__ __forceinline__ float maxm(float a, float b) {
+  return __builtin_elementwise_maximum(a, b);
+}
 template <int P>
-__device__ __forceinline__ float tree_max(const float* x) {
+__device__ __forceinline__ float vec_max(const float* x) {
   if constexpr (P == 1) return x[0];
-  else if constexpr (P == 4) return fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-  else return fmaxf(tree_max<4>(x), tree_max<4>(x + 4));
+  else if constexpr (P == 4) return maxm(maxm(maxm(x[0], x[1]), x[2]), x[3]);
+  else {
+    float m = maxm(maxm(x[0], x[1]), x[2]);
+    m = maxm(maxm(m, x[3]), x[4]);
+    m = maxm(maxm(m, x[5]), x[6]);
+    return maxm(m, x[7]);
+  }
 }
 template <int P>
 __device__ __forceinline__ float tree_sum(const float* x) {
@@ -354,22 +349,86 @@ __device__ __forceinline__ float tree_sum(const float* x) {
   else return tree_sum<4>(x) + tree_sum<4>(x + 4);
 }
 
-// Append the elements of one vector that pass both filters (wave-uniform
-// call; rare once the thresholds have settled).  Element e has id id0 + e.
-// Slots come from one ballot per element position: positions in the segment
-// follow (e, lane) order, which the segment does not need to preserve.
 __device__ __forceinline__ int lanes_below(uint64_t mask) {
   return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
                                         __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
+// Largest lane key k such that at least `keep` lanes (keep <= 64) hold a key
+// >= k: those lanes' entries are `keep` entries at least as good as k.
+__device__ __forceinline__ uint32_t wave_kth_lane_key(uint32_t lk, int keep) {
+  int ge = 0;
+#pragma unroll 4
+  for (int u = 0; u < 64; ++u) ge += (uint32_t)__builtin_amdgcn_readlane((int)lk, u) >= lk ? 1 : 0;
+  uint32_t cand = ge >= keep ? lk : 0u;
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    const uint32_t o = (uint32_t)__shfl_xor((int)cand, d, 64);
+    cand = o > cand ? o : cand;
+  }
+  return cand;
+}
+
+// As wave_kth_lane_key over two keys per lane (best b1, second b2; 0 when
+// absent), for keep <= 128.
+__device__ __forceinline__ uint32_t wave_kth_lane_key2(uint32_t b1, uint32_t b2, int keep) {
+  int ge1 = 0, ge2 = 0;
+#pragma unroll 4
+  for (int u = 0; u < 64; ++u) {
+    const uint32_t c1 = (uint32_t)__builtin_amdgcn_readlane((int)b1, u);
+    const uint32_t c2 = (uint32_t)__builtin_amdgcn_readlane((int)b2, u);
+    ge1 += (c1 >= b1 ? 1 : 0) + (c2 >= b1 ? 1 : 0);
+    ge2 += (c1 >= b2 ? 1 : 0) + (c2 >= b2 ? 1 : 0);
+  }
+  uint32_t cand = ge1 >= keep ? b1 : 0u;
+  if (ge2 >= keep && b2 > cand) cand = b2;
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    const uint32_t o = (uint32_t)__shfl_xor((int)cand, d, 64);
+    cand = o > cand ? o : cand;
+  }
+  return cand;
+}
+
+// Threshold key for `keep` <= 64 from per-lane best and second-best keys.
+__device__ __forceinline__ uint32_t wave_threshold_key(uint32_t b1, uint32_t b2, int keep) {
+  return keep <= 32 ? wave_kth_lane_key(b1, keep) : wave_kth_lane_key2(b1, b2, keep);
+}
+
+// Keep the entries of seg[0, n) whose key is >= kmin, in place (wave-local),
+// moving the companion array along when given; returns how many remain.
+template <class D = uint4>
+__device__ __forceinline__ int wave_keep_ge(uint64_t* seg, int n, uint32_t kmin,
+                                            D* dat = nullptr) {
+  const int l = lane_id();
+  int pos0 = 0;
+  for (int b0 = 0; b0 < n; b0 += 64) {
+    const int e = b0 + l;
+    const uint64_t v = e < n ? seg[e] : 0ull;
+    const bool k = e < n && (uint32_t)(v >> 32) >= kmin;
+    D dv{};
+    if (dat && k) dv = dat[e];
+    const uint64_t km = __ballot(k);
+    wave_lds_sync();
+    if (k) {  // never above e: reads of later rounds intact
+      seg[pos0 + lanes_below(km)] = v;
+      if (dat) dat[pos0 + lanes_below(km)] = dv;
+    }
+    pos0 += __popcll(km);
+    wave_lds_sync();
+  }
+  return pos0;
+}
+
+// Append the elements of one vector that beat both thresholds (wave-uniform
+// call).  Element e has id id0 + e; positions in the segment follow (e, lane)
+// order, which nothing downstream relies on.
 template <int P>
-__device__ __forceinline__ void wave_append(const float* x, int id0, bool ok, WaveBuf& wb,
-                                            uint64_t* seg) {
+__device__ __forceinline__ void wave_append(const float* x, int id0, WaveBuf& wb, uint64_t* seg) {
   int base = wb.count;
 #pragma unroll
   for (int e = 0; e < P; ++e) {
-    const bool pass = ok && !(x[e] <= wb.tau) && x[e] >= wb.tsh;
+    const bool pass = x[e] > wb.tau && x[e] >= wb.tsh;
     const uint64_t m = __ballot(pass);
     if (pass) {
       const int slot = base + lanes_below(m);
@@ -380,26 +439,64 @@ __device__ __forceinline__ void wave_append(const float* x, int id0, bool ok, Wa
   wb.count = base;
 }
 
-// One tile of U vectors of P elements held by this thread.  Ids increase with
-// (u, e).  The running max, argmax and sum reference move at most once per
-// tile; the buffer append is one wave-uniform branch per tile.
-template <bool BUF, bool SUM, bool ARG, int U, int P>
-__device__ __forceinline__ void consume_tile(const float* x, const int* ids, const bool* ok,
-                                             float c, StreamAcc& a, WaveBuf& wb, uint64_t* seg) {
-  float um[U];
+// Wave tile boundary: shrink the segment once it passed its limit, raising
+// tau.  For keep <= 64 the new tau is the largest key that `keep` lane
+// maxima reach (cheap, keeps a few more than `keep`); otherwise, or when that
+// leaves too many, a radix select keeps exactly `keep`.  Either way every
+// dropped entry has `keep` better ones left.  An overflowed segment stops
+// admitting (the row then takes the exact path).  With sharing on, a wave
+// also filters by the best threshold any wave has published (non-strict: ids
+// interleave across waves); stale reads only lower that filter.
+__device__ __forceinline__ void wave_tile_end(WaveBuf& wb, uint64_t* seg, uint32_t* hist,
+                                              RowShared& sh) {
+  if (wb.count > kWaveCap) {
+    wb.tau = __builtin_huge_valf();  // overflowed: admit nothing more
+  } else if (wb.count > wb.thresh) {
+    wave_lds_sync();
+    int n = wb.count;
+    if (wb.keep <= 64) {
+      uint32_t b1 = 0u, b2 = 0u;  // this lane's best two keys of its column
+      for (int e = lane_id(); e < n; e += 64) {
+        const uint32_t k = (uint32_t)(seg[e] >> 32);
+        if (k > b1) { b2 = b1; b1 = k; } else if (k > b2) { b2 = k; }
+      }
+      const uint32_t tk = wave_threshold_key(b1, b2, wb.keep);
+      if (tk != 0u) {  // 0: fewer than `keep` entries (not reached while n > thresh >= keep)
+        n = wave_keep_ge(seg, n, tk);
+        wb.tau = key_to_float(tk);
+      }
+    }
+    if (n > wb.thresh) {
+      const uint64_t th = wave_compact(seg, hist, n, wb.keep);
+      n = wb.keep;
+      wb.tau = entry_val(th);
+    }
+    wb.count = n;
+    if (wb.share && lane_id() == 0) sh.wtau[wave_id()] = wb.tau;
+    wave_lds_sync();
+  }
+  if (wb.share) {
+    float t = sh.wtau[0];
 #pragma unroll
-  for (int u = 0; u < U; ++u) um[u] = ok[u] ? tree_max<P>(x + u * P) : -3.402823466e38f;
-  float cm = um[0];
-#pragma unroll
-  for (int u = 1; u < U; ++u) cm = fmaxf(cm, um[u]);
-  if (cm > a.mx) {  // the running max moves: rare after the first tiles
+    for (int q = 1; q < kWaves; ++q) t = fmaxf(t, sh.wtau[q]);
+    wb.tsh = t;
+  }
+}
+
+// Running max, first argmax and exp-sum over a tile of U vectors of P
+// elements (masked elements are -inf).  The max and the sum reference move
+// at most once per tile.
+template <bool SUM, bool ARG, int U, int P>
+__device__ __forceinline__ void tile_stats(const float* x, const int* ids, float cm, float c,
+                                           StreamAcc& a) {
+  if (cm > a.mx) {  // rare after the first tiles
     if (ARG) {
       int first = 0x7FFFFFFF;
 #pragma unroll
       for (int u = U - 1; u >= 0; --u)
 #pragma unroll
         for (int e = P - 1; e >= 0; --e)
-          if (ok[u] && x[u * P + e] == cm) first = ids[u] + e;
+          if (x[u * P + e] == cm) first = ids[u] + e;
       a.bi = first;
     }
     if (SUM) {
@@ -410,190 +507,269 @@ __device__ __forceinline__ void consume_tile(const float* x, const int* ids, con
     }
   }
   if (SUM) {
-    float part[U];
+    float cs = 0.0f;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       float w[P];
 #pragma unroll
       for (int e = 0; e < P; ++e) w[e] = __builtin_amdgcn_exp2f(fmaf(x[u * P + e], c, a.nmc));
-      part[u] = ok[u] ? tree_sum<P>(w) : 0.0f;
+      cs += tree_sum<P>(w);
     }
-    float cs = part[0];
-#pragma unroll
-    for (int u = 1; u < U; ++u) cs += part[u];
     a.s += (double)cs * a.corr;
   }
-  if (BUF) {
-    const bool any = !(cm <= wb.tau) && cm >= wb.tsh && cm > -3.402823466e38f;
-    if (__ballot(any)) {
+}
+
+// Filter a tile into the wave segment and close the tile.
+template <int U, int P>
+__device__ __forceinline__ void tile_buffer(const float* x, const float* um, float cm,
+                                            const int* ids, WaveBuf& wb, uint64_t* seg,
+                                            uint32_t* hist, RowShared& sh) {
+  if (__ballot(cm > wb.tau && cm >= wb.tsh)) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const bool pu = ok[u] && !(um[u] <= wb.tau) && um[u] >= wb.tsh;
-        if (__ballot(pu)) wave_append<P>(x + u * P, ids[u], ok[u], wb, seg);
-      }
-    }
+    for (int u = 0; u < U; ++u)
+      if (__ballot(um[u] > wb.tau && um[u] >= wb.tsh)) wave_append<P>(x + u * P, ids[u], wb, seg);
+    wave_tile_end(wb, seg, hist, sh);
+  } else if (wb.share) {
+    wave_tile_end(wb, seg, hist, sh);
   }
 }
 
-// Wave tile boundary: compact the segment when it passed its limit; an
-// overflowed segment stops admitting (the row then takes the exact path).
-// Every wave filters by its own threshold (strict: its later elements have
-// larger ids) and by the best threshold any wave has published (non-strict:
-// ids interleave across waves).  An element below another wave's threshold
-// value has `keep` better elements there, so it is in neither the row's top-k
-// (k <= keep) nor the certified prefix; stale reads only lower the filter.
-__device__ __forceinline__ void wave_tile_end(WaveBuf& wb, uint64_t* seg, uint32_t* hist,
-                                              RowShared& sh) {
-  if (wb.count > wb.thresh) {
-    if (wb.count > kWaveCap) {
-      wb.tau = __int_as_float(0x7F800000);  // +inf: overflowed, admit nothing more
-      return;
-    }
+// Vector-candidate variant: entries are (vector max, vector index) with the
+// raw vector beside them; a row's top-k elements all lie in its top-k vectors
+// under that order, since every vector ahead of one holding a top-k element
+// owns a distinct better element.  Same shrinking rule as wave_tile_end
+// (keep <= 64), data moving with the entries; capacity kVecCap.
+__device__ __forceinline__ void wave_tile_end_vec(WaveBuf& wb, uint64_t* seg, uint4* dat,
+                                                  uint32_t* hist) {
+  if (wb.count > kVecCap) {
+    wb.tau = __builtin_huge_valf();  // overflowed: admit nothing more
+  } else if (wb.count > wb.thresh) {
     wave_lds_sync();
-    wb.theta = wb.keep <= 64 ? wave_select_small(seg, (uint64_t*)hist, wb.count, wb.keep)
-                             : wave_compact(seg, hist, wb.count, wb.keep);
-    wb.count = wb.keep;
-    wb.tau = entry_val(wb.theta);
-    if (lane_id() == 0) sh.wtau[wave_id()] = wb.tau;
+    int n = wb.count;
+    uint32_t b1 = 0u, b2 = 0u;
+    for (int e = lane_id(); e < n; e += 64) {
+      const uint32_t k = (uint32_t)(seg[e] >> 32);
+      if (k > b1) { b2 = b1; b1 = k; } else if (k > b2) { b2 = k; }
+    }
+    const uint32_t tk = wave_threshold_key(b1, b2, wb.keep);
+    if (tk != 0u) {
+      n = wave_keep_ge(seg, n, tk, dat);
+      wb.tau = key_to_float(tk);
+    }
+    if (n > wb.thresh) {
+      const uint64_t th = wave_compact(seg, hist, n, wb.keep, dat);
+      n = wb.keep;
+      wb.tau = entry_val(th);
+    }
+    wb.count = n;
+    wave_lds_sync();
   }
-  float t = sh.wtau[0];
-#pragma unroll
-  for (int q = 1; q < kWaves; ++q) t = fmaxf(t, sh.wtau[q]);
-  wb.tsh = t;
 }
 
-// Stream one row.  Buffered rows keep, per wave, the best `keep` elements
-// (compacting when a segment holds more than `thresh`); `ramp` extra small
-// tiles let a loose threshold settle before full tiles start.  Full tiles
-// alternate between two load buffers so the next tile is always in flight.
-template <int DT, bool BUF, bool SUM, bool ARG>
+// raw(u) gives the u-th vector's 16 bytes (kept or rebuilt from its elements).
+template <int U, class Raw>
+__device__ __forceinline__ void tile_buffer_vec(Raw&& raw, const float* um, float cm, int vi0,
+                                                WaveBuf& wb, uint64_t* seg, uint4* dat,
+                                                uint32_t* hist) {
+  if (__ballot(cm > wb.tau)) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool pass = um[u] > wb.tau;
+      const uint64_t m = __ballot(pass);
+      if (pass) {
+        const int slot = wb.count + lanes_below(m);
+        if (slot < kVecCap) {
+          seg[slot] = make_entry(um[u], vi0 + u * kBlock);
+          dat[slot] = raw(u);
+        }
+      }
+      wb.count += __popcll(m);
+    }
+    wave_tile_end_vec(wb, seg, dat, hist);
+  }
+}
+
+// Full tiles of U vectors per thread from vector v0 on, two load buffers in
+// turn so the next tile is in flight while one is consumed (the scheduling
+// barrier keeps the compiler from sinking the loads below the consumer).
+// Returns the first vector not consumed.
+template <int DT, int U, class F>
+__device__ __forceinline__ int stream_tiles(const RowSplit<DT>& sp, int v0, F&& consume) {
+  const int ntile = (sp.nvec - v0) / (U * kBlock);
+  uint4 A[U], B[U];
+  auto ld = [&](uint4* v, int t) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      v[u] = load_stream(sp.vbase + v0 + (t * U + u) * kBlock + (int)threadIdx.x);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  if (ntile >= 1) ld(A, 0);
+  int t = 0;
+  for (; t + 3 <= ntile; t += 2) {
+    ld(B, t + 1);
+    consume(A, v0 + t * U * kBlock);
+    ld(A, t + 2);
+    consume(B, v0 + (t + 1) * U * kBlock);
+  }
+  if (t + 2 == ntile) {
+    ld(B, t + 1);
+    consume(A, v0 + t * U * kBlock);
+    consume(B, v0 + (t + 1) * U * kBlock);
+  } else if (t + 1 == ntile) {
+    consume(A, v0 + t * U * kBlock);
+  }
+  return v0 + ntile * U * kBlock;
+}
+
+// Stream one row.  Element-buffered rows (BUF) keep, per wave, at least the
+// best `keep` elements seen (shrinking the segment when it holds more than
+// `thresh`), starting with `ramp` smaller tiles and sharing thresholds across
+// waves.  Vector-buffered rows (VEC, keep <= 64) keep the best `keep` body
+// vectors by their max instead; their first full tile admits only vectors
+// that `keep` lanes' best vectors reach.  Head and tail elements are not
+// buffered in VEC mode.
+template <int DT, bool BUF, bool SUM, bool ARG, bool VEC = false>
 __device__ __forceinline__ void stream_row(const void* row, int V, float c, int keep, int thresh,
                                            int ramp, RowShared& sh, StreamAcc& a) {
   constexpr int P = Vec<DT>::kEpv;
   constexpr int U = SV_UNROLL;
+  constexpr float kNegInf = -__builtin_huge_valf();
+  static_assert(!(BUF && VEC), "one buffer kind per row");
+  static_assert(!(VEC && (SUM || ARG)), "vector candidates stream alone");
   const RowSplit<DT> sp(row, V);
   const int tid = threadIdx.x;
   const int w = wave_id();
-  uint64_t* seg = sh.buf + w * kWaveCap;
+  uint64_t* seg = sh.buf + w * (VEC ? kVecStride : kWaveCap);
+  uint4* dat = (uint4*)(sh.buf + w * kVecStride + kVecDatOff);
   uint32_t* hist = sh.whist[w];
   a.bi = 0x7FFFFFFF;
   a.s = 0.0;
-  a.mx = -3.402823466e38f;  // before any finite element: weights of -inf are 0
+  a.mx = -3.402823466e38f;  // below every finite element: weights of -inf are 0
   a.nmc = 0.0f;
   a.corr = 1.0;
   WaveBuf wb;
   wb.count = 0;
-  wb.tau = __int_as_float(0x7FC00000);  // NaN
-  wb.tsh = -__int_as_float(0x7F800000);  // -inf
-  wb.theta = 0ull;
+  wb.tau = kNegInf;
+  wb.tsh = kNegInf;
   wb.keep = keep;
   wb.thresh = thresh;
+  wb.share = BUF;
 
-  // scalar pieces (head and tail): one element per thread
-  auto scalar = [&](int i, bool in) {
-    float x[1] = {in ? Vec<DT>::load1(row, i) : 0.0f};
-    int ids[1] = {i};
-    bool ok[1] = {in};
-    consume_tile<BUF, SUM, ARG, 1, 1>(x, ids, ok, c, a, wb, seg);
-    if (BUF) wave_tile_end(wb, seg, hist, sh);
+  // U vectors from vector vb (all in range) -> elements, vector maxima, tile max
+  auto unpack = [&](const uint4* v, int vb, float* x, float* um, int* ids) {
+    float cm = kNegInf;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      Vec<DT>::unpack(v[u], x + u * P);
+      um[u] = vec_max<P>(x + u * P);
+      cm = maxm(cm, um[u]);
+      ids[u] = sp.head + (vb + u * kBlock + tid) * P;
+    }
+    return cm;
   };
-  if (sp.head > 0) scalar(tid, tid < sp.head);
+  // scalar pieces (head and tail): one element per thread, -inf when out of range
+  auto scalar = [&](int i, bool in, int slot) {
+    float x[1] = {in ? Vec<DT>::load1(row, i) : kNegInf};
+    int ids[1] = {i};
+    tile_stats<SUM, ARG, 1, 1>(x, ids, x[0], c, a);
+    if (BUF) tile_buffer<1, 1>(x, x, x[0], ids, wb, seg, hist, sh);
+    if (VEC && in) sh.endx[slot] = x[0];  // kept aside for the finish
+  };
+  if (sp.head > 0) scalar(tid, tid < sp.head, tid);
 
   int v0 = 0;
-  auto small_tile = [&](auto Ut) {
-    constexpr int UU = decltype(Ut)::value;
-    uint4 v[UU];
+  if (VEC && sp.nvec >= U * kBlock) {
+    // first tile: admit vectors whose max reaches the threshold key of the
+    // lanes' best two vector maxima
+    uint4 v[U];
 #pragma unroll
-    for (int u = 0; u < UU; ++u) v[u] = load_stream(sp.vbase + v0 + u * kBlock + tid);
-    float x[UU * P];
-    int ids[UU];
-    bool ok[UU];
+    for (int u = 0; u < U; ++u) v[u] = load_stream(sp.vbase + u * kBlock + tid);
+    float x[U * P], um[U];
+    int ids[U];
+    const float cm = unpack(v, 0, x, um, ids);
+    tile_stats<SUM, ARG, U, P>(x, ids, cm, c, a);
+    uint32_t b1 = 0u, b2 = 0u;
 #pragma unroll
-    for (int u = 0; u < UU; ++u) {
-      Vec<DT>::unpack(v[u], x + u * P);
-      ids[u] = sp.head + (v0 + u * kBlock + tid) * P;
-      ok[u] = true;
+    for (int u = 0; u < U; ++u) {
+      const uint32_t k = fkey(um[u]);
+      if (k > b1) { b2 = b1; b1 = k; } else if (k > b2) { b2 = k; }
     }
-    consume_tile<BUF, SUM, ARG, UU, P>(x, ids, ok, c, a, wb, seg);
-    v0 += UU * kBlock;
-    if (BUF) wave_tile_end(wb, seg, hist, sh);
-  };
-  if (BUF && keep <= 64 && v0 + kBlock <= sp.nvec) {
-    // first tile: admit only entries at least as good as the keep-th best lane
-    // maximum -- keep lanes hold an entry that good, so nothing better is lost
-    const uint4 v = load_stream(sp.vbase + v0 + tid);
-    float x[P];
-    Vec<DT>::unpack(v, x);
-    const int id0 = sp.head + (v0 + tid) * P;
-    int ids[1] = {id0};
-    bool ok[1] = {true};
-    consume_tile<false, SUM, ARG, 1, P>(x, ids, ok, c, a, wb, seg);
-    uint64_t best = 0ull;
+    const uint32_t tk = wave_threshold_key(b1, b2, keep);
+    const float t0 = tk != 0u ? key_to_float(tk) : kNegInf;
 #pragma unroll
-    for (int e = 0; e < P; ++e) {
-      const uint64_t en = make_entry(x[e], id0 + e);
-      best = en > best ? en : best;
-    }
-    int rank = 0;
-#pragma unroll
-    for (int u = 0; u < 64; ++u) {
-      const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((uint32_t)best, u);
-      const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((uint32_t)(best >> 32), u);
-      rank += (((uint64_t)hi << 32) | (uint64_t)lo) > best ? 1 : 0;
-    }
-    const uint64_t sel = __ballot(rank == keep - 1);
-    uint64_t theta0 = 0ull;
-    if (sel) {
-      const int src = __ffsll((unsigned long long)sel) - 1;
-      const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((uint32_t)(best >> 32), src);
-      const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((uint32_t)best, src);
-      theta0 = ((uint64_t)hi << 32) | (uint64_t)lo;
-    }
-    int base = 0;
-#pragma unroll
-    for (int e = 0; e < P; ++e) {
-      const uint64_t en = make_entry(x[e], id0 + e);
-      const bool pass = en >= theta0;
+    for (int u = 0; u < U; ++u) {
+      const bool pass = um[u] >= t0;
       const uint64_t m = __ballot(pass);
       if (pass) {
-        const int slot = base + lanes_below(m);
-        if (slot < kWaveCap) seg[slot] = en;
+        const int slot = wb.count + lanes_below(m);
+        if (slot < kVecCap) {
+          seg[slot] = make_entry(um[u], u * kBlock + tid);
+          dat[slot] = v[u];
+        }
       }
-      base += __popcll(m);
+      wb.count += __popcll(m);
     }
-    wb.count = base;
-    if (theta0) {
-      wb.theta = theta0;
-      wb.tau = entry_val(theta0);
-      if (lane_id() == 0) sh.wtau[w] = wb.tau;
-    }
-    v0 += kBlock;
-    wave_tile_end(wb, seg, hist, sh);
+    wb.tau = t0;  // later vectors with max equal to t0 have larger ids: strict from here
+    wave_tile_end_vec(wb, seg, dat, hist);
+    v0 = U * kBlock;
   }
   if (BUF) {
-    if (v0 + kBlock <= sp.nvec) small_tile(std::integral_constant<int, 1>{});
-    if (v0 + kBlock <= sp.nvec) small_tile(std::integral_constant<int, 1>{});
+    // smaller tiles first, so the segment cannot overflow before tau settles
+    auto small = [&](auto Ut) {
+      constexpr int UU = decltype(Ut)::value;
+      uint4 v[UU];
+      float x[UU * P], um[UU];
+      int ids[UU];
+      float cm = kNegInf;
+#pragma unroll
+      for (int u = 0; u < UU; ++u) {
+        v[u] = load_stream(sp.vbase + v0 + u * kBlock + tid);
+        Vec<DT>::unpack(v[u], x + u * P);
+        um[u] = vec_max<P>(x + u * P);
+        cm = maxm(cm, um[u]);
+        ids[u] = sp.head + (v0 + u * kBlock + tid) * P;
+      }
+      tile_stats<SUM, ARG, UU, P>(x, ids, cm, c, a);
+      tile_buffer<UU, P>(x, um, cm, ids, wb, seg, hist, sh);
+      v0 += UU * kBlock;
+    };
+    if (v0 + kBlock <= sp.nvec) small(std::integral_constant<int, 1>{});
+    if (v0 + kBlock <= sp.nvec) small(std::integral_constant<int, 1>{});
     for (int r = 0; r < ramp; ++r)
-      if (v0 + 2 * kBlock <= sp.nvec) small_tile(std::integral_constant<int, 2>{});
+      if (v0 + 2 * kBlock <= sp.nvec) small(std::integral_constant<int, 2>{});
   }
-  while (v0 + U * kBlock <= sp.nvec) small_tile(std::integral_constant<int, U>{});
+  v0 = stream_tiles<DT, U>(sp, v0, [&](const uint4* v, int vb) {
+    float x[U * P], um[U];
+    int ids[U];
+    const float cm = unpack(v, vb, x, um, ids);
+    tile_stats<SUM, ARG, U, P>(x, ids, cm, c, a);
+    if (BUF) tile_buffer<U, P>(x, um, cm, ids, wb, seg, hist, sh);
+    if (VEC) tile_buffer_vec<U>([&](int u) { return v[u]; }, um, cm, vb + tid, wb, seg, dat, hist);
+  });
   // ragged last tiles of the body: vectors [v0, nvec), one per thread
-  for (; v0 < sp.nvec;) {
+  for (; v0 < sp.nvec; v0 += kBlock) {
     const int vi = v0 + tid;
-    const bool in = vi < sp.nvec;
     float x[P];
-    Vec<DT>::unpack(in ? load_stream(sp.vbase + vi) : make_uint4(0u, 0u, 0u, 0u), x);
+    uint4 rv = make_uint4(0u, 0u, 0u, 0u);
+    if (vi < sp.nvec) {
+      rv = load_stream(sp.vbase + vi);
+      Vec<DT>::unpack(rv, x);
+    } else {
+#pragma unroll
+      for (int e = 0; e < P; ++e) x[e] = kNegInf;
+    }
     int ids[1] = {sp.head + vi * P};
-    bool ok[1] = {in};
-    consume_tile<BUF, SUM, ARG, 1, P>(x, ids, ok, c, a, wb, seg);
-    v0 += kBlock;
-    if (BUF) wave_tile_end(wb, seg, hist, sh);
+    const float cm = vec_max<P>(x);
+    tile_stats<SUM, ARG, 1, P>(x, ids, cm, c, a);
+    if (BUF) tile_buffer<1, P>(x, &cm, cm, ids, wb, seg, hist, sh);
+    if (VEC) tile_buffer_vec<1>([&](int) { return rv; }, &cm, cm, vi, wb, seg, dat, hist);
   }
-  if (sp.tail0 < V) scalar(sp.tail0 + tid, sp.tail0 + tid < V);
-  if (BUF && lane_id() == 0) {
-    sh.wcount[w] = wb.count > kWaveCap ? kWaveCap : wb.count;
-    sh.wtheta[w] = wb.theta;
-    if (wb.count > kWaveCap) atomicOr(&sh.woverflow, 1);
+  if (sp.tail0 < V) scalar(sp.tail0 + tid, sp.tail0 + tid < V, 8 + tid);
+  if ((BUF || VEC) && lane_id() == 0) {
+    const int cap = VEC ? kVecCap : kWaveCap;
+    sh.wcount[w] = wb.count > cap ? cap : wb.count;
+    sh.wtau[w] = wb.tau;
+    if (wb.count > cap) atomicOr(&sh.woverflow, 1);
   }
 }
 

@@ -226,6 +226,235 @@ __device__ void exact_kept_set(const void* row, int V, float m, float T, int k_e
 }
 
 // -------------------------------------------------------- row pass kernel
+// LDS areas of the vector-candidate finish, past the wave regions (entries of
+// 8 bytes; each wave holds at most kThreshVec candidates when streaming ends
+// without overflow).
+constexpr int kVecGatherOff = kWaves * kVecStride;         // gathered candidates
+constexpr int kVecGatherCap = kWaves * kThreshVec;
+constexpr int kVecGIdxOff = kVecGatherOff + kVecGatherCap;  // their data slots (int)
+constexpr int kVecSortOff = kVecGIdxOff + kVecGatherCap / 2;
+constexpr int kVecSIdxOff = kVecSortOff + 64;               // 64 ints
+constexpr int kVecElemOff = kVecGatherOff;                  // reuses the gather area
+constexpr int kVecElemCap = kVecSortOff - kVecElemOff;
+static_assert(kVecSIdxOff + 32 <= kCap, "LDS layout");
+static_assert(kVecElemCap >= 64 * 8 + 16, "room for k vectors and the scalar ends");
+static_assert(kVecElemOff + kVecElemCap <= kVecSortOff, "elements stay clear of the sorted area");
+
+// The best min(n, k) of src[0, n) (distinct entries), by rank counting, to
+// dst[rank] (with their companions); wave-local.  Returns min(n, k).
+__device__ __forceinline__ int wave_rank_top(const uint64_t* src, const int* srci, int n, int k,
+                                             uint64_t* dst, int* dsti) {
+  const int l = lane_id();
+  if (n <= 64) {  // one entry per lane, the others read by lane broadcast
+    const uint64_t mine = l < n ? src[l] : 0ull;
+    const int comp = (srci && l < n) ? srci[l] : 0;
+    const uint32_t mlo = (uint32_t)mine, mhi = (uint32_t)(mine >> 32);
+    int rank = 0;
+    for (int u = 0; u < n; ++u) {
+      const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)mlo, u);
+      const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)mhi, u);
+      rank += (((uint64_t)hi << 32) | (uint64_t)lo) > mine ? 1 : 0;
+    }
+    wave_lds_sync();
+    if (l < n && rank < k) {
+      dst[rank] = mine;
+      if (srci) dsti[rank] = comp;
+    }
+    wave_lds_sync();
+    return n < k ? n : k;
+  }
+  for (int j0 = 0; j0 < n; j0 += 64) {
+    const int f = j0 + l;
+    const uint64_t mine = f < n ? src[f] : 0ull;
+    int rank = 0;
+    for (int u = 0; u < n; ++u) rank += src[u] > mine ? 1 : 0;
+    if (f < n && rank < k) {
+      dst[rank] = mine;
+      if (srci) dsti[rank] = srci[f];
+    }
+  }
+  wave_lds_sync();
+  return n < k ? n : k;
+}
+
+// Shrink src[0, n) (n > 64) toward `k` <= 64 entries by the lane-threshold
+// rule, then exactly to k by radix select if still above 64.
+__device__ __forceinline__ int wave_shrink(uint64_t* src, int* srci, int n, int k, uint32_t* hist) {
+  uint32_t b1 = 0u, b2 = 0u;
+  for (int e = lane_id(); e < n; e += 64) {
+    const uint32_t key = (uint32_t)(src[e] >> 32);
+    if (key > b1) { b2 = b1; b1 = key; } else if (key > b2) { b2 = key; }
+  }
+  const uint32_t tk = wave_threshold_key(b1, b2, k);
+  if (tk != 0u) n = wave_keep_ge(src, n, tk, srci);
+  return n;
+}
+
+// Top-k rows with k <= 64, run by wave 0 once the block's streaming is done:
+// the best k vectors among the wave candidates, their elements (and the
+// unvectorised head and tail) at or above the k-th vector max, the best k of
+// those in order, then the fp64 weights relative to the row max m, the top-p
+// walk over the k-set (Top-k sampling, then nucleus sampling on the
+// truncated distribution) and the kept list.  Returns false when the row
+// needs the exact path (fewer than k finite elements).
+template <int DT>
+__device__ __forceinline__ bool topk_vec_finish(int V, int k, float m, float T, bool topp_on,
+                                                float P, int d, const RowSplit<DT>& sp,
+                                                RowShared& sh, RowRec& out, double& pd,
+                                                ListEntry* L) {
+  constexpr int PE = Vec<DT>::kEpv;
+  constexpr float kNegInf = -__builtin_huge_valf();
+  const int l = lane_id();
+  uint64_t* C = sh.buf + kVecGatherOff;
+  int* CI = (int*)(sh.buf + kVecGIdxOff);
+  uint64_t* S = sh.buf + kVecSortOff;
+  int* SI = (int*)(sh.buf + kVecSIdxOff);
+  uint64_t* E = sh.buf + kVecElemOff;
+  uint32_t* hist = sh.whist[0];
+
+  // vectors below the best wave threshold have k better vectors in that wave
+  float tb = sh.wtau[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) tb = fmaxf(tb, sh.wtau[w]);
+  const uint32_t tkey = fkey(tb);
+  static_assert(kThreshVec <= 128, "two gather rounds per wave segment");
+  uint64_t cv[kWaves][2];  // every read issued before the first use
+  int cnt[kWaves];
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    cnt[w] = sh.wcount[w];
+    if (cnt[w] > 128) return false;  // not reached: segments end at or below kThreshVec
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int e = r * 64 + l;
+      cv[w][r] = e < cnt[w] ? sh.buf[w * kVecStride + e] : 0ull;
+    }
+  }
+  int nc = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w)
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const bool kp = r * 64 + l < cnt[w] && (uint32_t)(cv[w][r] >> 32) >= tkey;
+      const uint64_t mk = __ballot(kp);
+      if (kp) {
+        const int slot = nc + lanes_below(mk);
+        C[slot] = cv[w][r];
+        CI[slot] = w * kVecCap + r * 64 + l;
+      }
+      nc += __popcll(mk);
+    }
+  wave_lds_sync();
+  if (nc > 128) {  // many ties: shrink toward k first
+    nc = wave_shrink(C, CI, nc, k, hist);
+    if (nc > 128) {
+      nc = wave_rank_top(C, CI, nc, k, S, SI);
+      for (int t = l; t < nc; t += 64) {
+        C[t] = S[t];
+        CI[t] = SI[t];
+      }
+      wave_lds_sync();
+    }
+  }
+  // up to two candidates per lane; the k-th largest key by a ballot radix
+  // select (fewer than k candidates: no wave ever dropped a finite vector)
+  bool has[2];
+  uint64_t vent[2];
+  int di[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    has[r] = r * 64 + l < nc;
+    vent[r] = has[r] ? C[r * 64 + l] : 0ull;
+    di[r] = has[r] ? CI[r * 64 + l] : 0;
+  }
+  uint32_t tk = 0u;
+  if (nc >= k) {
+    for (int b = 31; b >= 0; --b) {
+      const uint32_t cand = tk | (1u << b);
+      const int cnt = __popcll(__ballot(has[0] && (uint32_t)(vent[0] >> 32) >= cand)) +
+                      __popcll(__ballot(has[1] && (uint32_t)(vent[1] >> 32) >= cand));
+      if (cnt >= k) tk = cand;
+    }
+  }
+  // every vector at or above the k-th key (ties included) holds the top-k;
+  // at least k elements reach its value
+  const float tv = tk != 0u ? key_to_float(tk) : kNegInf;
+  float x[2][PE];
+  int id0[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    has[r] = has[r] && (uint32_t)(vent[r] >> 32) >= tk;
+    const uint4* dat = (const uint4*)(sh.buf + (di[r] / kVecCap) * kVecStride + kVecDatOff);
+    Vec<DT>::unpack(has[r] ? dat[di[r] % kVecCap] : make_uint4(0u, 0u, 0u, 0u), x[r]);
+    id0[r] = sp.head + entry_idx(vent[r]) * PE;
+  }
+  const int ntail = V - sp.tail0;
+  const bool hs = l < sp.head;
+  const bool ts = l >= 32 && l - 32 < ntail;
+  const float xs = hs ? sh.endx[l] : (ts ? sh.endx[8 + l - 32] : kNegInf);
+  const int is = hs ? l : sp.tail0 + l - 32;
+  wave_lds_sync();  // gather area read: E may overwrite it
+
+  int ne = 0;
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    if (!__ballot(has[r])) continue;
+#pragma unroll
+    for (int e = 0; e < PE; ++e) {
+      const bool pass = has[r] && x[r][e] >= tv;
+      const uint64_t mk = __ballot(pass);
+      const int slot = ne + lanes_below(mk);
+      if (pass && slot < kVecElemCap) E[slot] = make_entry(x[r][e], id0[r] + e);
+      ne += __popcll(mk);
+    }
+  }
+  {
+    const bool pass = (hs || ts) && xs >= tv;
+    const uint64_t mk = __ballot(pass);
+    const int slot = ne + lanes_below(mk);
+    if (pass && slot < kVecElemCap) E[slot] = make_entry(xs, is);
+    ne += __popcll(mk);
+  }
+  if (ne < k || ne > kVecElemCap) return false;  // too few finite, or a pile of ties
+  wave_lds_sync();
+  if (ne > 64) ne = wave_shrink(E, nullptr, ne, k, hist);
+  if (ne > 64) {
+    wave_compact(E, hist, ne, k);
+    ne = k;
+  }
+  wave_rank_top(E, nullptr, ne, k, S, nullptr);
+  const uint64_t el = l < k ? S[l] : 0ull;
+  if (!(entry_val(S[k - 1]) > kNegInf)) return false;  // fewer than k finite elements
+
+  const bool valid = l < k;
+  const float xv = entry_val(el);
+  const int idv = entry_idx(el);
+  const double wgt = valid ? exp(((double)xv - (double)m) / (double)T) : 0.0;
+  const double incl = wave_inclusive_sum(wgt);
+  double excl = __shfl_up(incl, 1, 64);
+  if (l == 0) excl = 0.0;
+  const double zk = __shfl(incl, k - 1, 64);
+  const double target = topp_on ? (double)P * zk : 2.0 * zk + 1.0;
+  const uint64_t stop = __ballot(valid && !(excl < target));
+  int nkeep = stop ? __ffsll((unsigned long long)stop) - 1 : k;
+  if (nkeep < 1) nkeep = 1;
+  const double zn = __shfl(incl, nkeep - 1, 64);
+  const uint64_t fm = __ballot(l < nkeep && idv == d);
+  pd = fm ? __shfl(wgt, __ffsll((unsigned long long)fm) - 1, 64) / zn : 0.0;
+  out.a = __shfl(idv, 0, 64);
+  out.zk = zk;
+  out.zn = zn;
+  out.nkeep = nkeep;
+  out.mode = kModeList;
+  if (l < nkeep) {
+    ListEntry le;
+    le.idx = idv;
+    le.x = xv;
+    L[l] = le;
+  }
+  return true;
+}
+
 template <int DT>
 __device__ __forceinline__ void row_pass(const VerifyArgs& A, RowShared& sh) {
   const int i = blockIdx.x;
@@ -266,6 +495,9 @@ __device__ __forceinline__ void row_pass(const VerifyArgs& A, RowShared& sh) {
   const void* row = (const char*)A.logits + (size_t)i * (size_t)A.ld_logits * (DT == 1 ? 2 : 4);
   const int d = tested ? A.draft_tokens[i] : -1;
   const bool d_ok = d >= 0 && d < V;
+  // q(d) is read now so its latency hides behind the stream
+  const float qd = (!greedy && d_ok && A.draft_probs)
+                       ? A.draft_probs[(size_t)i * (size_t)A.ld_q + d] : 0.0f;
   const uint32_t rid = A.request_id ? A.request_id[r] : (uint32_t)r;
   const uint32_t pos0 = A.position0 ? A.position0[r] : 0u;
 
@@ -308,7 +540,10 @@ __device__ __forceinline__ void row_pass(const VerifyArgs& A, RowShared& sh) {
 
   // ------------------------------------------------ sampled rows
   const bool all_mode = k_eff == V && !topp_on;
-  const bool topk_mode = k_eff < V && k_eff <= kTopkFast;
+  // vector candidates on the verify path; the build path also sums the row
+  // and takes the element buffer (fewer live registers than both together)
+  const bool vec_mode = !need_sum_build && k_eff < V && k_eff <= kTopkVec;
+  const bool topk_mode = k_eff < V && k_eff <= kTopkFast && !vec_mode;
   const bool topp_mode = k_eff == V && topp_on;
   const bool buf_mode = topk_mode || topp_mode;
   const bool need_sum = need_sum_build || all_mode || topp_mode;
@@ -322,7 +557,9 @@ __device__ __forceinline__ void row_pass(const VerifyArgs& A, RowShared& sh) {
     thresh = kThreshTopP;
     ramp = 2;
   }
-  if (all_mode) {
+  if (vec_mode) {
+    stream_row<DT, false, false, false, true>(row, V, c, k_eff, kThreshVec, 0, sh, acc);
+  } else if (all_mode) {
     if (need_sum_build) stream_row<DT, false, true, true>(row, V, c, 1, 1, 0, sh, acc);
     else stream_row<DT, false, true, false>(row, V, c, 1, 1, 0, sh, acc);
   } else if (buf_mode) {
@@ -342,9 +579,19 @@ __device__ __forceinline__ void row_pass(const VerifyArgs& A, RowShared& sh) {
   out.m = m;
   const double Td = (double)T;
   double pd = 0.0;
-  bool exact = !buf_mode && !all_mode;
+  bool exact = !buf_mode && !all_mode && !vec_mode;
 
-  if (all_mode) {
+  if (vec_mode) {
+    if (sh.woverflow) {
+      exact = true;
+    } else {
+      if (wave_id() != 0) return;  // one wave finishes the row; no block barrier follows
+      ListEntry* L = A.list + (size_t)i * kListCap;
+      if (!topk_vec_finish<DT>(V, k_eff, m, T, topp_on, P, d_ok ? d : -1, RowSplit<DT>(row, V),
+                               sh, out, pd, L))
+        exact = true;
+    }
+  } else if (all_mode) {
     if (need_sum_build) {
       const uint64_t cand = acc.mx == m ? (uint64_t)(uint32_t)(0x7FFFFFFF - acc.bi) : 0ull;
       out.a = 0x7FFFFFFF - (int)(uint32_t)block_max_u64(cand, sh.uscr);
@@ -364,9 +611,11 @@ __device__ __forceinline__ void row_pass(const VerifyArgs& A, RowShared& sh) {
     if (sh.woverflow) {
       exact = true;
     } else {
-      uint64_t theta = 0ull;  // certified prefix: entries >= the largest wave threshold
+      // certified prefix: every element above the largest wave threshold is held
+      float tstar = sh.wtau[0];
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) theta = sh.wtheta[w] > theta ? sh.wtheta[w] : theta;
+      for (int w = 1; w < kWaves; ++w) tstar = fmaxf(tstar, sh.wtau[w]);
+      const uint32_t tkey = fkey(tstar);
       n = merge_segments(sh);
       if (topk_mode) {
         if (n < k_eff) {
@@ -377,7 +626,7 @@ __device__ __forceinline__ void row_pass(const VerifyArgs& A, RowShared& sh) {
         }
       } else {
         int cert = 0;
-        for (int t = tid; t < n; t += kBlock) cert += sh.buf[t] >= theta ? 1 : 0;
+        for (int t = tid; t < n; t += kBlock) cert += (uint32_t)(sh.buf[t] >> 32) > tkey ? 1 : 0;
         cert = block_sum_i(cert, sh.iscr);
         const int use = cert < kTopPSortCap ? cert : kTopPSortCap;
         if (n > use) {
@@ -465,7 +714,7 @@ __device__ __forceinline__ void row_pass(const VerifyArgs& A, RowShared& sh) {
     if (!d_ok) {
       out.flags |= kRecBadDraft;
     } else {
-      const double q = (double)A.draft_probs[(size_t)i * (size_t)A.ld_q + d];
+      const double q = (double)qd;
       const double ratio = q > 0.0 ? fmin(1.0, pd / q) : (pd > 0.0 ? 1.0 : 0.0);
       const double u = accept_uniform(A.seed, rid, pos0 + (uint32_t)j);
       if (u < ratio) out.flags |= kRecAccept;
