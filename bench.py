@@ -60,6 +60,49 @@ def measured_traffic():
     return t.get("bytes_per_launch")
 
 
+def _counter_means(path, counter):
+    """Mean value per dispatch of `counter` for the row pass and for the
+    512 MiB calibration copy, from a rocprofv3 counter_collection.csv."""
+    import csv
+    rp, cp = [], []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            name, v = r["Kernel_Name"], float(r["Counter_Value"])
+            if "row_pass_kernel" in name:
+                rp.append(v)
+            elif "copyBuffer" in name and int(r["Grid_Size"]) > 65536:
+                cp.append(v)
+    if not rp or not cp:
+        raise SystemExit(f"{path}: no {counter} values for the row pass or the copy kernel")
+    return sum(rp) / len(rp), sum(cp) / len(cp), len(rp)
+
+
+def summarize_counters(fetch_csv, write_csv):
+    """HBM bytes per row-pass launch: each counter (KiB per dispatch) is scaled
+    by what it reads for a plain copy of known size (512 MiB read + written)."""
+    copy_kib = float(512 << 10)
+    f_rp, f_cp, n_f = _counter_means(fetch_csv, "FETCH_SIZE")
+    w_rp, w_cp, n_w = _counter_means(write_csv, "WRITE_SIZE")
+    f_scale, w_scale = copy_kib / f_cp, copy_kib / w_cp
+    fetch_b = f_rp * f_scale * 1024.0
+    write_b = w_rp * w_scale * 1024.0
+    out = {"source_hash": kernel_source_hash(),
+           "bytes_per_launch": round(fetch_b + write_b),
+           "fetch_bytes": round(fetch_b), "write_bytes": round(write_b),
+           "fetch_kib_raw": round(f_rp, 3), "write_kib_raw": round(w_rp, 3),
+           "copy_fetch_kib_raw": round(f_cp, 3), "copy_write_kib_raw": round(w_cp, 3),
+           "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+           "dispatches": [n_f, n_w],
+           "algorithmic_bytes": ROWS * VOCAB * 2}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
+
+
 def make_inputs(torch, B, nsets: int):
     """nsets independent input sets (logits, draft distributions, drafts)."""
     dev = torch.device("cuda:0")
@@ -132,11 +175,17 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--sets", type=int, default=3, help="rotating logits buffer sets")
-    ap.add_argument("--cpu-requests", type=int, default=48,
+    ap.add_argument("--cpu-requests", type=int, default=80,
                     help="requests in the CPU-baseline sample (0 skips it)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 512 MiB device copy (counter calibration)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
+                         "script with --calibrate-copy into profiles/row_pass_traffic.json")
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the verify step "
               "shards by request with no exchange, see DESIGN.md", file=sys.stderr)
@@ -159,30 +208,39 @@ def main():
         "row_flags": torch.empty(ROWS, dtype=torch.uint8, device="cuda"),
     }
 
+    calls = [B.PreparedRejectionSample(logits, qo, drafts, q, params, out=out)
+             for logits, q, drafts in sets]
+
     def step(i):
-        logits, q, drafts = sets[i % len(sets)]
-        B.rejection_sample(logits, qo, drafts, q, params, out=out)
+        calls[i % len(calls)]()
 
     if args.calibrate_copy:
         a = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
         b = torch.empty_like(a)
         torch.cuda.synchronize()
-        b.copy_(a)
+        b.copy_(a)   # a plain device copy of known size (runtime copy kernel)
         torch.cuda.synchronize()
         del a, b
 
-    B.profile_enable(True)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    B.profile_reset()
+    # pass 1: the step as a caller runs it (no timing instrumentation)
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    # pass 2: the same steps with each kernel's dispatch stamping HIP events on
+    # the call's stream (begin and end of the kernel); the completion signals
+    # add gaps between kernels, so this pass gives kernel durations only
+    print(f"[bench] timing {args.steps} steps with kernel events", file=sys.stderr, flush=True)
+    B.profile_enable(True)
+    B.profile_reset()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
     n_rp, ms_rp = B.profile_read("row_pass")
     n_fz, ms_fz = B.profile_read("finalize")
     B.profile_enable(False)

@@ -206,6 +206,47 @@ def rejection_sample(logits: torch.Tensor, qo_indptr: torch.Tensor, draft_tokens
     return out
 
 
+class PreparedRejectionSample:
+    """rejection_sample with its arguments checked and marshalled once: each
+    call is one foreign call on the stream current at construction.  The
+    tensors must stay alive and keep their shapes and storage."""
+
+    def __init__(self, logits, qo_indptr, draft_tokens, draft_probs, params: Params,
+                 verify_cap=None, out=None):
+        dt = _logits(logits)
+        rows, V = logits.shape
+        qo = _dev(qo_indptr, torch.int32, "qo_indptr")
+        R = qo.numel() - 1
+        d = _dev(draft_tokens, torch.int32, "draft_tokens")
+        if draft_probs is not None and (draft_probs.dtype != torch.float32 or
+                                        not draft_probs.is_cuda or draft_probs.stride(1) != 1):
+            raise ValueError("draft_probs must be a 2-D fp32 device tensor")
+        cap = _dev(verify_cap, torch.int32, "verify_cap")
+        dev = logits.device
+        if out is None:
+            out = {
+                "accept_len": torch.empty(R, dtype=torch.int32, device=dev),
+                "out_tokens": torch.empty(rows, dtype=torch.int32, device=dev),
+                "next_token": torch.empty(R, dtype=torch.int32, device=dev),
+                "row_flags": torch.empty(rows, dtype=torch.uint8, device=dev),
+            }
+        ws = workspace(rows, V, R, 0, dev)
+        ldq = draft_probs.stride(0) if draft_probs is not None else V
+        self.out = out
+        self._keep = (logits, qo, d, draft_probs, cap, params, ws)
+        self._fn = load().spec_verify_rejection_sample
+        self._args = (_ptr(logits), dt, logits.stride(0), V, _ptr(qo), R, rows, _ptr(d),
+                      _ptr(draft_probs), ldq, _ptr(cap), ctypes.byref(params.s),
+                      _ptr(out["accept_len"]), _ptr(out["out_tokens"]), _ptr(out["next_token"]),
+                      _ptr(out["row_flags"]), _ptr(ws), ws.numel(), _stream())
+
+    def __call__(self):
+        rc = self._fn(*self._args)
+        if rc:
+            _check(rc)
+        return self.out
+
+
 def plan_windows(confidence: torch.Tensor, budget: int, want_survival: bool = True):
     conf = _dev(confidence, torch.float32, "confidence")
     R, B = conf.shape

@@ -1,5 +1,6 @@
 // sv_api.hip -- host side of libspecverify: argument checks, workspace
 // carving, launches, status codes and optional per-kernel event timing.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
@@ -51,34 +52,37 @@ Prof& prof() {
   return p;
 }
 
-struct ProfScope {
-  int id;
-  hipStream_t s;
-  hipEvent_t a = nullptr, b = nullptr;
-  bool active = false;
-  ProfScope(int id_, hipStream_t s_) : id(id_), s(s_) {
-    Prof& p = prof();
+// Launch a kernel; with timing on, the dispatch itself stamps a pair of
+// pooled events (begin and end of the kernel, no extra stream packets).
+template <class... KArgs, class... Args>
+void launch(int id, void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t s,
+            Args... args) {
+  Prof& p = prof();
+  hipEvent_t ev[2] = {nullptr, nullptr};
+  {
     std::lock_guard<std::mutex> g(p.mu);
-    if (!p.on) return;
-    for (hipEvent_t* ev : {&a, &b}) {
-      if (!p.pool.empty()) {
-        *ev = p.pool.back();
-        p.pool.pop_back();
-      } else if (hipEventCreate(ev) != hipSuccess) {
-        return;
+    if (p.on) {
+      for (hipEvent_t& e : ev) {
+        if (!p.pool.empty()) {
+          e = p.pool.back();
+          p.pool.pop_back();
+        } else if (hipEventCreate(&e) != hipSuccess) {
+          e = nullptr;
+        }
       }
     }
-    (void)hipEventRecord(a, s);
-    active = true;
   }
-  ~ProfScope() {
-    if (!active) return;
-    (void)hipEventRecord(b, s);
-    Prof& p = prof();
+  if (ev[0] && ev[1]) {
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, ev[0], ev[1], 0, args...);
     std::lock_guard<std::mutex> g(p.mu);
-    p.pending.push_back({id, a, b});
+    p.pending.push_back({id, ev[0], ev[1]});
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
+    std::lock_guard<std::mutex> g(p.mu);
+    for (hipEvent_t e : ev)
+      if (e) p.pool.push_back(e);
   }
-};
+}
 
 int32_t check_launch(const char* what) {
   hipError_t e = hipGetLastError();
@@ -179,10 +183,7 @@ int32_t spec_verify_build_target_probs(const void* logits, sv_dtype dt, int64_t 
   sv::VerifyArgs A = base_args(logits, dt, ld_logits, vocab, qo_indptr, num_requests, num_rows,
                                sp, workspace);
   A.build = 1;
-  {
-    ProfScope ps(0, s);
-    hipLaunchKernelGGL(sv::row_pass_kernel, dim3(num_rows), dim3(sv::kRowBlock), 0, s, A);
-  }
+  launch(0, sv::row_pass_kernel, dim3(num_rows), dim3(sv::kRowBlock), s, A);
   if ((rc = check_launch("row pass"))) return rc;
   sv::BuildOutArgs B;
   B.probs = probs;
@@ -193,10 +194,7 @@ int32_t spec_verify_build_target_probs(const void* logits, sv_dtype dt, int64_t 
   B.kept_count = kept_count;
   B.kept_idx = kept_idx;
   B.kmax = kept_idx ? kmax : 0;
-  {
-    ProfScope ps(2, s);
-    hipLaunchKernelGGL(sv::build_out_kernel, dim3(num_rows), dim3(sv::kRowBlock), 0, s, A, B);
-  }
+  launch(2, sv::build_out_kernel, dim3(num_rows), dim3(sv::kRowBlock), s, A, B);
   return check_launch("build outputs");
 }
 
@@ -238,15 +236,9 @@ int32_t spec_verify_rejection_sample(const void* target_logits, sv_dtype dt, int
   A.next_token = next_token;
   A.row_flags = row_flags;
   if (!draft_probs) A.temperature = nullptr;  // SV_ALL_GREEDY: every request greedy
-  if (num_rows > 0) {
-    ProfScope ps(0, s);
-    hipLaunchKernelGGL(sv::row_pass_kernel, dim3(num_rows), dim3(sv::kRowBlock), 0, s, A);
-  }
+  if (num_rows > 0) launch(0, sv::row_pass_kernel, dim3(num_rows), dim3(sv::kRowBlock), s, A);
   if ((rc = check_launch("row pass"))) return rc;
-  {
-    ProfScope ps(1, s);
-    hipLaunchKernelGGL(sv::finalize_kernel, dim3(num_requests), dim3(sv::kRowBlock), 0, s, A);
-  }
+  launch(1, sv::finalize_kernel, dim3(num_requests), dim3(sv::kRowBlock), s, A);
   return check_launch("finalize");
 }
 
@@ -276,10 +268,7 @@ int32_t spec_verify_plan_windows(const float* confidence, int64_t ld_conf, int32
   A.qo_indptr = qo_indptr;
   A.survival = survival;
   A.keys = (uint64_t*)((char*)workspace + L.keys);
-  {
-    ProfScope ps(3, s);
-    hipLaunchKernelGGL(sv::plan_kernel, dim3(1), dim3(sv::kPlanBlock), 0, s, A);
-  }
+  launch(3, sv::plan_kernel, dim3(1), dim3(sv::kPlanBlock), s, A);
   return check_launch("planner");
 }
 
@@ -290,11 +279,8 @@ int32_t spec_verify_accept_prefix(const uint8_t* accepted, const int32_t* qo_ind
   if (num_requests == 0) return SV_OK;
   if (!accepted || !qo_indptr || !accept_len) return fail(SV_ERR_NULL, "null pointer");
   hipStream_t s = (hipStream_t)stream;
-  {
-    ProfScope ps(4, s);
-    hipLaunchKernelGGL(sv::accept_prefix_kernel, dim3((num_requests + 3) / 4), dim3(256), 0, s,
-                       accepted, qo_indptr, num_requests, verify_cap, accept_len);
-  }
+  launch(4, sv::accept_prefix_kernel, dim3((num_requests + 3) / 4), dim3(256), s, accepted,
+         qo_indptr, num_requests, verify_cap, accept_len);
   return check_launch("accept prefix");
 }
 

@@ -54,7 +54,9 @@ enum : int32_t {
   kRecAccept = 1,
   kRecTested = 2,
   kRecExact = 4,      // kept set came from the multi-pass exact path
-  kRecBadDraft = 8
+  kRecBadDraft = 8,
+  kRecSampled = 16,   // `sample` holds this row's emitted token if it is the emit row
+  kRecResidEmpty = 32 // that sample came from p: the residual was zero on the kept set
 };
 
 struct RowRec {
@@ -69,7 +71,7 @@ struct RowRec {
   int32_t flags;
   float lse;      // log sum exp(x / T_eff) over the row (build path)
   float pd;       // p(d) of the tested draft (diagnostic)
-  int32_t pad;
+  int32_t sample;  // kRecSampled: token emitted when this row is the request's emit row
 };
 static_assert(sizeof(RowRec) == 56, "RowRec layout");
 

@@ -226,6 +226,40 @@ __device__ void exact_kept_set(const void* row, int V, float m, float T, int k_e
 }
 
 // -------------------------------------------------------- row pass kernel
+// ----------------------------------------------------------------- races
+// Exponential race: winner = argmax over weight_v / E_v, E_v = -ln U_v; ties
+// go to the lower id.  Reduces (key, id) pairs across the block.
+struct RaceBest {
+  double key;
+  int id;
+};
+__device__ __forceinline__ bool race_better(double k1, int i1, double k2, int i2) {
+  return k1 > k2 || (k1 == k2 && i1 < i2);
+}
+__device__ inline RaceBest block_race_best(RaceBest b, RowShared& sh) {
+#pragma unroll
+  for (int dd = 32; dd >= 1; dd >>= 1) {
+    const double ok = __shfl_xor(b.key, dd, 64);
+    const int oi = __shfl_xor(b.id, dd, 64);
+    if (race_better(ok, oi, b.key, b.id)) { b.key = ok; b.id = oi; }
+  }
+  __syncthreads();
+  if (lane_id() == 0) {
+    sh.dscr[wave_id()] = b.key;
+    sh.iscr[wave_id()] = b.id;
+  }
+  __syncthreads();
+  RaceBest r = {sh.dscr[0], sh.iscr[0]};
+  for (int w = 1; w < kWaves; ++w)
+    if (race_better(sh.dscr[w], sh.iscr[w], r.key, r.id)) { r.key = sh.dscr[w]; r.id = sh.iscr[w]; }
+  __syncthreads();
+  return r;
+}
+
+__device__ __forceinline__ double race_e(uint64_t seed, uint32_t rid, uint32_t pos, uint32_t v) {
+  return -log(race_uniform(seed, rid, pos, 1u, v));
+}
+
 // LDS areas of the vector-candidate finish, past the wave regions (entries of
 // 8 bytes; each wave holds at most kThreshVec candidates when streaming ends
 // without overflow).
@@ -297,11 +331,21 @@ __device__ __forceinline__ int wave_shrink(uint64_t* src, int* srci, int n, int 
 // walk over the k-set (Top-k sampling, then nucleus sampling on the
 // truncated distribution) and the kept list.  Returns false when the row
 // needs the exact path (fewer than k finite elements).
+// One kept entry per lane of wave 0 after the vector-candidate finish.
+struct VecKept {
+  float x;    // logit
+  int id;     // token
+  double w;   // exp((x - m) / T); 0 past nkeep
+  double q;   // q(id), gathered when the row is tested
+  int nkeep;
+  double zn;
+};
+
 template <int DT>
 __device__ __forceinline__ bool topk_vec_finish(int V, int k, float m, float T, bool topp_on,
                                                 float P, int d, const RowSplit<DT>& sp,
-                                                RowShared& sh, RowRec& out, double& pd,
-                                                ListEntry* L) {
+                                                const float* qrow, RowShared& sh, RowRec& out,
+                                                double& pd, ListEntry* L, VecKept& kk) {
   constexpr int PE = Vec<DT>::kEpv;
   constexpr float kNegInf = -__builtin_huge_valf();
   const int l = lane_id();
@@ -429,6 +473,8 @@ __device__ __forceinline__ bool topk_vec_finish(int V, int k, float m, float T, 
   const bool valid = l < k;
   const float xv = entry_val(el);
   const int idv = entry_idx(el);
+  // q on the kept candidates, issued early: a rejected row races over p - q
+  const double qv = (qrow && valid) ? (double)qrow[idv] : 0.0;
   const double wgt = valid ? exp(((double)xv - (double)m) / (double)T) : 0.0;
   const double incl = wave_inclusive_sum(wgt);
   double excl = __shfl_up(incl, 1, 64);
@@ -452,7 +498,41 @@ __device__ __forceinline__ bool topk_vec_finish(int V, int k, float m, float T, 
     le.x = xv;
     L[l] = le;
   }
+  kk.x = xv;
+  kk.id = idv;
+  kk.w = l < nkeep ? wgt : 0.0;
+  kk.q = qv;
+  kk.nkeep = nkeep;
+  kk.zn = zn;
   return true;
+}
+
+// The race of list_race over the kept set held one entry per lane (wave 0):
+// weights p (residual = false) or max(0, p - q); an empty residual falls
+// back to p and sets `empty`.  Returns the token (-1 when every weight is 0).
+__device__ __forceinline__ int wave_kept_race(const VecKept& kk, bool residual, uint64_t seed,
+                                              uint32_t rid, uint32_t pos, bool& empty) {
+  const bool valid = lane_id() < kk.nkeep;
+  const double p = valid ? kk.w / kk.zn : 0.0;
+  const double e = valid ? race_e(seed, rid, pos, (uint32_t)kk.id) : 1.0;
+  auto best = [&](double wgt) {
+    RaceBest b = {-1.0, 0x7FFFFFFF};
+    if (valid && wgt > 0.0) { b.key = wgt / e; b.id = kk.id; }
+#pragma unroll
+    for (int dd = 32; dd >= 1; dd >>= 1) {
+      const double ok = __shfl_xor(b.key, dd, 64);
+      const int oi = __shfl_xor(b.id, dd, 64);
+      if (race_better(ok, oi, b.key, b.id)) { b.key = ok; b.id = oi; }
+    }
+    return b;
+  };
+  empty = false;
+  RaceBest b = best(residual ? p - kk.q : p);
+  if (residual && !(b.key > 0.0)) {
+    empty = true;
+    b = best(p);
+  }
+  return b.key > 0.0 ? b.id : -1;
 }
 
 template <int DT>
@@ -580,6 +660,7 @@ __device__ __forceinline__ void row_pass(const VerifyArgs& A, RowShared& sh) {
   const double Td = (double)T;
   double pd = 0.0;
   bool exact = !buf_mode && !all_mode && !vec_mode;
+  VecKept kk = {};
 
   if (vec_mode) {
     if (sh.woverflow) {
@@ -587,8 +668,9 @@ __device__ __forceinline__ void row_pass(const VerifyArgs& A, RowShared& sh) {
     } else {
       if (wave_id() != 0) return;  // one wave finishes the row; no block barrier follows
       ListEntry* L = A.list + (size_t)i * kListCap;
+      const float* qrow = tested ? A.draft_probs + (size_t)i * (size_t)A.ld_q : nullptr;
       if (!topk_vec_finish<DT>(V, k_eff, m, T, topp_on, P, d_ok ? d : -1, RowSplit<DT>(row, V),
-                               sh, out, pd, L))
+                               qrow, sh, out, pd, L, kk))
         exact = true;
     }
   } else if (all_mode) {
@@ -720,6 +802,16 @@ __device__ __forceinline__ void row_pass(const VerifyArgs& A, RowShared& sh) {
       if (u < ratio) out.flags |= kRecAccept;
     }
   }
+  if (vec_mode) {
+    // the token this row emits if it is its request's emit row: after a
+    // rejection (residual race; p for an out-of-range draft) or as the bonus
+    const bool rejected = tested && !(out.flags & kRecAccept);
+    if (rejected || (!A.build && j == cap_eff)) {
+      bool empty = false;
+      out.sample = wave_kept_race(kk, rejected && d_ok, A.seed, rid, pos0 + (uint32_t)j, empty);
+      out.flags |= kRecSampled | (empty ? kRecResidEmpty : 0);
+    }
+  }
   if (tid == 0) *rec = out;
 }
 
@@ -785,40 +877,6 @@ __device__ void resolve_pending(const VerifyArgs& A, int i, int r, int j, bool t
   if (threadIdx.x == 0) A.rec[i] = out;
   __threadfence_block();
   __syncthreads();
-}
-
-// ----------------------------------------------------------------- races
-// Exponential race: winner = argmax over weight_v / E_v, E_v = -ln U_v; ties
-// go to the lower id.  Reduces (key, id) pairs across the block.
-struct RaceBest {
-  double key;
-  int id;
-};
-__device__ __forceinline__ bool race_better(double k1, int i1, double k2, int i2) {
-  return k1 > k2 || (k1 == k2 && i1 < i2);
-}
-__device__ inline RaceBest block_race_best(RaceBest b, RowShared& sh) {
-#pragma unroll
-  for (int dd = 32; dd >= 1; dd >>= 1) {
-    const double ok = __shfl_xor(b.key, dd, 64);
-    const int oi = __shfl_xor(b.id, dd, 64);
-    if (race_better(ok, oi, b.key, b.id)) { b.key = ok; b.id = oi; }
-  }
-  __syncthreads();
-  if (lane_id() == 0) {
-    sh.dscr[wave_id()] = b.key;
-    sh.iscr[wave_id()] = b.id;
-  }
-  __syncthreads();
-  RaceBest r = {sh.dscr[0], sh.iscr[0]};
-  for (int w = 1; w < kWaves; ++w)
-    if (race_better(sh.dscr[w], sh.iscr[w], r.key, r.id)) { r.key = sh.dscr[w]; r.id = sh.iscr[w]; }
-  __syncthreads();
-  return r;
-}
-
-__device__ __forceinline__ double race_e(uint64_t seed, uint32_t rid, uint32_t pos, uint32_t v) {
-  return -log(race_uniform(seed, rid, pos, 1u, v));
 }
 
 // fp32 screening bound for the stream race: |log2 key_32 - log2 key| < kEta.
@@ -966,6 +1024,43 @@ __device__ void finalize(const VerifyArgs& A, RowShared& sh) {
   if (A.verify_cap) {
     int cv = A.verify_cap[r];
     cap_eff = cv < 0 ? 0 : (cv > gamma ? gamma : cv);
+  }
+  // fast path: every record read in one round by wave 0; taken when no row
+  // is pending and the emit row's token is already known
+  if (nr <= 64) {
+    if (wave_id() == 0) {
+      const int j = lane_id();
+      const bool in = j < nr;
+      const RowRec rj = in ? A.rec[s + j] : RowRec{};
+      const int dj = in ? A.draft_tokens[s + j] : -1;
+      const bool pend = __ballot(in && j <= cap_eff && rj.mode == kModePending) != 0;
+      const uint64_t mk = __ballot(j < cap_eff && !(rj.flags & kRecAccept));
+      const int L = mk ? __ffsll((unsigned long long)mk) - 1 : cap_eff;
+      const int fl = __shfl(rj.flags, L, 64);
+      const int md = __shfl(rj.mode, L, 64);
+      const int smp = __shfl((fl & kRecSampled) ? rj.sample : rj.a, L, 64);
+      const bool fast = !pend && ((fl & kRecSampled) || md == kModeGreedy);
+      if (fast) {
+        const bool empty = (fl & kRecSampled) && (fl & kRecResidEmpty);
+        if (in) {
+          A.out_tokens[s + j] = j < L ? dj : (j == L ? smp : -1);
+          if (A.row_flags) {
+            uint8_t f = 0;
+            if (j < cap_eff && (rj.flags & kRecAccept)) f |= 1;
+            if (j == L) f |= 2;
+            if (j == L && empty) f |= 32;
+            A.row_flags[s + j] = f;
+          }
+        }
+        if (j == 0) {
+          A.accept_len[r] = L;
+          A.next_token[r] = smp;
+        }
+      }
+      if (j == 0) sh.sel_exact = fast ? 1 : 0;
+    }
+    __syncthreads();
+    if (sh.sel_exact) return;
   }
   // rows of this request the streaming pass left to the exact path
   for (int j = 0; j <= cap_eff; ++j) {
