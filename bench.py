@@ -103,35 +103,100 @@ def summarize_counters(fetch_csv, write_csv):
     print(json.dumps(out))
 
 
-def make_inputs(torch, B, nsets: int):
-    """nsets independent input sets (logits, draft distributions, drafts)."""
+WORKLOADS = {
+    # name: (requests, rows per request, vocab, description)
+    "c1": (4, 5, 1024, "greedy, fp32 logits N(0,2), drafts = argmax with 30% replaced"),
+    "c2": (16, 6, 32000, "bf16 N(0,3), draft = target + N(0,1), T 0.7, top-k 50, top-p 0.9"),
+    "c3": (R_REQ, BLOCK, VOCAB, "bf16 N(0,4) + 8 at one index per row, draft = target + "
+                                "N(0,1), T 1.0, top-k 20, top-p 0.95"),
+    "c4": (512, 8, 129280, "bf16 N(0,3), draft = target + N(0,1); half the requests greedy, "
+                           "the rest T ~ U[0.3,1.2], top-k in {0,20,50}, top-p in {1,0.9}"),
+    "c5": (256, 17, 248320, "planner over 256 x 16 confidences sigmoid(N(1,1.5))*0.95^j, "
+                            "budget 1536 -> 1792 rows; bf16 as c3; T 0.8, top-k off, top-p 0.95"),
+}
+
+
+def make_inputs(torch, B, nsets: int, workload: str = "c3"):
+    """nsets independent input sets (logits, draft distributions, drafts) of
+    one workload, generated on the GPU; returns (sets, qo, params, rows, V,
+    extra) where extra holds the planner timing for c5."""
     dev = torch.device("cuda:0")
     g = torch.Generator(device=dev)
-    g.manual_seed(SEED)
-    rows = torch.arange(ROWS, device=dev)
-    qo = (torch.arange(R_REQ + 1, device=dev, dtype=torch.int32) * BLOCK).contiguous()
-    Tt = torch.full((R_REQ,), T, device=dev, dtype=torch.float32)
-    kt = torch.full((R_REQ,), TOPK, device=dev, dtype=torch.int32)
-    pt = torch.full((R_REQ,), TOPP, device=dev, dtype=torch.float32)
-    rid = torch.arange(R_REQ, device=dev, dtype=torch.int32)
-    pos0 = torch.randint(0, 4096, (R_REQ,), generator=g, device=dev, dtype=torch.int32)
-    params = B.Params(Tt, kt, pt, rid, pos0, SEED)
+    g.manual_seed(SEED if workload == "c3" else SEED + 1000 * int(workload[1:]))
+    R, nb, V, _ = WORKLOADS[workload]
+    extra = {}
+    if workload == "c5":
+        z = torch.randn((R, nb - 1), generator=g, device=dev) * 1.5 + 1.0
+        decay = 0.95 ** torch.arange(nb - 1, device=dev, dtype=torch.float32)
+        conf = (torch.sigmoid(z) * decay).contiguous()
+        budget = 1536
+        B.plan_windows(conf, budget)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(20):
+            _, qo, _ = B.plan_windows(conf, budget, want_survival=False)
+        torch.cuda.synchronize()
+        extra["planner_us"] = round((time.perf_counter() - t0) / 20 * 1e6, 2)
+        rows = min(budget, R * (nb - 1)) + R
+    else:
+        qo = (torch.arange(R + 1, device=dev, dtype=torch.int32) * nb).contiguous()
+        rows = R * nb
+    rid = torch.arange(R, device=dev, dtype=torch.int32)
+    pos0 = torch.randint(0, 4096, (R,), generator=g, device=dev, dtype=torch.int32)
+    if workload == "c1":
+        Tt = torch.zeros(R, device=dev)
+        kt = torch.zeros(R, device=dev, dtype=torch.int32)
+        pt = torch.ones(R, device=dev)
+    elif workload == "c2":
+        Tt = torch.full((R,), 0.7, device=dev)
+        kt = torch.full((R,), 50, device=dev, dtype=torch.int32)
+        pt = torch.full((R,), 0.9, device=dev)
+    elif workload == "c3":
+        Tt = torch.full((R,), T, device=dev)
+        kt = torch.full((R,), TOPK, device=dev, dtype=torch.int32)
+        pt = torch.full((R,), TOPP, device=dev)
+    elif workload == "c4":
+        greedy = torch.zeros(R, device=dev, dtype=torch.bool)
+        greedy[torch.randperm(R, generator=g, device=dev)[: R // 2]] = True
+        Tt = torch.rand(R, generator=g, device=dev) * 0.9 + 0.3
+        Tt[greedy] = 0.0
+        kt = torch.tensor([0, 20, 50], device=dev, dtype=torch.int32)[
+            torch.randint(0, 3, (R,), generator=g, device=dev)]
+        pt = torch.tensor([1.0, 0.9], device=dev)[torch.randint(0, 2, (R,), generator=g, device=dev)]
+    else:  # c5
+        Tt = torch.full((R,), 0.8, device=dev)
+        kt = torch.zeros(R, device=dev, dtype=torch.int32)
+        pt = torch.full((R,), 0.95, device=dev)
+    params = B.Params(Tt.float().contiguous(), kt.contiguous(), pt.float().contiguous(), rid,
+                      pos0, SEED if workload == "c3" else SEED + int(workload[1:]),
+                      all_greedy=(workload == "c1"))
+    scale = {"c1": 2.0, "c2": 3.0, "c3": 4.0, "c4": 3.0, "c5": 4.0}[workload]
     sets = []
     for s in range(nsets):
-        x = torch.randn((ROWS, VOCAB), generator=g, device=dev, dtype=torch.float32) * 4.0
-        peak = torch.randint(0, VOCAB, (ROWS,), generator=g, device=dev)
-        x[rows, peak] += 8.0
+        x = torch.randn((rows, V), generator=g, device=dev, dtype=torch.float32) * scale
+        if workload in ("c3", "c5"):
+            peak = torch.randint(0, V, (rows,), generator=g, device=dev)
+            x[torch.arange(rows, device=dev), peak] += 8.0
+        if workload == "c1":
+            logits = x.contiguous()
+            drafts = torch.argmax(x, dim=1).to(torch.int32)
+            swap = torch.rand(rows, generator=g, device=dev) < 0.3
+            drafts[swap] = torch.randint(0, V, (int(swap.sum()),), generator=g, device=dev,
+                                         dtype=torch.int32)
+            sets.append((logits, None, drafts.contiguous()))
+            continue
         logits = x.to(torch.bfloat16)
-        x += torch.randn((ROWS, VOCAB), generator=g, device=dev)
+        x += torch.randn((rows, V), generator=g, device=dev)
         draft = x.to(torch.bfloat16)
         del x
         # draft distributions: the library's own target-probs build on the draft logits
+        # (one-hot at the argmax for greedy requests)
         q = B.build_target_probs(draft, qo, params, want_probs=True)["probs"]
         del draft
         drafts = torch.multinomial(q, 1, generator=g).view(-1).to(torch.int32).contiguous()
         sets.append((logits, q, drafts))
     torch.cuda.synchronize()
-    return sets, qo, params
+    return sets, qo, params, rows, V, extra
 
 
 def cpu_baseline(n_requests: int):
@@ -175,6 +240,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--sets", type=int, default=3, help="rotating logits buffer sets")
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="c3",
+                    help="c3 (default) is the headline configuration; the others report the "
+                         "same line for the other four configurations")
     ap.add_argument("--cpu-requests", type=int, default=80,
                     help="requests in the CPU-baseline sample (0 skips it)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -199,13 +267,15 @@ def main():
         sys.exit(1)
     torch.cuda.set_device(0)
 
-    print(f"[bench] building inputs ({args.sets} logits sets)", file=sys.stderr, flush=True)
-    sets, qo, params = make_inputs(torch, B, args.sets)
+    wl = args.workload
+    R, _, V, desc = WORKLOADS[wl]
+    print(f"[bench] building {wl} inputs ({args.sets} logits sets)", file=sys.stderr, flush=True)
+    sets, qo, params, rows, V, extra = make_inputs(torch, B, args.sets, wl)
     out = {
-        "accept_len": torch.empty(R_REQ, dtype=torch.int32, device="cuda"),
-        "out_tokens": torch.empty(ROWS, dtype=torch.int32, device="cuda"),
-        "next_token": torch.empty(R_REQ, dtype=torch.int32, device="cuda"),
-        "row_flags": torch.empty(ROWS, dtype=torch.uint8, device="cuda"),
+        "accept_len": torch.empty(R, dtype=torch.int32, device="cuda"),
+        "out_tokens": torch.empty(rows, dtype=torch.int32, device="cuda"),
+        "next_token": torch.empty(R, dtype=torch.int32, device="cuda"),
+        "row_flags": torch.empty(rows, dtype=torch.uint8, device="cuda"),
     }
 
     calls = [B.PreparedRejectionSample(logits, qo, drafts, q, params, out=out)
@@ -245,13 +315,18 @@ def main():
     n_fz, ms_fz = B.profile_read("finalize")
     B.profile_enable(False)
     ms_per_step = elapsed * 1e3 / args.steps
-    rows_per_s = ROWS / (ms_per_step * 1e-3)
-    alg_bytes = ROWS * VOCAB * 2
+    rows_per_s = rows / (ms_per_step * 1e-3)
+    alg_bytes = rows * V * (4 if wl == "c1" else 2)
     kern_ms = ms_rp / max(n_rp, 1)
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
     acc = out["accept_len"].float().mean().item()   # of the last step's set
 
-    cpu = cpu_baseline(args.cpu_requests) if args.cpu_requests > 0 else None
+    cpu = cpu_baseline(args.cpu_requests) if (args.cpu_requests > 0 and wl == "c3") else None
+    config = {"workload": f"{wl}: {R} requests, {rows} rows x {V} vocab; {desc}",
+              "rows": rows, "requests": R, "vocab": V,
+              "draft_probs": "dense fp32, gathered" if wl != "c1" else "none (all greedy)",
+              "logit_sets": args.sets}
+    config.update(extra)
     line = {
         "metric": "verify rows/s and achieved HBM GB/s (% of peak) at 1024 rows x 248k vocab bf16",
         "value": round(rows_per_s, 1),
@@ -263,14 +338,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "f32" if wl == "c1" else "bf16",
         "data": "synthetic",
-        "config": {"workload": "prob_128x8_v248320_bf16", "rows": ROWS, "requests": R_REQ,
-                   "vocab": VOCAB, "temperature": T, "top_k": TOPK, "top_p": TOPP,
-                   "draft_probs": "dense fp32, gathered", "logit_sets": args.sets},
+        "config": config,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": measured_traffic(),
+                     "traffic": measured_traffic() if wl == "c3" else None,
                      "kernel": "row_pass_kernel", "kernel_ms": round(kern_ms, 5),
                      "algorithmic_bytes": alg_bytes,
                      "finalize_ms": round(ms_fz / max(n_fz, 1), 5)},

@@ -790,6 +790,31 @@ __device__ __forceinline__ void for_each_element(const void* row, int V, F&& f) 
   if (sp.tail0 + tid < V) f(Vec<DT>::load1(row, sp.tail0 + tid), sp.tail0 + tid);
 }
 
+// As for_each_element with a small register footprint: one 32-bit word of a
+// vector at a time (the exact path runs inside the streaming kernel).
+template <int DT, class F>
+__device__ __forceinline__ void for_each_element_lean(const void* row, int V, F&& f) {
+  constexpr int P = Vec<DT>::kEpv;
+  const RowSplit<DT> sp(row, V);
+  const int tid = threadIdx.x;
+  if (tid < sp.head) f(Vec<DT>::load1(row, tid), tid);
+  for (int vi = tid; vi < sp.nvec; vi += kBlock) {
+    const uint4 v = __ldg(sp.vbase + vi);
+    const int b = sp.head + vi * P;
+#pragma unroll 1
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t w = q == 0 ? v.x : (q == 1 ? v.y : (q == 2 ? v.z : v.w));
+      if (DT == 1) {
+        f(bf16_lo(w), b + 2 * q);
+        f(bf16_hi(w), b + 2 * q + 1);
+      } else {
+        f(__uint_as_float(w), b + q);
+      }
+    }
+  }
+  if (sp.tail0 + tid < V) f(Vec<DT>::load1(row, sp.tail0 + tid), sp.tail0 + tid);
+}
+
 // Visit every element in tiles of increasing ids with a block-wide rank of the
 // elements for which `tie(x)` holds: f(x, id, rank) where rank counts tie
 // elements with a smaller id.  Every thread must call it.

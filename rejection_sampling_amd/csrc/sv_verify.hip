@@ -92,7 +92,7 @@ __device__ void exact_kept_set(const void* row, int V, float m, float T, int k_e
     for (int b = threadIdx.x; b < 256; b += kBlock) { sh.whist[0][b] = 0u; mass[b] = 0ull; }
     __syncthreads();
     const bool fst = first;
-    for_each_element<DT>(row, V, [&](float x, int i) {
+    for_each_element_lean<DT>(row, V, [&](float x, int i) {
       const uint32_t key = fkey(x);
       if (fst) {
         if (x == m && i < amin) amin = i;
@@ -211,7 +211,7 @@ __device__ void exact_kept_set(const void* row, int V, float m, float T, int k_e
 
   if (first) {
     // no histogram pass ran (cannot happen: callers need top-k or top-p)
-    for_each_element<DT>(row, V, [&](float x, int i) {
+    for_each_element_lean<DT>(row, V, [&](float x, int i) {
       if (x == m && i < amin) amin = i;
       if (d >= 0 && i < d && fkey(x) == keyd) ++tied;
     });
@@ -536,6 +536,10 @@ __device__ __forceinline__ int wave_kept_race(const VecKept& kk, bool residual, 
 }
 
 template <int DT>
+__device__ __forceinline__ void resolve_pending(const VerifyArgs& A, int i, int r, int j,
+                                                bool tested, RowShared& sh);
+
+template <int DT>
 __device__ __forceinline__ void row_pass(const VerifyArgs& A, RowShared& sh) {
   const int i = blockIdx.x;
   const int tid = threadIdx.x;
@@ -666,12 +670,17 @@ __device__ __forceinline__ void row_pass(const VerifyArgs& A, RowShared& sh) {
     if (sh.woverflow) {
       exact = true;
     } else {
-      if (wave_id() != 0) return;  // one wave finishes the row; no block barrier follows
-      ListEntry* L = A.list + (size_t)i * kListCap;
-      const float* qrow = tested ? A.draft_probs + (size_t)i * (size_t)A.ld_q : nullptr;
-      if (!topk_vec_finish<DT>(V, k_eff, m, T, topp_on, P, d_ok ? d : -1, RowSplit<DT>(row, V),
-                               qrow, sh, out, pd, L, kk))
-        exact = true;
+      // one wave finishes the row; the others wait only to join an exact fallback
+      if (wave_id() == 0) {
+        ListEntry* L = A.list + (size_t)i * kListCap;
+        const float* qrow = tested ? A.draft_probs + (size_t)i * (size_t)A.ld_q : nullptr;
+        const bool ok = topk_vec_finish<DT>(V, k_eff, m, T, topp_on, P, d_ok ? d : -1,
+                                            RowSplit<DT>(row, V), qrow, sh, out, pd, L, kk);
+        if (lane_id() == 0) sh.found = ok ? 1 : 0;
+      }
+      __syncthreads();
+      if (!sh.found) exact = true;
+      else if (wave_id() != 0) return;
     }
   } else if (all_mode) {
     if (need_sum_build) {
@@ -783,10 +792,12 @@ __device__ __forceinline__ void row_pass(const VerifyArgs& A, RowShared& sh) {
   }
 
   if (exact) {
-    // resolved by resolve_pending(): the multi-pass exact path needs more
-    // registers than the streaming kernel should carry
+    // the multi-pass exact path, run by this row's workgroup
     out.mode = kModePending;
     if (tid == 0) *rec = out;
+    __threadfence_block();
+    __syncthreads();
+    resolve_pending<DT>(A, i, r, j, tested, sh);
     return;
   }
 
@@ -826,8 +837,8 @@ __global__ __launch_bounds__(kBlock) void row_pass_kernel(VerifyArgs A) {
 // overflow, a top-p mass beyond the buffer, or top-k above the buffer), then
 // p(d) and the ratio test of its draft.  Rewrites the row record.
 template <int DT>
-__device__ void resolve_pending(const VerifyArgs& A, int i, int r, int j, bool tested,
-                                RowShared& sh) {
+__device__ __forceinline__ void resolve_pending(const VerifyArgs& A, int i, int r, int j,
+                                                bool tested, RowShared& sh) {
   RowRec out = A.rec[i];
   const int V = A.vocab;
   const float T = A.temperature ? A.temperature[r] : 0.0f;
