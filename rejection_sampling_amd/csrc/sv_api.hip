@@ -172,7 +172,7 @@ int32_t spec_verify_build_target_probs(const void* logits, sv_dtype dt, int64_t 
   int32_t rc = check_common(logits, dt, ld_logits, num_rows, vocab, qo_indptr, num_requests, sp);
   if (rc) return rc;
   if (probs && ld_probs < vocab) return fail(SV_ERR_SHAPE, "ld_probs < vocab");
-  if (kmax < 0 || kmax > sv::kListCap) return fail(SV_ERR_SHAPE, "kmax must be in [0, 1024]");
+  if (kmax < 0 || kmax > sv::kKmaxCap) return fail(SV_ERR_SHAPE, "kmax must be in [0, 1024]");
   if (kept_idx && kmax == 0) return fail(SV_ERR_SHAPE, "kept_idx needs kmax > 0");
   if (num_rows == 0) return SV_OK;
   if (!workspace) return fail(SV_ERR_WORKSPACE, "workspace is NULL");

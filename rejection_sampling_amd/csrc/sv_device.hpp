@@ -32,11 +32,12 @@ constexpr int kWaves = kBlock / 64;
 constexpr int kCap = 4096;                // LDS candidate buffer (64-bit entries)
 constexpr int kKeepTopP = 384;            // candidates kept per wave for top-k-off rows
 constexpr int kThreshTopP = 640;          // per-wave compaction limit for those rows
-constexpr int kTopPSortCap = 1024;        // certified candidates sorted for top-p
+constexpr int kTopPEnd = 512;             // top-p vector candidates per wave after the stream
 constexpr int kTopkFast = 256;            // largest k on the buffer path
 constexpr int kTopkVec = 64;              // largest k on the vector-candidate path
 constexpr int kThreshVec = 128;           // per-wave compaction limit there (>= 2 kTopkVec)
-constexpr int kListCap = 1024;            // kept-set entries stored per row
+constexpr int kListCap = 4096;            // kept-set entries stored per row (workspace)
+constexpr int kKmaxCap = 1024;            // largest kmax of the target-probs build
 constexpr float kLog2e = 1.4426950408889634f;
 
 // Row modes recorded by the row pass.

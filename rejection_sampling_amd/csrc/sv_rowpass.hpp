@@ -395,6 +395,43 @@ __device__ __forceinline__ uint32_t wave_threshold_key(uint32_t b1, uint32_t b2,
   return keep <= 32 ? wave_kth_lane_key(b1, keep) : wave_kth_lane_key2(b1, b2, keep);
 }
 
+// k-th largest of one key per lane (lanes with ok == false hold none), by a
+// ballot radix over the 32 key bits; 0 when fewer than k keys are held.
+__device__ __forceinline__ uint32_t wave_kth_key_ballot(uint32_t key, bool ok, int k) {
+  uint32_t t = 0u;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t cand = t | (1u << b);
+    if (__popcll(__ballot(ok && key >= cand)) >= k) t = cand;
+  }
+  return t;
+}
+
+// A key t such that lo <= #(entries of seg[0, n) with key >= t) <= hi,
+// estimated from a 64-entry sample and checked by one counting pass (a few
+// attempts); 0 when none was found.  Wave-local, n >= hi.
+__device__ __forceinline__ uint32_t wave_sample_threshold(const uint64_t* seg, int n, int lo,
+                                                          int hi) {
+  const int l = lane_id();
+  const uint32_t smp = (uint32_t)(seg[(int)(((long long)l * n) >> 6)] >> 32);
+  int target = (lo + hi) >> 1;
+#pragma unroll 1
+  for (int att = 0; att < 4; ++att) {
+    int rnk = (int)(((long long)target * 64 + n - 1) / n);
+    rnk = rnk < 1 ? 1 : (rnk > 64 ? 64 : rnk);
+    const uint32_t t = wave_kth_key_ballot(smp, true, rnk);
+    int cnt = 0;
+    for (int e0 = 0; e0 < n; e0 += 64) {
+      const int e = e0 + l;
+      cnt += __popcll(__ballot(e < n && (uint32_t)(seg[e] >> 32) >= t));
+    }
+    if (cnt >= lo && cnt <= hi) return t;
+    // move the target the other way by the observed miss
+    target = cnt < lo ? target + (lo - cnt) + (hi - lo) / 4 : target - (cnt - hi) - (hi - lo) / 4;
+    if (target < 1) target = 1;
+  }
+  return 0u;
+}
+
 // Keep the entries of seg[0, n) whose key is >= kmin, in place (wave-local),
 // moving the companion array along when given; returns how many remain.
 template <class D = uint4>
@@ -539,22 +576,34 @@ __device__ __forceinline__ void tile_buffer(const float* x, const float* um, flo
 // under that order, since every vector ahead of one holding a top-k element
 // owns a distinct better element.  Same shrinking rule as wave_tile_end
 // (keep <= 64), data moving with the entries; capacity kVecCap.
+// dat == nullptr: entries only (capacity kWaveCap), for keeps beyond 64 with
+// thresholds shared across the block's waves as in wave_tile_end.
 __device__ __forceinline__ void wave_tile_end_vec(WaveBuf& wb, uint64_t* seg, uint4* dat,
-                                                  uint32_t* hist) {
-  if (wb.count > kVecCap) {
+                                                  uint32_t* hist, RowShared& sh) {
+  const int cap = dat ? kVecCap : kWaveCap;
+  if (wb.count > cap) {
     wb.tau = __builtin_huge_valf();  // overflowed: admit nothing more
   } else if (wb.count > wb.thresh) {
     wave_lds_sync();
     int n = wb.count;
-    uint32_t b1 = 0u, b2 = 0u;
-    for (int e = lane_id(); e < n; e += 64) {
-      const uint32_t k = (uint32_t)(seg[e] >> 32);
-      if (k > b1) { b2 = b1; b1 = k; } else if (k > b2) { b2 = k; }
-    }
-    const uint32_t tk = wave_threshold_key(b1, b2, wb.keep);
-    if (tk != 0u) {
-      n = wave_keep_ge(seg, n, tk, dat);
-      wb.tau = key_to_float(tk);
+    if (wb.keep <= 64) {
+      uint32_t b1 = 0u, b2 = 0u;
+      for (int e = lane_id(); e < n; e += 64) {
+        const uint32_t k = (uint32_t)(seg[e] >> 32);
+        if (k > b1) { b2 = b1; b1 = k; } else if (k > b2) { b2 = k; }
+      }
+      const uint32_t tk = wave_threshold_key(b1, b2, wb.keep);
+      if (tk != 0u) {
+        n = wave_keep_ge(seg, n, tk, dat);
+        wb.tau = key_to_float(tk);
+      }
+    } else {
+      // keep between `keep` and halfway to the limit, by a sampled threshold
+      const uint32_t tk = wave_sample_threshold(seg, n, wb.keep, (wb.keep + wb.thresh) >> 1);
+      if (tk != 0u) {
+        n = wave_keep_ge(seg, n, tk, dat);
+        wb.tau = key_to_float(tk);
+      }
     }
     if (n > wb.thresh) {
       const uint64_t th = wave_compact(seg, hist, n, wb.keep, dat);
@@ -562,30 +611,40 @@ __device__ __forceinline__ void wave_tile_end_vec(WaveBuf& wb, uint64_t* seg, ui
       wb.tau = entry_val(th);
     }
     wb.count = n;
+    if (wb.share && lane_id() == 0) sh.wtau[wave_id()] = wb.tau;
     wave_lds_sync();
+  }
+  if (wb.share) {
+    float t = sh.wtau[0];
+#pragma unroll
+    for (int q = 1; q < kWaves; ++q) t = fmaxf(t, sh.wtau[q]);
+    wb.tsh = t;
   }
 }
 
 // raw(u) gives the u-th vector's 16 bytes (kept or rebuilt from its elements).
-template <int U, class Raw>
+template <int U, bool DATA, class Raw>
 __device__ __forceinline__ void tile_buffer_vec(Raw&& raw, const float* um, float cm, int vi0,
                                                 WaveBuf& wb, uint64_t* seg, uint4* dat,
-                                                uint32_t* hist) {
-  if (__ballot(cm > wb.tau)) {
+                                                uint32_t* hist, RowShared& sh) {
+  constexpr int cap = DATA ? kVecCap : kWaveCap;
+  if (__ballot(cm > wb.tau && cm >= wb.tsh)) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const bool pass = um[u] > wb.tau;
+      const bool pass = um[u] > wb.tau && um[u] >= wb.tsh;
       const uint64_t m = __ballot(pass);
       if (pass) {
         const int slot = wb.count + lanes_below(m);
-        if (slot < kVecCap) {
+        if (slot < cap) {
           seg[slot] = make_entry(um[u], vi0 + u * kBlock);
-          dat[slot] = raw(u);
+          if (DATA) dat[slot] = raw(u);
         }
       }
       wb.count += __popcll(m);
     }
-    wave_tile_end_vec(wb, seg, dat, hist);
+    wave_tile_end_vec(wb, seg, DATA ? dat : nullptr, hist, sh);
+  } else if (wb.share) {
+    wave_tile_end_vec(wb, seg, DATA ? dat : nullptr, hist, sh);
   }
 }
 
@@ -628,18 +687,19 @@ __device__ __forceinline__ int stream_tiles(const RowSplit<DT>& sp, int v0, F&& 
 // vectors by their max instead; their first full tile admits only vectors
 // that `keep` lanes' best vectors reach.  Head and tail elements are not
 // buffered in VEC mode.
-template <int DT, bool BUF, bool SUM, bool ARG, bool VEC = false>
+template <int DT, bool BUF, bool SUM, bool ARG, int VEC = 0>
 __device__ __forceinline__ void stream_row(const void* row, int V, float c, int keep, int thresh,
                                            int ramp, RowShared& sh, StreamAcc& a) {
   constexpr int P = Vec<DT>::kEpv;
   constexpr int U = SV_UNROLL;
   constexpr float kNegInf = -__builtin_huge_valf();
+  constexpr bool VD = VEC == 1;  // vector candidates with their raw bytes (small keep)
   static_assert(!(BUF && VEC), "one buffer kind per row");
-  static_assert(!(VEC && (SUM || ARG)), "vector candidates stream alone");
+  static_assert(!(VD && (SUM || ARG)), "vector candidates with data stream alone");
   const RowSplit<DT> sp(row, V);
   const int tid = threadIdx.x;
   const int w = wave_id();
-  uint64_t* seg = sh.buf + w * (VEC ? kVecStride : kWaveCap);
+  uint64_t* seg = sh.buf + w * (VD ? kVecStride : kWaveCap);
   uint4* dat = (uint4*)(sh.buf + w * kVecStride + kVecDatOff);
   uint32_t* hist = sh.whist[w];
   a.bi = 0x7FFFFFFF;
@@ -653,7 +713,7 @@ __device__ __forceinline__ void stream_row(const void* row, int V, float c, int 
   wb.tsh = kNegInf;
   wb.keep = keep;
   wb.thresh = thresh;
-  wb.share = BUF;
+  wb.share = BUF || VEC == 2;
 
   // U vectors from vector vb (all in range) -> elements, vector maxima, tile max
   auto unpack = [&](const uint4* v, int vb, float* x, float* um, int* ids) {
@@ -673,12 +733,12 @@ __device__ __forceinline__ void stream_row(const void* row, int V, float c, int 
     int ids[1] = {i};
     tile_stats<SUM, ARG, 1, 1>(x, ids, x[0], c, a);
     if (BUF) tile_buffer<1, 1>(x, x, x[0], ids, wb, seg, hist, sh);
-    if (VEC && in) sh.endx[slot] = x[0];  // kept aside for the finish
+    if (VD && in) sh.endx[slot] = x[0];  // kept aside for the finish
   };
   if (sp.head > 0) scalar(tid, tid < sp.head, tid);
 
   int v0 = 0;
-  if (VEC && sp.nvec >= U * kBlock) {
+  if (VD && sp.nvec >= U * kBlock) {
     // first tile: admit vectors whose max reaches the threshold key of the
     // lanes' best two vector maxima
     uint4 v[U];
@@ -710,7 +770,7 @@ __device__ __forceinline__ void stream_row(const void* row, int V, float c, int 
       wb.count += __popcll(m);
     }
     wb.tau = t0;  // later vectors with max equal to t0 have larger ids: strict from here
-    wave_tile_end_vec(wb, seg, dat, hist);
+    wave_tile_end_vec(wb, seg, dat, hist, sh);
     v0 = U * kBlock;
   }
   if (BUF) {
@@ -744,7 +804,9 @@ __device__ __forceinline__ void stream_row(const void* row, int V, float c, int 
     const float cm = unpack(v, vb, x, um, ids);
     tile_stats<SUM, ARG, U, P>(x, ids, cm, c, a);
     if (BUF) tile_buffer<U, P>(x, um, cm, ids, wb, seg, hist, sh);
-    if (VEC) tile_buffer_vec<U>([&](int u) { return v[u]; }, um, cm, vb + tid, wb, seg, dat, hist);
+    if (VEC)
+      tile_buffer_vec<U, VD>([&](int u) { return v[u]; }, um, cm, vb + tid, wb, seg, dat, hist,
+                             sh);
   });
   // ragged last tiles of the body: vectors [v0, nvec), one per thread
   for (; v0 < sp.nvec; v0 += kBlock) {
@@ -762,11 +824,26 @@ __device__ __forceinline__ void stream_row(const void* row, int V, float c, int 
     const float cm = vec_max<P>(x);
     tile_stats<SUM, ARG, 1, P>(x, ids, cm, c, a);
     if (BUF) tile_buffer<1, P>(x, &cm, cm, ids, wb, seg, hist, sh);
-    if (VEC) tile_buffer_vec<1>([&](int) { return rv; }, &cm, cm, vi, wb, seg, dat, hist);
+    if (VEC) tile_buffer_vec<1, VD>([&](int) { return rv; }, &cm, cm, vi, wb, seg, dat, hist, sh);
   }
   if (sp.tail0 < V) scalar(sp.tail0 + tid, sp.tail0 + tid < V, 8 + tid);
+  if (VEC == 2 && wb.count > kTopPEnd && wb.count <= kWaveCap) {
+    // at most kTopPEnd per wave at the end, so the block's certified vectors fit
+    wave_lds_sync();
+    int n = wb.count;
+    const uint32_t tk = wave_sample_threshold(seg, n, keep, kTopPEnd);
+    if (tk != 0u) {
+      n = wave_keep_ge(seg, n, tk);
+      wb.tau = key_to_float(tk);
+    } else {
+      wb.tau = entry_val(wave_compact(seg, hist, n, keep));
+      n = keep;
+    }
+    wb.count = n;
+    wave_lds_sync();
+  }
   if ((BUF || VEC) && lane_id() == 0) {
-    const int cap = VEC ? kVecCap : kWaveCap;
+    const int cap = VD ? kVecCap : kWaveCap;
     sh.wcount[w] = wb.count > cap ? cap : wb.count;
     sh.wtau[w] = wb.tau;
     if (wb.count > cap) atomicOr(&sh.woverflow, 1);

@@ -439,34 +439,34 @@ __device__ __forceinline__ bool topk_vec_finish(int V, int k, float m, float T, 
   const int is = hs ? l : sp.tail0 + l - 32;
   wave_lds_sync();  // gather area read: E may overwrite it
 
-  int ne = 0;
+  // each lane counts its passing elements; one wave scan gives its slots
+  int ecnt = 0;
 #pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    if (!__ballot(has[r])) continue;
+  for (int r = 0; r < 2; ++r)
 #pragma unroll
-    for (int e = 0; e < PE; ++e) {
-      const bool pass = has[r] && x[r][e] >= tv;
-      const uint64_t mk = __ballot(pass);
-      const int slot = ne + lanes_below(mk);
-      if (pass && slot < kVecElemCap) E[slot] = make_entry(x[r][e], id0[r] + e);
-      ne += __popcll(mk);
-    }
-  }
-  {
-    const bool pass = (hs || ts) && xs >= tv;
-    const uint64_t mk = __ballot(pass);
-    const int slot = ne + lanes_below(mk);
-    if (pass && slot < kVecElemCap) E[slot] = make_entry(xs, is);
-    ne += __popcll(mk);
-  }
+    for (int e = 0; e < PE; ++e) ecnt += (has[r] && x[r][e] >= tv) ? 1 : 0;
+  const bool sp_in = (hs || ts) && xs >= tv;
+  ecnt += sp_in ? 1 : 0;
+  const int eincl = wave_inclusive_sum(ecnt);
+  const int ne = __shfl(eincl, 63, 64);
   if (ne < k || ne > kVecElemCap) return false;  // too few finite, or a pile of ties
-  wave_lds_sync();
-  if (ne > 64) ne = wave_shrink(E, nullptr, ne, k, hist);
-  if (ne > 64) {
-    wave_compact(E, hist, ne, k);
-    ne = k;
+  {
+    int slot = eincl - ecnt;
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int e = 0; e < PE; ++e)
+        if (has[r] && x[r][e] >= tv) E[slot++] = make_entry(x[r][e], id0[r] + e);
+    if (sp_in) E[slot] = make_entry(xs, is);
   }
-  wave_rank_top(E, nullptr, ne, k, S, nullptr);
+  wave_lds_sync();
+  int nel = ne;
+  if (nel > 64) nel = wave_shrink(E, nullptr, nel, k, hist);
+  if (nel > 64) {
+    wave_compact(E, hist, nel, k);
+    nel = k;
+  }
+  wave_rank_top(E, nullptr, nel, k, S, nullptr);
   const uint64_t el = l < k ? S[l] : 0ull;
   if (!(entry_val(S[k - 1]) > kNegInf)) return false;  // fewer than k finite elements
 
@@ -538,6 +538,115 @@ __device__ __forceinline__ int wave_kept_race(const VecKept& kk, bool residual, 
 template <int DT>
 __device__ __forceinline__ void resolve_pending(const VerifyArgs& A, int i, int r, int j,
                                                 bool tested, RowShared& sh);
+
+// Top-p rows (top-k off): every element above the largest wave threshold T*
+// lies in a candidate vector whose max is above T* (each wave dropped only
+// vectors at or below its own threshold).  Those vectors are re-read and their
+// elements above T* written to sh.buf[0, n) as entries; returns n, or -1 when
+// they do not fit (the row then takes the exact path).  Block level.
+constexpr int kMatVecPerThread = 8;
+template <int DT>
+__device__ __forceinline__ int topp_certified(const void* row, int V, RowShared& sh) {
+  constexpr int PE = Vec<DT>::kEpv;
+  const RowSplit<DT> sp(row, V);
+  const int tid = threadIdx.x, w = wave_id();
+  float tstar = sh.wtau[0];
+#pragma unroll
+  for (int q = 1; q < kWaves; ++q) tstar = fmaxf(tstar, sh.wtau[q]);
+  const uint32_t tkey = fkey(tstar);
+  {
+    uint64_t* seg = sh.buf + w * kWaveCap;
+    int nw = sh.wcount[w];
+    nw = tkey == 0xFFFFFFFFu ? 0 : wave_keep_ge(seg, nw, tkey + 1u);
+    __syncthreads();  // every wave has read its count
+    if (lane_id() == 0) sh.wcount[w] = nw;
+  }
+  __syncthreads();
+  int base[kWaves];
+  int nv = 0;
+#pragma unroll
+  for (int q = 0; q < kWaves; ++q) {
+    base[q] = nv;
+    nv += sh.wcount[q];
+  }
+  if (nv > kBlock * kMatVecPerThread) return -1;
+  uint4 raw[kMatVecPerThread];
+  int vid[kMatVecPerThread];
+  int cnt = 0;
+#pragma unroll
+  for (int r = 0; r < kMatVecPerThread; ++r) {
+    const int g = r * kBlock + tid;
+    vid[r] = -1;
+    raw[r] = make_uint4(0u, 0u, 0u, 0u);
+    if (g < nv) {
+      int q = 0;
+#pragma unroll
+      for (int t = 1; t < kWaves; ++t)
+        if (g >= base[t]) q = t;
+      vid[r] = entry_idx(sh.buf[q * kWaveCap + (g - base[q])]);
+      raw[r] = __ldg(sp.vbase + vid[r]);
+    }
+  }
+  // the unvectorised head and tail elements are candidates too
+  const int ntail = V - sp.tail0;
+  const bool hs = tid < sp.head;
+  const bool ts = tid >= 8 && tid - 8 < ntail;
+  const int is = hs ? tid : sp.tail0 + tid - 8;
+  const float xs = (hs || ts) ? Vec<DT>::load1(row, is) : 0.0f;
+  const bool sp_in = (hs || ts) && xs > tstar;
+#pragma unroll
+  for (int r = 0; r < kMatVecPerThread; ++r) {
+    float x[PE];
+    Vec<DT>::unpack(raw[r], x);
+#pragma unroll
+    for (int e = 0; e < PE; ++e) cnt += (vid[r] >= 0 && x[e] > tstar) ? 1 : 0;
+  }
+  cnt += sp_in ? 1 : 0;
+  int total;
+  int pos = block_exclusive_sum(cnt, sh.iscr, &total);  // every candidate entry read
+  if (total > kCap) return -1;
+#pragma unroll
+  for (int r = 0; r < kMatVecPerThread; ++r) {
+    float x[PE];
+    Vec<DT>::unpack(raw[r], x);
+    const int id0 = sp.head + vid[r] * PE;
+#pragma unroll
+    for (int e = 0; e < PE; ++e)
+      if (vid[r] >= 0 && x[e] > tstar) sh.buf[pos++] = make_entry(x[e], id0 + e);
+  }
+  if (sp_in) sh.buf[pos++] = make_entry(xs, is);
+  __syncthreads();
+  return total;
+}
+
+// Race of list_race over the sorted kept entries sh.buf[0, nkeep) (block
+// level); an all-zero residual falls back to p and sets `empty`.
+__device__ __forceinline__ int block_kept_race(int nkeep, float m, double zn, float T,
+                                               const float* qrow, bool residual, uint64_t seed,
+                                               uint32_t rid, uint32_t pos, RowShared& sh,
+                                               bool& empty) {
+  const double Td = T;
+  auto run = [&](bool resid) {
+    RaceBest b = {-1.0, 0x7FFFFFFF};
+    for (int t = threadIdx.x; t < nkeep; t += kBlock) {
+      const uint64_t en = sh.buf[t];
+      const int id = entry_idx(en);
+      double wgt = exp(((double)entry_val(en) - (double)m) / Td) / zn;
+      if (resid) wgt = wgt - (double)qrow[id];
+      if (!(wgt > 0.0)) continue;
+      const double key = wgt / race_e(seed, rid, pos, (uint32_t)id);
+      if (race_better(key, id, b.key, b.id)) { b.key = key; b.id = id; }
+    }
+    return block_race_best(b, sh);
+  };
+  empty = false;
+  RaceBest b = run(residual);
+  if (residual && !(b.key > 0.0)) {
+    empty = true;
+    b = run(false);
+  }
+  return b.key > 0.0 ? b.id : -1;
+}
 
 template <int DT>
 __device__ __forceinline__ void row_pass(const VerifyArgs& A, RowShared& sh) {
@@ -642,10 +751,12 @@ __device__ __forceinline__ void row_pass(const VerifyArgs& A, RowShared& sh) {
     ramp = 2;
   }
   if (vec_mode) {
-    stream_row<DT, false, false, false, true>(row, V, c, k_eff, kThreshVec, 0, sh, acc);
+    stream_row<DT, false, false, false, 1>(row, V, c, k_eff, kThreshVec, 0, sh, acc);
   } else if (all_mode) {
     if (need_sum_build) stream_row<DT, false, true, true>(row, V, c, 1, 1, 0, sh, acc);
     else stream_row<DT, false, true, false>(row, V, c, 1, 1, 0, sh, acc);
+  } else if (topp_mode) {
+    stream_row<DT, false, true, false, 2>(row, V, c, keep, thresh, 0, sh, acc);
   } else if (buf_mode) {
     if (need_sum) stream_row<DT, true, true, false>(row, V, c, keep, thresh, ramp, sh, acc);
     else stream_row<DT, true, false, false>(row, V, c, keep, thresh, ramp, sh, acc);
@@ -670,7 +781,10 @@ __device__ __forceinline__ void row_pass(const VerifyArgs& A, RowShared& sh) {
     if (sh.woverflow) {
       exact = true;
     } else {
-      // one wave finishes the row; the others wait only to join an exact fallback
+      // one wave finishes the row; the others wait only to join an exact
+      // fallback (wave 1 draws the ratio-test uniform meanwhile)
+      if (wave_id() == 1 && lane_id() == 0 && tested)
+        sh.dscr[1] = accept_uniform(A.seed, rid, pos0 + (uint32_t)j);
       if (wave_id() == 0) {
         ListEntry* L = A.list + (size_t)i * kListCap;
         const float* qrow = tested ? A.draft_probs + (size_t)i * (size_t)A.ld_q : nullptr;
@@ -701,29 +815,16 @@ __device__ __forceinline__ void row_pass(const VerifyArgs& A, RowShared& sh) {
     int n = 0;
     if (sh.woverflow) {
       exact = true;
+    } else if (topp_mode) {
+      n = topp_certified<DT>(row, V, sh);
+      if (n < 0) exact = true;
     } else {
-      // certified prefix: every element above the largest wave threshold is held
-      float tstar = sh.wtau[0];
-#pragma unroll
-      for (int w = 1; w < kWaves; ++w) tstar = fmaxf(tstar, sh.wtau[w]);
-      const uint32_t tkey = fkey(tstar);
       n = merge_segments(sh);
-      if (topk_mode) {
-        if (n < k_eff) {
-          exact = true;  // fewer finite candidates than k
-        } else if (n > k_eff) {
-          compact_top(sh, n, k_eff);
-          n = k_eff;
-        }
-      } else {
-        int cert = 0;
-        for (int t = tid; t < n; t += kBlock) cert += (uint32_t)(sh.buf[t] >> 32) > tkey ? 1 : 0;
-        cert = block_sum_i(cert, sh.iscr);
-        const int use = cert < kTopPSortCap ? cert : kTopPSortCap;
-        if (n > use) {
-          compact_top(sh, n, use);
-          n = use;
-        }
+      if (n < k_eff) {
+        exact = true;  // fewer finite candidates than k
+      } else if (n > k_eff) {
+        compact_top(sh, n, k_eff);
+        n = k_eff;
       }
     }
     if (!exact) {
@@ -809,17 +910,22 @@ __device__ __forceinline__ void row_pass(const VerifyArgs& A, RowShared& sh) {
     } else {
       const double q = (double)qd;
       const double ratio = q > 0.0 ? fmin(1.0, pd / q) : (pd > 0.0 ? 1.0 : 0.0);
-      const double u = accept_uniform(A.seed, rid, pos0 + (uint32_t)j);
+      const double u = vec_mode && !exact ? sh.dscr[1] : accept_uniform(A.seed, rid, pos0 + (uint32_t)j);
       if (u < ratio) out.flags |= kRecAccept;
     }
   }
-  if (vec_mode) {
-    // the token this row emits if it is its request's emit row: after a
-    // rejection (residual race; p for an out-of-range draft) or as the bonus
-    const bool rejected = tested && !(out.flags & kRecAccept);
-    if (rejected || (!A.build && j == cap_eff)) {
-      bool empty = false;
+  // the token this row emits if it is its request's emit row: after a
+  // rejection (residual race; p for an out-of-range draft) or as the bonus
+  const bool rejected = tested && !(out.flags & kRecAccept);
+  if (rejected || (!A.build && j == cap_eff)) {
+    bool empty = false;
+    if (vec_mode) {
       out.sample = wave_kept_race(kk, rejected && d_ok, A.seed, rid, pos0 + (uint32_t)j, empty);
+      out.flags |= kRecSampled | (empty ? kRecResidEmpty : 0);
+    } else if (buf_mode && out.mode == kModeList) {
+      const float* qrow = A.draft_probs + (size_t)i * (size_t)A.ld_q;
+      out.sample = block_kept_race(out.nkeep, m, out.zn, T, qrow, rejected && d_ok, A.seed, rid,
+                                   pos0 + (uint32_t)j, sh, empty);
       out.flags |= kRecSampled | (empty ? kRecResidEmpty : 0);
     }
   }
@@ -925,6 +1031,9 @@ __device__ int stream_race(const void* row, int V, const RowRec& rr, float T, co
     const bool in = !range || key > bkey || (key == bkey && rank < nb);
     if (!in) return;
     const float y = (x - rr.m) * c;          // log2 of the weight relative to the max
+    // -log2 E_v <= 24 (race uniforms lie in [2^-24, 1 - 2^-24]): an element whose
+    // weight cannot beat the best lower bound even then needs no uniform
+    if (!(y - (residual ? l2zn : 0.0f) + 24.0f + 2.0f * kEta >= best_lo)) return;
     float lo, up;
     if (!residual) {
       if (!(y > -1.0e30f)) return;
