@@ -57,7 +57,8 @@ enum : int32_t {
   kRecExact = 4,      // kept set came from the multi-pass exact path
   kRecBadDraft = 8,
   kRecSampled = 16,   // `sample` holds this row's emitted token if it is the emit row
-  kRecResidEmpty = 32 // that sample came from p: the residual was zero on the kept set
+  kRecResidEmpty = 32, // that sample came from p: the residual was zero on the kept set
+  kRecTieCut = 64      // kModeRange: tie_cut holds the id past the last kept element at bkey
 };
 
 struct RowRec {
@@ -73,8 +74,10 @@ struct RowRec {
   float lse;      // log sum exp(x / T_eff) over the row (build path)
   float pd;       // p(d) of the tested draft (diagnostic)
   int32_t sample;  // kRecSampled: token emitted when this row is the request's emit row
+  int32_t tie_cut; // kRecTieCut: elements at bkey with a smaller id are the kept ties
+  int32_t pad;
 };
-static_assert(sizeof(RowRec) == 56, "RowRec layout");
+static_assert(sizeof(RowRec) == 64, "RowRec layout");
 
 struct ListEntry {
   int32_t idx;

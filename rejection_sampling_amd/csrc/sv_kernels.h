@@ -72,7 +72,7 @@ __global__ void accept_prefix_kernel(const uint8_t* accepted, const int32_t* qo,
 // sizes shared with the host
 constexpr int kRowBlock = SV_BLOCK;
 constexpr int kPlanBlock = 1024;
-constexpr size_t kRowRecBytes = 56;
+constexpr size_t kRowRecBytes = 64;
 constexpr size_t kListBytesPerRow = 1024 * 8;
 
 }  // namespace sv

@@ -29,6 +29,7 @@ struct ExactOut {
   double zk, zn;   // masses relative to exp(m/T)
   int argmax;
   int tie_d;       // ties of the draft value with a smaller id
+  int ntie;        // elements of K at bkey (nb of them are kept)
 };
 
 __device__ __forceinline__ uint32_t key_of_prefix(uint32_t prefix, bool bf16) {
@@ -141,6 +142,7 @@ __device__ void exact_kept_set(const void* row, int V, float m, float T, int k_e
     zk = mass_above + (double)nbk * (double)(unsigned long long)((double)wb * scale);
     o.bkey = bk;
     o.nb = nbk;
+    o.ntie = cnt_bk;
     o.nkeep = k_eff;
   }
 
@@ -202,6 +204,7 @@ __device__ void exact_kept_set(const void* row, int V, float m, float T, int k_e
     if (nb < 1) nb = 1;
     o.bkey = bp;
     o.nb = nb;
+    o.ntie = avail;
     o.nkeep = (int)cnt_above + nb;
     o.zn = (mass_above + (double)nb * fw) / scale;
   } else {
@@ -537,7 +540,7 @@ __device__ __forceinline__ int wave_kept_race(const VecKept& kk, bool residual, 
 
 template <int DT>
 __device__ __forceinline__ void resolve_pending(const VerifyArgs& A, int i, int r, int j,
-                                                bool tested, RowShared& sh);
+                                                bool tested, bool bonus, RowShared& sh);
 
 // Top-p rows (top-k off): every element above the largest wave threshold T*
 // lies in a candidate vector whose max is above T* (each wave dropped only
@@ -898,7 +901,7 @@ __device__ __forceinline__ void row_pass(const VerifyArgs& A, RowShared& sh) {
     if (tid == 0) *rec = out;
     __threadfence_block();
     __syncthreads();
-    resolve_pending<DT>(A, i, r, j, tested, sh);
+    resolve_pending<DT>(A, i, r, j, tested, !A.build && j == cap_eff, sh);
     return;
   }
 
@@ -944,7 +947,7 @@ __global__ __launch_bounds__(kBlock) void row_pass_kernel(VerifyArgs A) {
 // p(d) and the ratio test of its draft.  Rewrites the row record.
 template <int DT>
 __device__ __forceinline__ void resolve_pending(const VerifyArgs& A, int i, int r, int j,
-                                                bool tested, RowShared& sh) {
+                                                bool tested, bool bonus, RowShared& sh) {
   RowRec out = A.rec[i];
   const int V = A.vocab;
   const float T = A.temperature ? A.temperature[r] : 0.0f;
@@ -970,25 +973,78 @@ __device__ __forceinline__ void resolve_pending(const VerifyArgs& A, int i, int 
   out.zk = eo.zk;
   out.zn = eo.zn;
   out.flags |= kRecExact;
+  // a kept set that fits becomes an explicit list, sorted (ranked pass for the
+  // ties at the boundary, then a sort of the kept entries)
+  bool listed = false;
+  {
+    // one ranked pass: the kept entries (when they fit a list) and the id
+    // just past the last kept tie at the boundary
+    const uint32_t bkey = eo.bkey;
+    const int nb = eo.nb;
+    const bool fits = eo.nkeep <= kListCap;
+    if (threadIdx.x == 0) {
+      sh.count = 0;
+      sh.found = V;
+    }
+    __syncthreads();
+    for_each_element_ranked<DT>(
+        row, V, [&](float x) { return fkey(x) == bkey; },
+        [&](float x, int v, int rank) {
+          const uint32_t key = fkey(x);
+          if (key == bkey && rank == nb - 1) sh.found = v + 1;
+          if (fits && (key > bkey || (key == bkey && rank < nb))) {
+            const int slot = atomicAdd(&sh.count, 1);
+            if (slot < kCap) sh.buf[slot] = make_entry(x, v);
+          }
+        },
+        sh);
+    __syncthreads();
+    const int n = sh.count;
+    out.tie_cut = sh.found;
+    out.flags |= kRecTieCut;
+    __syncthreads();
+    if (fits && n == eo.nkeep) {
+      sort_desc(sh, n);
+      ListEntry* L = A.list + (size_t)i * kListCap;
+      for (int t = threadIdx.x; t < n; t += kBlock) {
+        const uint64_t en = sh.buf[t];
+        ListEntry le;
+        le.idx = entry_idx(en);
+        le.x = entry_val(en);
+        L[t] = le;
+      }
+      out.mode = kModeList;
+      listed = true;
+    }
+  }
   double pd = 0.0;
   if (d_ok) {
     const uint32_t kd = fkey(xd);
     const bool in = kd > eo.bkey || (kd == eo.bkey && eo.tie_d < eo.nb);
     pd = in ? exp(((double)xd - (double)out.m) / (double)T) / eo.zn : 0.0;
   }
+  const uint32_t rid = A.request_id ? A.request_id[r] : (uint32_t)r;
+  const uint32_t pos0 = A.position0 ? A.position0[r] : 0u;
   if (tested) {
     out.flags |= kRecTested;
     out.pd = (float)pd;
     if (!d_ok) {
       out.flags |= kRecBadDraft;
     } else {
-      const uint32_t rid = A.request_id ? A.request_id[r] : (uint32_t)r;
-      const uint32_t pos0 = A.position0 ? A.position0[r] : 0u;
       const double q = (double)A.draft_probs[(size_t)i * (size_t)A.ld_q + d];
       const double ratio = q > 0.0 ? fmin(1.0, pd / q) : (pd > 0.0 ? 1.0 : 0.0);
       const double u = accept_uniform(A.seed, rid, pos0 + (uint32_t)j);
       if (u < ratio) out.flags |= kRecAccept;
     }
+  }
+  // the emitted token if this row is its request's emit row (listed sets only)
+  const bool rejected = tested && !(out.flags & kRecAccept);
+  if (listed && (rejected || bonus)) {
+    bool empty = false;
+    const float* qrow = A.draft_probs + (size_t)i * (size_t)A.ld_q;
+    out.sample = block_kept_race(out.nkeep, out.m, out.zn, T, qrow, rejected && d_ok, A.seed,
+                                 rid, pos0 + (uint32_t)j, sh, empty);
+    out.flags |= kRecSampled | (empty ? kRecResidEmpty : 0);
   }
   __syncthreads();
   if (threadIdx.x == 0) A.rec[i] = out;
@@ -1108,6 +1164,106 @@ __device__ int stream_race(const void* row, int V, const RowRec& rr, float T, co
   return w.key > 0.0 ? w.id : -1;
 }
 
+// Race over every element of an all-mode row.  Each element gets a fp32 log2
+// key (log2 of the weight minus log2 E) within kEta of the exact one, from one
+// Philox call per four consecutive tokens; an element whose best possible key
+// is below the thread's best lower bound needs no uniform (-log2 E <= 24).
+// Each thread keeps its two best upper bounds and the largest one it dropped;
+// when every dropped bound is below the block's best lower bound B, the winner
+// is among the kept candidates with upper bound >= B, which are evaluated
+// exactly in fp64.  Returns -2 when that does not hold (the caller falls back).
+template <int DT>
+__device__ int stream_race_all(const void* row, int V, float m, double zn, uint32_t kmin,
+                               int tie_cut, float T, const float* qrow, bool residual,
+                               uint64_t seed, uint32_t rid, uint32_t pos, RowShared& sh) {
+  constexpr int P = Vec<DT>::kEpv;
+  constexpr float kNegInf = -__builtin_huge_valf();
+  const float c = kLog2e / T;
+  const float l2zn = residual ? (float)log2(zn) : 0.0f;
+  float best_lo = kNegInf, up1 = kNegInf, up2 = kNegInf, dropped = kNegInf;
+  int id1 = -1, id2 = -1;
+  uint32_t gcache = 0xFFFFFFFFu;
+  uint4 oc = make_uint4(0u, 0u, 0u, 0u);
+  const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+  auto elem = [&](float x, int v) {
+    const float y = (x - m) * c - l2zn;  // log2 of p (residual) or of the relative weight
+    if (!(y + 24.0f + 2.0f * kEta >= best_lo)) return;
+    const uint32_t key = fkey(x);
+    if (key < kmin || (key == kmin && v >= tie_cut)) return;  // outside the kept range
+    const uint32_t g = (uint32_t)v >> 2;
+    if (g != gcache) {
+      oc = philox4x32_10(k0, k1, make_uint4(pos, rid, 1u, g));
+      gcache = g;
+    }
+    const uint32_t ln = (uint32_t)v & 3u;
+    const uint32_t wv = ln == 0 ? oc.x : (ln == 1 ? oc.y : (ln == 2 ? oc.z : oc.w));
+    // log2 E, E = -ln U, within far less than kEta: a short series for U near 1
+    const float U = (float)(2u * (wv >> 9) + 1u) * 0x1.0p-24f;
+    const float dlt = 1.0f - U;  // exact
+    const float E = dlt < 0x1.0p-10f ? dlt * (1.0f + 0.5f * dlt)
+                                     : -__builtin_amdgcn_logf(U) * 0.6931471805599453f;
+    const float l2e = __builtin_amdgcn_logf(E);
+    float lo, up;
+    if (!residual) {
+      lo = y - l2e - kEta;
+      up = y - l2e + kEta;
+    } else {
+      if (!(y + 2.0e-4f - l2e + kEta >= best_lo)) return;  // even with q = 0
+      const float p32 = exp2f(y);
+      const float q = qrow[v];
+      const float rhi = p32 * (1.0f + kRelP) - q;
+      if (!(rhi > 0.0f)) return;
+      const float rlo = p32 * (1.0f - kRelP) - q;
+      up = log2f(rhi) - l2e + kEta;
+      lo = rlo > 0.0f ? log2f(rlo) - l2e - kEta : kNegInf;
+    }
+    best_lo = fmaxf(best_lo, lo);
+    if (up > up1) {
+      dropped = fmaxf(dropped, up2);
+      up2 = up1; id2 = id1;
+      up1 = up; id1 = v;
+    } else if (up > up2) {
+      dropped = fmaxf(dropped, up2);
+      up2 = up; id2 = v;
+    } else {
+      dropped = fmaxf(dropped, up);
+    }
+  };
+  const RowSplit<DT> sp(row, V);
+  const int tid = threadIdx.x;
+  if (tid < sp.head) elem(Vec<DT>::load1(row, tid), tid);
+  for (int vi = tid; vi < sp.nvec; vi += kBlock) {
+    float x[P];
+    Vec<DT>::unpack(__ldg(sp.vbase + vi), x);
+    // whole vectors below the bound skip their uniforms
+    const float ym = (vec_max<P>(x) - m) * c - l2zn;
+    if (!(ym + 24.0f + 2.0f * kEta >= best_lo)) continue;
+    const int b = sp.head + vi * P;
+#pragma unroll
+    for (int e = 0; e < P; ++e) elem(x[e], b + e);
+  }
+  if (sp.tail0 + tid < V) elem(Vec<DT>::load1(row, sp.tail0 + tid), sp.tail0 + tid);
+  const float B = block_max_f(best_lo, sh.fscr);
+  const float D = block_max_f(dropped, sh.fscr);
+  if (D > kNegInf && !(D < B)) return -2;
+  const double Td = T;
+  RaceBest b = {-1.0, 0x7FFFFFFF};
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int v = t == 0 ? id1 : id2;
+    const float u = t == 0 ? up1 : up2;
+    if (v < 0 || !(u >= B)) continue;
+    const double x = (double)Vec<DT>::load1(row, v);
+    double wgt = exp((x - (double)m) / Td) / zn;
+    if (residual) wgt = wgt - (double)qrow[v];
+    if (!(wgt > 0.0)) continue;
+    const double key = wgt / race_e(seed, rid, pos, (uint32_t)v);
+    if (race_better(key, v, b.key, b.id)) { b.key = key; b.id = v; }
+  }
+  const RaceBest w = block_race_best(b, sh);
+  return w.key > 0.0 ? w.id : -1;
+}
+
 // Race over an explicit kept list (kModeList), fp64 throughout.
 __device__ int list_race(const ListEntry* L, const RowRec& rr, float T, const float* qrow,
                          bool residual, uint64_t seed, uint32_t rid, uint32_t pos, RowShared& sh) {
@@ -1184,7 +1340,8 @@ __device__ void finalize(const VerifyArgs& A, RowShared& sh) {
   }
   // rows of this request the streaming pass left to the exact path
   for (int j = 0; j <= cap_eff; ++j) {
-    if (A.rec[s + j].mode == kModePending) resolve_pending<DT>(A, s + j, r, j, j < cap_eff, sh);
+    if (A.rec[s + j].mode == kModePending)
+      resolve_pending<DT>(A, s + j, r, j, j < cap_eff, j == cap_eff, sh);
   }
   // accepted prefix: first row j < cap_eff whose test rejected (wave 0 ballots)
   if (wave_id() == 0) {
@@ -1225,10 +1382,21 @@ __device__ void finalize(const VerifyArgs& A, RowShared& sh) {
         sample = list_race(Lst, rr, T, qrow, false, A.seed, rid, pos, sh);
       }
     } else {
-      sample = stream_race<DT>(row, A.vocab, rr, T, qrow, residual, A.seed, rid, pos, sh);
+      auto race = [&](bool resid) {
+        int smp = -2;
+        if (rr.mode == kModeAll || (rr.mode == kModeRange && (rr.flags & kRecTieCut)))
+          smp = stream_race_all<DT>(row, A.vocab, rr.m, rr.zn,
+                                    rr.mode == kModeRange ? rr.bkey : 0u,
+                                    rr.mode == kModeRange ? rr.tie_cut : 0x7FFFFFFF, T, qrow,
+                                    resid, A.seed, rid, pos, sh);
+        if (smp == -2)
+          smp = stream_race<DT>(row, A.vocab, rr, T, qrow, resid, A.seed, rid, pos, sh);
+        return smp;
+      };
+      sample = race(residual);
       if (residual && sample < 0) {
         resid_empty = true;
-        sample = stream_race<DT>(row, A.vocab, rr, T, qrow, false, A.seed, rid, pos, sh);
+        sample = race(false);
       }
     }
   }
@@ -1262,7 +1430,7 @@ __device__ void build_out(const VerifyArgs& A, const BuildOutArgs& B, RowShared&
   const int tid = threadIdx.x;
   const int V = A.vocab;
   const int r = row_to_request(A.qo, A.num_requests, i);
-  if (A.rec[i].mode == kModePending) resolve_pending<DT>(A, i, r, i - A.qo[r], false, sh);
+  if (A.rec[i].mode == kModePending) resolve_pending<DT>(A, i, r, i - A.qo[r], false, false, sh);
   const RowRec rr = A.rec[i];
   const float T = A.temperature ? A.temperature[r] : 0.0f;
   const void* row = (const char*)A.logits + (size_t)i * (size_t)A.ld_logits * (DT == 1 ? 2 : 4);
