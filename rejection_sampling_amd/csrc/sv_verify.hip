@@ -622,6 +622,171 @@ __device__ __forceinline__ int topp_certified(const void* row, int V, RowShared&
   return total;
 }
 
+// Top-p kept set among the n certified elements in sh.buf (block level):
+// the boundary value by a fixed-point mass walk over 8-bit digits of the order
+// key (exact integer sums, no sort), ties at the boundary by id, then the kept
+// entries compacted to sh.buf[0, nkeep) (sorted only when `sorted`).  Returns
+// false when the certified mass does not reach P * Z.
+struct TopPOut {
+  int nkeep, a;
+  double zn, pd;
+};
+template <int DT>
+__device__ __forceinline__ bool topp_select(RowShared& sh, int n, float m, float T, float P,
+                                            double Z, int d, bool sorted, TopPOut& o) {
+  constexpr bool kBf = DT == 1;
+  const int tid = threadIdx.x;
+  const float c = kLog2e / T;
+  int lg = 0;
+  while ((1 << lg) < n + 1) ++lg;
+  const double scale = ldexp(1.0, 62 - lg);
+  // fixed-point weight of an entry (fp32 exp2, as the exact path)
+  auto wfx = [&](uint64_t e) {
+    return (unsigned long long)((double)exp2f((entry_val(e) - m) * c) * scale);
+  };
+  double wsum = 0.0;
+  for (int t = tid; t < n; t += kBlock) wsum += (double)wfx(sh.buf[t]);
+  const double target = (double)P * Z * scale;
+  if (block_sum_d(wsum, sh.dscr) < target) return false;
+  unsigned long long* mh = (unsigned long long*)sh.mhist;
+  uint32_t* ch = sh.whist[0];
+  uint32_t prefix = 0, pmask = 0;
+  double above = 0.0;
+  int above_cnt = 0, avail = 0;
+  const int nlev = kBf ? 2 : 4;
+  for (int lev = 0; lev < nlev; ++lev) {
+    const int shift = 24 - 8 * lev;
+    for (int b = tid; b < 256; b += kBlock) { ch[b] = 0u; mh[b] = 0ull; }
+    __syncthreads();
+    for (int t = tid; t < n; t += kBlock) {
+      const uint64_t e = sh.buf[t];
+      const uint32_t key = (uint32_t)(e >> 32);
+      if ((key & pmask) == prefix) {
+        const uint32_t dg = (key >> shift) & 255u;
+        atomicAdd(&ch[dg], 1u);
+        atomicAdd(&mh[dg], wfx(e));
+      }
+    }
+    __syncthreads();
+    if (wave_id() == 0) {
+      // digit (from the top) where the running mass first reaches the target
+      const int l = lane_id();
+      double h[4];
+      int cc[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        h[q] = (double)mh[255 - 4 * l - q];
+        cc[q] = (int)ch[255 - 4 * l - q];
+      }
+      const double loc = (h[0] + h[1]) + (h[2] + h[3]);
+      const int cloc = (cc[0] + cc[1]) + (cc[2] + cc[3]);
+      const double incl = wave_inclusive_sum(loc);
+      const int cincl = wave_inclusive_sum(cloc);
+      const double excl = incl - loc;
+      const int cexcl = cincl - cloc;
+      uint64_t mk = __ballot(above + excl < target && target <= above + incl);
+      if (mk == 0) mk = __ballot(l == 63);  // rounding past the total: the lowest digit
+      const int src = __ffsll((unsigned long long)mk) - 1;
+      if (l == src) {
+        double acc = above + excl;
+        int cacc = cexcl, q = 0;
+        while (q < 3 && !(acc + h[q] >= target)) { acc += h[q]; cacc += cc[q]; ++q; }
+        sh.sel_digit = 255 - 4 * l - q;
+        sh.zn_shared = acc;
+        sh.sel_need = above_cnt + cacc;
+        sh.sel_exact = cc[q];
+      }
+    }
+    __syncthreads();
+    above = sh.zn_shared;
+    above_cnt = sh.sel_need;
+    avail = sh.sel_exact;
+    prefix |= (uint32_t)sh.sel_digit << shift;
+    pmask |= 0xFFu << shift;
+    __syncthreads();
+  }
+  // the final bin holds one value; its elements keep in id order while the
+  // mass before them is below the target
+  uint32_t bkey = prefix;
+  if (kBf) {
+    const uint32_t k16 = prefix >> 16;
+    const uint32_t u16 = (k16 & 0x8000u) ? (k16 & 0x7FFFu) : (~k16 & 0xFFFFu);
+    bkey = fkey(__uint_as_float(u16 << 16));
+  }
+  const double wb = (double)(unsigned long long)((double)exp2f((key_to_float(bkey) - m) * c) * scale);
+  const double need = wb > 0.0 ? ceil((target - above) / wb) : 1.0;
+  int nb = need < 1.0 ? 1 : (need > (double)avail ? avail : (int)need);
+  if (nb < 1) nb = 1;
+  // id just past the nb-th tie (all ties when none drops): the tie ids are
+  // gathered (spare histogram space) and ranked among themselves
+  if (tid == 0) sh.found = 0x7FFFFFFF;
+  __syncthreads();
+  constexpr int kTieCap = (kWaves - 1) * 256;
+  if (nb < avail && avail <= kTieCap) {
+    int* tie_id = (int*)sh.whist[1];
+    int pos0 = 0;
+    for (int b0 = 0; b0 < n; b0 += kBlock) {
+      const int t = b0 + tid;
+      const uint64_t e = t < n ? sh.buf[t] : 0ull;
+      const bool tie = t < n && (uint32_t)(e >> 32) == bkey;
+      int total;
+      const int off = block_exclusive_sum(tie ? 1 : 0, sh.iscr, &total);
+      if (tie) tie_id[pos0 + off] = entry_idx(e);
+      pos0 += total;
+    }
+    __syncthreads();
+    for (int t = tid; t < avail; t += kBlock) {
+      const int id = tie_id[t];
+      int rank = 0;
+      for (int u = 0; u < avail; ++u) rank += tie_id[u] < id ? 1 : 0;
+      if (rank == nb - 1) sh.found = id + 1;
+    }
+  } else if (nb < avail) {
+    for (int t = tid; t < n; t += kBlock) {
+      const uint64_t e = sh.buf[t];
+      if ((uint32_t)(e >> 32) != bkey) continue;
+      const int id = entry_idx(e);
+      int rank = 0;
+      for (int u = 0; u < n; ++u) {
+        const uint64_t o2 = sh.buf[u];
+        rank += ((uint32_t)(o2 >> 32) == bkey && entry_idx(o2) < id) ? 1 : 0;
+      }
+      if (rank == nb - 1) sh.found = id + 1;
+    }
+  }
+  __syncthreads();
+  const int cut = sh.found;
+  // compact the kept entries to the front, one round of kBlock at a time
+  double zloc = 0.0, pdl = 0.0;
+  uint64_t best = 0ull;
+  int pos0 = 0;
+  for (int b0 = 0; b0 < n; b0 += kBlock) {
+    const int t = b0 + tid;
+    const uint64_t e = t < n ? sh.buf[t] : 0ull;
+    const uint32_t key = (uint32_t)(e >> 32);
+    const bool k = t < n && (key > bkey || (key == bkey && entry_idx(e) < cut));
+    int total;
+    const int off = block_exclusive_sum(k ? 1 : 0, sh.iscr, &total);  // reads of the round done
+    if (k) {
+      sh.buf[pos0 + off] = e;
+      const double w = exp(((double)entry_val(e) - (double)m) / (double)T);
+      zloc += w;
+      if (entry_idx(e) == d) pdl = w;
+      best = e > best ? e : best;
+    }
+    pos0 += total;
+  }
+  const double zn = block_sum_d(zloc, sh.dscr);
+  const double pdw = block_sum_d(pdl, sh.dscr);
+  o.a = entry_idx(block_max_u64(best, sh.uscr));
+  o.nkeep = pos0;
+  o.zn = zn;
+  o.pd = pdw / zn;
+  if (sorted) sort_desc(sh, pos0);
+  __syncthreads();
+  return true;
+}
+
 // Race of list_race over the sorted kept entries sh.buf[0, nkeep) (block
 // level); an all-zero residual falls back to p and sets `empty`.
 __device__ __forceinline__ int block_kept_race(int nkeep, float m, double zn, float T,
@@ -830,7 +995,27 @@ __device__ __forceinline__ void row_pass(const VerifyArgs& A, RowShared& sh) {
         n = k_eff;
       }
     }
-    if (!exact) {
+    if (!exact && topp_mode) {
+      TopPOut tp;
+      if (!topp_select<DT>(sh, n, m, T, P, Z, d_ok ? d : -1, A.build != 0, tp)) {
+        exact = true;  // the certified candidates do not reach the top-p mass
+      } else {
+        out.a = tp.a;
+        out.zk = Z;
+        out.zn = tp.zn;
+        out.nkeep = tp.nkeep;
+        pd = tp.pd;
+        out.mode = kModeList;
+        ListEntry* L = A.list + (size_t)i * kListCap;
+        for (int t = tid; t < tp.nkeep; t += kBlock) {
+          const uint64_t v = sh.buf[t];
+          ListEntry le;
+          le.idx = entry_idx(v);
+          le.x = entry_val(v);
+          L[t] = le;
+        }
+      }
+    } else if (!exact) {
       sort_desc(sh, n);
       // fp64 weights and prefix masses over contiguous per-thread chunks
       const int ch = (n + kBlock - 1) / kBlock;
