@@ -313,6 +313,8 @@ def main():
     torch.cuda.synchronize()
     n_rp, ms_rp = B.profile_read("row_pass")
     n_fz, ms_fz = B.profile_read("finalize")
+    n_rs, ms_rs = B.profile_read("race_segment")
+    n_rf, ms_rf = B.profile_read("race_finish")
     B.profile_enable(False)
     ms_per_step = elapsed * 1e3 / args.steps
     rows_per_s = rows / (ms_per_step * 1e-3)
@@ -346,7 +348,8 @@ def main():
                      "traffic": measured_traffic() if wl == "c3" else None,
                      "kernel": "row_pass_kernel", "kernel_ms": round(kern_ms, 5),
                      "algorithmic_bytes": alg_bytes,
-                     "finalize_ms": round(ms_fz / max(n_fz, 1), 5)},
+                     "finalize_ms": round(ms_fz / max(n_fz, 1), 5),
+                     "race_ms": round((ms_rs + ms_rf) / max(n_fz, 1), 5)},
         "cpu_baseline": cpu,
         "mean_accept_len": round(acc, 4),
     }

@@ -54,9 +54,15 @@ enum {
 
 /* Hints in sv_sampling.flags. */
 enum {
-  SV_ALL_GREEDY = 1u /* every request is greedy: draft_probs may be NULL. The
-                        host-side all-greedy skip of the consolidation study,
-                        section 6 (sampling prep is inert at temperature 0). */
+  SV_ALL_GREEDY = 1u, /* every request is greedy: draft_probs may be NULL. The
+                         host-side all-greedy skip of the consolidation study,
+                         section 6 (sampling prep is inert at temperature 0). */
+  SV_LIST_BOUNDED = 2u /* every sampled request has 0 < top_k <= 4096, so no
+                         correction or bonus token is sampled over the whole
+                         vocabulary: the call skips the two launches that split
+                         such samples over workgroups.  A performance hint only:
+                         a request that breaks it is still sampled exactly (by
+                         one workgroup). */
 };
 
 /* Row flag bits written by spec_verify_rejection_sample (row_flags). */
@@ -73,7 +79,14 @@ typedef struct {
   const uint32_t* request_id;/* [R] device or NULL (r): Philox counter word         */
   const uint32_t* position0; /* [R] device or NULL (0): absolute position of row 0  */
   uint64_t seed;             /* Philox4x32-10 key                                   */
-  uint32_t flags;            /* SV_ALL_GREEDY                                       */
+  uint32_t flags;            /* SV_ALL_GREEDY | SV_LIST_BOUNDED                     */
+  const int32_t* row_order;  /* [num_rows] device or NULL (natural order): the order
+                                in which rows are scheduled, a permutation of
+                                0..num_rows-1 (anything else leaves the results
+                                undefined; ids outside the range are skipped).  A
+                                load-balance hint: rows that may need the multi-pass
+                                exact top-p path (top-k off, top-p on) placed first
+                                overlap their extra passes with the other rows. */
 } sv_sampling;
 
 /* Bytes of device workspace the calls below need for these sizes (block: the
@@ -164,7 +177,8 @@ const char* spec_verify_last_error(void);
  * library records a pair of HIP events on the call's stream; read() waits for
  * them and returns, per kernel id, the launch count and the summed
  * milliseconds since the last reset.  Kernel ids: 0 row pass, 1 request
- * finalize, 2 target-probs writer, 3 planner, 4 accept prefix. */
+ * finalize, 2 target-probs writer, 3 planner, 4 accept prefix, 5 race
+ * segments, 6 race finish. */
 int32_t spec_verify_profile_enable(int32_t on);
 int32_t spec_verify_profile_read(int32_t kernel_id, int64_t* launches, double* total_ms);
 int32_t spec_verify_profile_reset(void);

@@ -19,8 +19,12 @@ LIB_PATH = os.path.join(HERE, "libspecverify.so")
 
 SV_F32, SV_BF16 = 0, 1
 SV_ALL_GREEDY = 1
+SV_LIST_BOUNDED = 2
+LIST_CAP = 4096  # kept-set entries a row can list (top-k bound of SV_LIST_BOUNDED)
+TOPK_SINGLE_PASS = 256  # largest top-k the streaming pass selects by itself
 ROW_ACCEPT, ROW_SAMPLED, ROW_RESID_EMPTY = 1, 2, 32
-KERNEL_IDS = {"row_pass": 0, "finalize": 1, "build_out": 2, "planner": 3, "accept_prefix": 4}
+KERNEL_IDS = {"row_pass": 0, "finalize": 1, "build_out": 2, "planner": 3, "accept_prefix": 4,
+              "race_segment": 5, "race_finish": 6}
 
 EXPORTS = [
     "spec_verify_workspace_bytes", "spec_verify_build_target_probs",
@@ -34,7 +38,7 @@ class Sampling(ctypes.Structure):
     _fields_ = [("temperature", ctypes.c_void_p), ("top_k", ctypes.c_void_p),
                 ("top_p", ctypes.c_void_p), ("request_id", ctypes.c_void_p),
                 ("position0", ctypes.c_void_p), ("seed", ctypes.c_uint64),
-                ("flags", ctypes.c_uint32)]
+                ("flags", ctypes.c_uint32), ("row_order", ctypes.c_void_p)]
 
 
 _lib = None
@@ -137,7 +141,7 @@ class Params:
     """Per-request sampling values as device tensors (kept alive with the call)."""
 
     def __init__(self, temperature, top_k=None, top_p=None, request_id=None, position0=None,
-                 seed: int = 0, all_greedy: bool = False):
+                 seed: int = 0, all_greedy: bool = False, list_bounded=None):
         self.T = _dev(temperature, torch.float32, "temperature")
         self.k = _dev(top_k, torch.int32, "top_k")
         self.P = _dev(top_p, torch.float32, "top_p")
@@ -145,9 +149,50 @@ class Params:
         # the same bits
         self.rid = _dev(request_id, torch.int32, "request_id")
         self.pos0 = _dev(position0, torch.int32, "position0")
+        # one host copy of the values (here, never per call) for the hints
+        self._host = None
+        if self.T is not None:
+            R = self.T.numel()
+            Th = self.T.cpu()
+            kh = self.k.cpu() if self.k is not None else torch.zeros(R, dtype=torch.int32)
+            Ph = self.P.cpu() if self.P is not None else torch.ones(R)
+            self._host = (Th, kh, Ph)
+        if list_bounded is None:
+            # every sampled request keeps at most LIST_CAP tokens by top-k
+            if self._host is None:
+                list_bounded = True  # every request greedy
+            elif self.k is None:
+                list_bounded = False
+            else:
+                Th, kh, _ = self._host
+                sampled = Th > 0
+                list_bounded = bool(((kh[sampled] > 0) & (kh[sampled] <= LIST_CAP)).all())
+        flags = (SV_ALL_GREEDY if all_greedy else 0) | (SV_LIST_BOUNDED if list_bounded else 0)
         self.s = Sampling(_ptr(self.T), _ptr(self.k), _ptr(self.P), _ptr(self.rid),
-                          _ptr(self.pos0), int(seed) & ((1 << 64) - 1),
-                          SV_ALL_GREEDY if all_greedy else 0)
+                          _ptr(self.pos0), int(seed) & ((1 << 64) - 1), flags, None)
+
+    def heavy_requests(self, vocab: int):
+        """Requests whose rows may take the multi-pass exact path: sampled,
+        top-k off with top-p on, or top-k above the single-pass limit."""
+        if self._host is None:
+            return None
+        Th, kh, Ph = self._host
+        k_off = (kh <= 0) | (kh >= vocab)
+        return (Th > 0) & ((k_off & (Ph < 1) & (Ph > 0)) | ((kh > TOPK_SINGLE_PASS) & ~k_off))
+
+
+def row_order(qo_indptr: torch.Tensor, params: Params, vocab: int):
+    """Row schedule with the rows of heavy requests first (a device int32
+    permutation), or None when no reordering helps (none or all heavy)."""
+    heavy = params.heavy_requests(vocab)
+    if heavy is None or not bool(heavy.any()) or bool(heavy.all()):
+        return None
+    qo = qo_indptr.cpu().to(torch.int64)
+    rows = torch.arange(int(qo[-1]), dtype=torch.int64)
+    req = torch.searchsorted(qo[1:], rows, right=True)
+    first = heavy[req]
+    order = torch.cat([rows[first], rows[~first]]).to(torch.int32)
+    return order.to(qo_indptr.device)
 
 
 def build_target_probs(logits: torch.Tensor, qo_indptr: torch.Tensor, params: Params,
@@ -212,7 +257,7 @@ class PreparedRejectionSample:
     tensors must stay alive and keep their shapes and storage."""
 
     def __init__(self, logits, qo_indptr, draft_tokens, draft_probs, params: Params,
-                 verify_cap=None, out=None):
+                 verify_cap=None, out=None, reorder: bool = True):
         dt = _logits(logits)
         rows, V = logits.shape
         qo = _dev(qo_indptr, torch.int32, "qo_indptr")
@@ -232,11 +277,15 @@ class PreparedRejectionSample:
             }
         ws = workspace(rows, V, R, 0, dev)
         ldq = draft_probs.stride(0) if draft_probs is not None else V
+        # this call's copy of the sampling block, with the heavy rows first
+        order = row_order(qo, params, V) if reorder else None
+        self._s = Sampling(*[getattr(params.s, f) for f, _ in Sampling._fields_])
+        self._s.row_order = _ptr(order)
         self.out = out
-        self._keep = (logits, qo, d, draft_probs, cap, params, ws)
+        self._keep = (logits, qo, d, draft_probs, cap, params, ws, order)
         self._fn = load().spec_verify_rejection_sample
         self._args = (_ptr(logits), dt, logits.stride(0), V, _ptr(qo), R, rows, _ptr(d),
-                      _ptr(draft_probs), ldq, _ptr(cap), ctypes.byref(params.s),
+                      _ptr(draft_probs), ldq, _ptr(cap), ctypes.byref(self._s),
                       _ptr(out["accept_len"]), _ptr(out["out_tokens"]), _ptr(out["next_token"]),
                       _ptr(out["row_flags"]), _ptr(ws), ws.numel(), _stream())
 

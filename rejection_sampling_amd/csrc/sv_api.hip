@@ -25,16 +25,28 @@ int32_t fail(int32_t code, const char* what) {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t rec, list, keys, total;
+  size_t rec, list, race_job, race_part, keys, total;
 };
 
 Layout layout(int64_t rows, int64_t R, int64_t block) {
   Layout L;
   L.rec = 0;
   L.list = align256((size_t)rows * sizeof(sv::RowRec));
-  L.keys = L.list + align256((size_t)rows * sv::kListCap * sizeof(sv::ListEntry));
+  L.race_job = L.list + align256((size_t)rows * sv::kListCap * sizeof(sv::ListEntry));
+  L.race_part = L.race_job + align256((size_t)R * sizeof(int32_t));
+  L.keys = L.race_part + align256((size_t)R * sv::kMaxRaceSegs * sizeof(sv::RacePart));
   L.total = L.keys + align256((size_t)(R * block) * sizeof(uint64_t)) + 256;
   return L;
+}
+
+// Workgroups per full-vocabulary race: none when no request can need one
+// (every request greedy, or every kept set bounded by a list), else one per
+// kRaceSegElems elements (at least two).
+int race_segments(int V, uint32_t flags) {
+  if (flags & (SV_ALL_GREEDY | SV_LIST_BOUNDED)) return 0;
+  int s = (V + sv::kRaceSegElems - 1) / sv::kRaceSegElems;
+  if (s > sv::kMaxRaceSegs) s = sv::kMaxRaceSegs;
+  return s < 2 ? 0 : s;
 }
 
 // ---- optional event timing
@@ -154,10 +166,13 @@ static sv::VerifyArgs base_args(const void* logits, sv_dtype dt, int64_t ld, int
   A.top_p = sp->top_p;
   A.request_id = sp->request_id;
   A.position0 = sp->position0;
+  A.row_order = sp->row_order;
   A.seed = sp->seed;
   Layout L = layout(rows, R, 0);
   A.rec = (sv::RowRec*)((char*)ws + L.rec);
   A.list = (sv::ListEntry*)((char*)ws + L.list);
+  A.race_job = (int32_t*)((char*)ws + L.race_job);
+  A.race_part = (sv::RacePart*)((char*)ws + L.race_part);
   return A;
 }
 
@@ -236,10 +251,20 @@ int32_t spec_verify_rejection_sample(const void* target_logits, sv_dtype dt, int
   A.next_token = next_token;
   A.row_flags = row_flags;
   if (!draft_probs) A.temperature = nullptr;  // SV_ALL_GREEDY: every request greedy
+  A.race_segs = draft_probs ? race_segments(vocab, sp->flags) : 0;
   if (num_rows > 0) launch(0, sv::row_pass_kernel, dim3(num_rows), dim3(sv::kRowBlock), s, A);
   if ((rc = check_launch("row pass"))) return rc;
   launch(1, sv::finalize_kernel, dim3(num_requests), dim3(sv::kRowBlock), s, A);
-  return check_launch("finalize");
+  if ((rc = check_launch("finalize"))) return rc;
+  if (A.race_segs > 0) {
+    const int items = A.race_segs * num_requests;
+    launch(5, sv::race_segment_kernel, dim3(items < sv::kRaceGrid ? items : sv::kRaceGrid),
+           dim3(sv::kRowBlock), s, A);
+    if ((rc = check_launch("race segments"))) return rc;
+    launch(6, sv::race_finish_kernel, dim3(num_requests), dim3(sv::kRowBlock), s, A);
+    if ((rc = check_launch("race finish"))) return rc;
+  }
+  return SV_OK;
 }
 
 int32_t spec_verify_plan_windows(const float* confidence, int64_t ld_conf, int32_t num_requests,

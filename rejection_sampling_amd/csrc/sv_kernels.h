@@ -12,6 +12,13 @@ namespace sv {
 struct RowRec;
 struct ListEntry;
 
+// Best (key, id) of one segment of a full-vocabulary race (key <= 0: none).
+struct RacePart {
+  double key;
+  int32_t id;
+  int32_t pad;
+};
+
 struct VerifyArgs {
   const void* logits;
   int64_t ld_logits;
@@ -29,6 +36,7 @@ struct VerifyArgs {
   const float* top_p;
   const uint32_t* request_id;
   const uint32_t* position0;
+  const int32_t* row_order;   // [num_rows] or NULL: row of each row-pass workgroup
   uint64_t seed;
   int32_t build;          // 1: target-probs build (every row, lse), 0: verify
   RowRec* rec;            // [num_rows]
@@ -37,6 +45,11 @@ struct VerifyArgs {
   int32_t* out_tokens;
   int32_t* next_token;
   uint8_t* row_flags;
+  // full-vocabulary samples split over workgroups (race_segs 0: finalize runs
+  // them in one workgroup)
+  int32_t race_segs;
+  int32_t* race_job;      // [num_requests]: 2 * row + residual, or -1
+  RacePart* race_part;    // [num_requests, race_segs]
 };
 
 struct BuildOutArgs {
@@ -64,6 +77,8 @@ struct PlanArgs {
 
 __global__ void row_pass_kernel(VerifyArgs A);
 __global__ void finalize_kernel(VerifyArgs A);
+__global__ void race_segment_kernel(VerifyArgs A);
+__global__ void race_finish_kernel(VerifyArgs A);
 __global__ void build_out_kernel(VerifyArgs A, BuildOutArgs B);
 __global__ void plan_kernel(PlanArgs A);
 __global__ void accept_prefix_kernel(const uint8_t* accepted, const int32_t* qo, int32_t R,
@@ -73,6 +88,8 @@ __global__ void accept_prefix_kernel(const uint8_t* accepted, const int32_t* qo,
 constexpr int kRowBlock = SV_BLOCK;
 constexpr int kPlanBlock = 1024;
 constexpr size_t kRowRecBytes = 64;
-constexpr size_t kListBytesPerRow = 1024 * 8;
+constexpr int kRaceSegElems = 8192;  // vocabulary elements per race segment
+constexpr int kMaxRaceSegs = 64;
+constexpr int kRaceGrid = 768;      // race-segment workgroups (three per CU resident)
 
 }  // namespace sv

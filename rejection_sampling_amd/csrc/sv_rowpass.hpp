@@ -892,6 +892,53 @@ __device__ __forceinline__ void for_each_element_lean(const void* row, int V, F&
   if (sp.tail0 + tid < V) f(Vec<DT>::load1(row, sp.tail0 + tid), sp.tail0 + tid);
 }
 
+// As for_each_element_lean with up to 2U vectors in flight per thread (the
+// next group of U is loaded while the current one is visited): a pass that
+// one workgroup makes over a whole row is bound by load latency otherwise.
+template <int DT, int U, class F>
+__device__ __forceinline__ void for_each_element_deep(const void* row, int V, F&& f) {
+  constexpr int P = Vec<DT>::kEpv;
+  const RowSplit<DT> sp(row, V);
+  const int tid = threadIdx.x;
+  if (tid < sp.head) f(Vec<DT>::load1(row, tid), tid);
+  auto load = [&](int v0, uint4* w) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int vi = v0 + u * kBlock;
+      w[u] = vi < sp.nvec ? __ldg(sp.vbase + vi) : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  auto visit = [&](int v0, const uint4* w) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int vi = v0 + u * kBlock;
+      if (vi >= sp.nvec) break;
+      const int b = sp.head + vi * P;
+#pragma unroll 1
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t x = q == 0 ? w[u].x : (q == 1 ? w[u].y : (q == 2 ? w[u].z : w[u].w));
+        if (DT == 1) {
+          f(bf16_lo(x), b + 2 * q);
+          f(bf16_hi(x), b + 2 * q + 1);
+        } else {
+          f(__uint_as_float(x), b + q);
+        }
+      }
+    }
+  };
+  constexpr int G = kBlock * U;  // vectors per group
+  uint4 wa[U], wb[U];
+  load(tid, wa);
+  for (int v0 = tid; v0 < sp.nvec; v0 += 2 * G) {
+    if (v0 + G < sp.nvec) load(v0 + G, wb);
+    visit(v0, wa);
+    if (v0 + G >= sp.nvec) break;
+    if (v0 + 2 * G < sp.nvec) load(v0 + 2 * G, wa);
+    visit(v0 + G, wb);
+  }
+  if (sp.tail0 + tid < V) f(Vec<DT>::load1(row, sp.tail0 + tid), sp.tail0 + tid);
+}
+
 // Visit every element in tiles of increasing ids with a block-wide rank of the
 // elements for which `tie(x)` holds: f(x, id, rank) where rank counts tie
 // elements with a smaller id.  Every thread must call it.

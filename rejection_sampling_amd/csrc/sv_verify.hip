@@ -228,6 +228,202 @@ __device__ void exact_kept_set(const void* row, int V, float m, float T, int k_e
   }
 }
 
+// Exact top-p kept set of a bf16 row with top-k off (the same fixed-point
+// masses and boundary rule as exact_kept_set), in one histogram pass: each of
+// the kNbCodes bf16 values just below the maximum is its own bin (a count; the
+// weight is the same for every element of a bin), and the mass of the elements
+// further down is summed in registers.  A block scan over the bins from the
+// top finds the boundary value; a second pass, when needed, lists the kept set
+// (when it fits a list) and collects the ids of the ties at the boundary,
+// ranked to give the cut when only some of them are kept.  Returns false when
+// the boundary lies below the binned values or the ties overflow their buffer
+// (the caller then runs the general path).
+constexpr int kNbCodes = 4 * kBlock;
+constexpr int kTieBuf = kWaves * 256;
+
+__device__ __forceinline__ float bf16_code_value(uint32_t k16) {
+  const uint32_t u16 = (k16 & 0x8000u) ? (k16 & 0x7FFFu) : (~k16 & 0xFFFFu);
+  return __uint_as_float(u16 << 16);
+}
+
+template <int DT>
+__device__ __forceinline__ bool exact_topp_codes(const void* row, int V, float m, float T, float P,
+                                                 int d, float xd, bool sorted, ListEntry* L,
+                                                 RowShared& sh, ExactOut& o, int& tie_cut,
+                                                 bool& listed) {
+  static_assert(DT == 1, "bf16 rows only");
+  const int tid = threadIdx.x;
+  if (!(m > -INFINITY) || !(m < INFINITY)) return false;
+  const float c = kLog2e / T;
+  int lg = 0;
+  while ((1ll << lg) < (long long)V + 1) ++lg;
+  const double scale = ldexp(1.0, 62 - lg);
+  auto fx = [&](float x) { return (uint64_t)((double)exp2f((x - m) * c) * scale); };
+  uint32_t* cnt = (uint32_t*)sh.buf;  // [kNbCodes]
+  for (int b = tid; b < kNbCodes; b += kBlock) cnt[b] = 0u;
+  if (tid == 0) sh.sel_digit = -1;
+  __syncthreads();
+  const uint32_t mk16 = fkey(m) >> 16;
+  const uint32_t keyd = d >= 0 ? fkey(xd) : 0u;
+  uint64_t below = 0;
+  int amin = 0x7FFFFFFF, tied = 0;
+  for_each_element_deep<DT, 4>(row, V, [&](float x, int i) {
+    const uint32_t key = fkey(x);
+    const uint32_t bin = mk16 - (key >> 16);
+    if (bin < (uint32_t)kNbCodes) atomicAdd(&cnt[bin], 1u);
+    else below += fx(x);
+    if (x == m && i < amin) amin = i;
+    if (d >= 0 && i < d && key == keyd) ++tied;
+  });
+  __syncthreads();
+  // masses of this thread's four bins (from the top), then a block scan
+  uint32_t cb[4];
+  uint64_t mb[4], loc = 0;
+  uint32_t lcnt = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int b = 4 * tid + q;
+    cb[q] = cnt[b];
+    mb[q] = cb[q] ? (uint64_t)cb[q] * fx(bf16_code_value(mk16 - (uint32_t)b)) : 0ull;
+    loc += mb[q];
+    lcnt += cb[q];
+  }
+  uint64_t incl = loc;
+  uint32_t cincl = lcnt;
+#pragma unroll
+  for (int s = 1; s < 64; s <<= 1) {
+    const uint64_t y = ((uint64_t)__shfl_up((uint32_t)(incl >> 32), s, 64) << 32) |
+                       __shfl_up((uint32_t)incl, s, 64);
+    const uint32_t yc = __shfl_up(cincl, s, 64);
+    if (lane_id() >= s) {
+      incl += y;
+      cincl += yc;
+    }
+  }
+  uint64_t bsum = below;
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) bsum += shfl_xor_u64(bsum, s);
+  uint64_t* wtot = (uint64_t*)sh.mhist;  // [0..3] bin masses, [4..7] counts, [8..11] below
+  if (lane_id() == 63) {
+    wtot[wave_id()] = incl;
+    wtot[4 + wave_id()] = cincl;
+    wtot[8 + wave_id()] = bsum;
+  }
+  __syncthreads();
+  uint64_t base = 0, tot = 0, blw = 0;
+  uint32_t cbase = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    if (w < wave_id()) {
+      base += wtot[w];
+      cbase += (uint32_t)wtot[4 + w];
+    }
+    tot += wtot[w];
+    blw += wtot[8 + w];
+  }
+  const uint64_t zk_fx = tot + blw;
+  const double target = (double)P * (double)zk_fx;
+  {
+    uint64_t above = base + incl - loc;
+    uint32_t cab = cbase + cincl - lcnt;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if ((double)above < target && target <= (double)(above + mb[q])) {
+        sh.sel_digit = 4 * tid + q;
+        sh.sel_entry = above;
+        sh.sel_need = (int)cab;
+        sh.count = (int)cb[q];
+      }
+      above += mb[q];
+      cab += cb[q];
+    }
+  }
+  __syncthreads();
+  const int bstar = sh.sel_digit;
+  if (bstar < 0) return false;  // the boundary lies below the binned values
+  const uint64_t above = sh.sel_entry;
+  const int cnt_above = sh.sel_need;
+  const int avail = sh.count;
+  const uint32_t bp16 = mk16 - (uint32_t)bstar;
+  const float xb = bf16_code_value(bp16);
+  const uint64_t fw = fx(xb);
+  const double need = ceil((target - (double)above) / (double)fw);
+  int nb = need < 1.0 ? 1 : (need > (double)avail ? avail : (int)need);
+  if (nb < 1) nb = 1;
+  o.bkey = fkey(xb);
+  o.nb = nb;
+  o.ntie = avail;
+  o.nkeep = cnt_above + nb;
+  o.zk = (double)zk_fx / scale;
+  o.zn = ((double)above + (double)nb * (double)fw) / scale;
+  o.argmax = 0x7FFFFFFF - (int)(uint32_t)block_max_u64((uint64_t)(uint32_t)(0x7FFFFFFF - amin),
+                                                      sh.uscr);
+  o.tie_d = block_sum_i(tied, sh.iscr);
+  tie_cut = V;
+  listed = false;
+  const bool want_list = o.nkeep <= kListCap;
+  const bool want_ties = nb < avail;
+  if (!want_list && !want_ties) return true;
+  if (want_ties && avail > kTieBuf) return false;
+  // second pass: kept entries above the boundary (listed rows) and the ties
+  int* tie_ids = (int*)&sh.whist[0][0];
+  if (tid == 0) {
+    sh.count = 0;
+    sh.wcount[0] = 0;
+    sh.found = V;
+  }
+  __syncthreads();
+  for_each_element_deep<DT, 4>(row, V, [&](float x, int i) {
+    const uint32_t k16 = fkey(x) >> 16;
+    if (k16 < bp16) return;
+    if (k16 == bp16 && want_ties) {
+      const int t = atomicAdd(&sh.wcount[0], 1);
+      if (t < kTieBuf) tie_ids[t] = i;
+    } else if (want_list) {
+      const int slot = atomicAdd(&sh.count, 1);
+      if (slot < kCap) sh.buf[slot] = make_entry(x, i);
+    }
+  });
+  __syncthreads();
+  if (want_ties) {
+    const int nt = sh.wcount[0];
+    if (nt != avail) return false;
+    // the nb-th smallest id among the ties: the kept ones lie below it + 1
+    for (int t = tid; t < nt; t += kBlock) {
+      const int id = tie_ids[t];
+      int rank = 0;
+      for (int u = 0; u < nt; ++u) rank += tie_ids[u] < id ? 1 : 0;
+      if (rank == nb - 1) sh.found = id + 1;
+    }
+    __syncthreads();
+    tie_cut = sh.found;
+    if (want_list) {
+      for (int t = tid; t < nt; t += kBlock) {
+        const int id = tie_ids[t];
+        if (id < tie_cut) {
+          const int slot = atomicAdd(&sh.count, 1);
+          if (slot < kCap) sh.buf[slot] = make_entry(xb, id);
+        }
+      }
+      __syncthreads();
+    }
+  }
+  if (!want_list) return true;
+  const int n = sh.count;
+  __syncthreads();
+  if (n != o.nkeep) return true;  // not listed: the range and the tie cut describe the set
+  if (sorted) sort_desc(sh, n);
+  for (int t = tid; t < n; t += kBlock) {
+    const uint64_t en = sh.buf[t];
+    ListEntry le;
+    le.idx = entry_idx(en);
+    le.x = entry_val(en);
+    L[t] = le;
+  }
+  listed = true;
+  return true;
+}
+
 // -------------------------------------------------------- row pass kernel
 // ----------------------------------------------------------------- races
 // Exponential race: winner = argmax over weight_v / E_v, E_v = -ln U_v; ties
@@ -796,14 +992,26 @@ __device__ __forceinline__ int block_kept_race(int nkeep, float m, double zn, fl
   const double Td = T;
   auto run = [&](bool resid) {
     RaceBest b = {-1.0, 0x7FFFFFFF};
-    for (int t = threadIdx.x; t < nkeep; t += kBlock) {
-      const uint64_t en = sh.buf[t];
-      const int id = entry_idx(en);
-      double wgt = exp(((double)entry_val(en) - (double)m) / Td) / zn;
-      if (resid) wgt = wgt - (double)qrow[id];
-      if (!(wgt > 0.0)) continue;
-      const double key = wgt / race_e(seed, rid, pos, (uint32_t)id);
-      if (race_better(key, id, b.key, b.id)) { b.key = key; b.id = id; }
+    // four entries per thread at a time, their draft probabilities loaded first
+    for (int t0 = threadIdx.x; t0 < nkeep; t0 += 4 * kBlock) {
+      uint64_t en[4];
+      float qv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int t = t0 + u * kBlock;
+        en[u] = t < nkeep ? sh.buf[t] : 0ull;
+        qv[u] = (resid && t < nkeep) ? qrow[entry_idx(en[u])] : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (t0 + u * kBlock >= nkeep) break;
+        const int id = entry_idx(en[u]);
+        double wgt = exp(((double)entry_val(en[u]) - (double)m) / Td) / zn;
+        if (resid) wgt = wgt - (double)qv[u];
+        if (!(wgt > 0.0)) continue;
+        const double key = wgt / race_e(seed, rid, pos, (uint32_t)id);
+        if (race_better(key, id, b.key, b.id)) { b.key = key; b.id = id; }
+      }
     }
     return block_race_best(b, sh);
   };
@@ -818,7 +1026,8 @@ __device__ __forceinline__ int block_kept_race(int nkeep, float m, double zn, fl
 
 template <int DT>
 __device__ __forceinline__ void row_pass(const VerifyArgs& A, RowShared& sh) {
-  const int i = blockIdx.x;
+  const int i = A.row_order ? A.row_order[blockIdx.x] : (int)blockIdx.x;
+  if (i < 0 || i >= A.num_rows) return;
   const int tid = threadIdx.x;
   const int V = A.vocab;
   const int r = row_to_request(A.qo, A.num_requests, i);
@@ -1149,21 +1358,20 @@ __device__ __forceinline__ void resolve_pending(const VerifyArgs& A, int i, int 
   const bool d_ok = d >= 0 && d < V;
   const float xd = d_ok ? Vec<DT>::load1(row, d) : 0.0f;
   ExactOut eo;
-  exact_kept_set<DT>(row, V, out.m, T, k_eff, topp_on ? P : 1.0f, d_ok ? d : -1, xd, sh, eo);
-  out.mode = kModeRange;
-  out.a = eo.argmax;
-  out.bkey = eo.bkey;
-  out.nb = eo.nb;
-  out.nkeep = eo.nkeep;
-  out.zk = eo.zk;
-  out.zn = eo.zn;
-  out.flags |= kRecExact;
-  // a kept set that fits becomes an explicit list, sorted (ranked pass for the
-  // ties at the boundary, then a sort of the kept entries)
-  bool listed = false;
-  {
+  bool listed = false, done = false;
+  if constexpr (DT == 1) {
+    if (k_eff == V && topp_on) {
+      int tcut = V;
+      done = exact_topp_codes<DT>(row, V, out.m, T, P, d_ok ? d : -1, xd, A.build != 0,
+                                  A.list + (size_t)i * kListCap, sh, eo, tcut, listed);
+      out.tie_cut = tcut;
+    }
+  }
+  if (!done) {
+    exact_kept_set<DT>(row, V, out.m, T, k_eff, topp_on ? P : 1.0f, d_ok ? d : -1, xd, sh, eo);
     // one ranked pass: the kept entries (when they fit a list) and the id
-    // just past the last kept tie at the boundary
+    // just past the last kept tie at the boundary; a kept set that fits
+    // becomes an explicit list, sorted
     const uint32_t bkey = eo.bkey;
     const int nb = eo.nb;
     const bool fits = eo.nkeep <= kListCap;
@@ -1186,7 +1394,6 @@ __device__ __forceinline__ void resolve_pending(const VerifyArgs& A, int i, int 
     __syncthreads();
     const int n = sh.count;
     out.tie_cut = sh.found;
-    out.flags |= kRecTieCut;
     __syncthreads();
     if (fits && n == eo.nkeep) {
       sort_desc(sh, n);
@@ -1198,10 +1405,17 @@ __device__ __forceinline__ void resolve_pending(const VerifyArgs& A, int i, int 
         le.x = entry_val(en);
         L[t] = le;
       }
-      out.mode = kModeList;
       listed = true;
     }
   }
+  out.mode = listed ? kModeList : kModeRange;
+  out.a = eo.argmax;
+  out.bkey = eo.bkey;
+  out.nb = eo.nb;
+  out.nkeep = eo.nkeep;
+  out.zk = eo.zk;
+  out.zn = eo.zn;
+  out.flags |= kRecExact | kRecTieCut;
   double pd = 0.0;
   if (d_ok) {
     const uint32_t kd = fkey(xd);
@@ -1349,32 +1563,46 @@ __device__ int stream_race(const void* row, int V, const RowRec& rr, float T, co
   return w.key > 0.0 ? w.id : -1;
 }
 
-// Race over every element of an all-mode row.  Each element gets a fp32 log2
-// key (log2 of the weight minus log2 E) within kEta of the exact one, from one
-// Philox call per four consecutive tokens; an element whose best possible key
-// is below the thread's best lower bound needs no uniform (-log2 E <= 24).
-// Each thread keeps its two best upper bounds and the largest one it dropped;
-// when every dropped bound is below the block's best lower bound B, the winner
-// is among the kept candidates with upper bound >= B, which are evaluated
-// exactly in fp64.  Returns -2 when that does not hold (the caller falls back).
-template <int DT>
-__device__ int stream_race_all(const void* row, int V, float m, double zn, uint32_t kmin,
-                               int tie_cut, float T, const float* qrow, bool residual,
-                               uint64_t seed, uint32_t rid, uint32_t pos, RowShared& sh) {
-  constexpr int P = Vec<DT>::kEpv;
-  constexpr float kNegInf = -__builtin_huge_valf();
-  const float c = kLog2e / T;
-  const float l2zn = residual ? (float)log2(zn) : 0.0f;
-  float best_lo = kNegInf, up1 = kNegInf, up2 = kNegInf, dropped = kNegInf;
-  int id1 = -1, id2 = -1;
-  uint32_t gcache = 0xFFFFFFFFu;
-  uint4 oc = make_uint4(0u, 0u, 0u, 0u);
-  const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
-  auto elem = [&](float x, int v) {
+// fp32 bounds on log2 of an element's race key (weight / E, E = -ln U) for
+// the rows whose kept set is the whole row or a key range: lo <= log2 key <=
+// up within kEta of the exact value, from one Philox call per four
+// consecutive tokens (cached).  An element whose best possible key is below a
+// bound `bl` needs no uniform (-log2 E <= 24: race uniforms lie in
+// [2^-24, 1 - 2^-24]).
+struct RaceBounds {
+  float m, c, l2zn;      // max, log2(e)/T, log2 Z_N (residual) or 0
+  uint32_t kmin;         // kept keys: > kmin, or == kmin with id < tie_cut
+  int tie_cut;
+  bool residual;
+  const float* qrow;
+  uint32_t k0, k1, rid, pos;
+  uint32_t gcache;
+  uint4 oc;
+
+  __device__ __forceinline__ RaceBounds(float m_, double zn, float T, uint32_t kmin_, int tie_cut_,
+                                        bool residual_, const float* qrow_, uint64_t seed,
+                                        uint32_t rid_, uint32_t pos_)
+      : m(m_), c(kLog2e / T), l2zn(residual_ ? (float)log2(zn) : 0.0f), kmin(kmin_),
+        tie_cut(tie_cut_), residual(residual_), qrow(qrow_), k0((uint32_t)seed),
+        k1((uint32_t)(seed >> 32)), rid(rid_), pos(pos_), gcache(0xFFFFFFFFu),
+        oc(make_uint4(0u, 0u, 0u, 0u)) {}
+
+  // log2 weight bound of a whole vector from its maximum
+  __device__ __forceinline__ bool vector_may_reach(float vmax, float bl) const {
+    return (vmax - m) * c - l2zn + 24.0f + 2.0f * kEta >= bl;
+  }
+
+  // false when the element is outside the kept range or cannot reach bl
+  __device__ __forceinline__ bool bounds(float x, int v, float bl, float& lo, float& up) {
+    return bounds(x, v, residual ? qrow[v] : 0.0f, bl, lo, up);
+  }
+  // the same with the element's draft probability q (residual rows) given
+  __device__ __forceinline__ bool bounds(float x, int v, float q, float bl, float& lo, float& up) {
+    constexpr float kNegInf = -__builtin_huge_valf();
     const float y = (x - m) * c - l2zn;  // log2 of p (residual) or of the relative weight
-    if (!(y + 24.0f + 2.0f * kEta >= best_lo)) return;
+    if (!(y + 24.0f + 2.0f * kEta >= bl)) return false;
     const uint32_t key = fkey(x);
-    if (key < kmin || (key == kmin && v >= tie_cut)) return;  // outside the kept range
+    if (key < kmin || (key == kmin && v >= tie_cut)) return false;
     const uint32_t g = (uint32_t)v >> 2;
     if (g != gcache) {
       oc = philox4x32_10(k0, k1, make_uint4(pos, rid, 1u, g));
@@ -1388,31 +1616,78 @@ __device__ int stream_race_all(const void* row, int V, float m, double zn, uint3
     const float E = dlt < 0x1.0p-10f ? dlt * (1.0f + 0.5f * dlt)
                                      : -__builtin_amdgcn_logf(U) * 0.6931471805599453f;
     const float l2e = __builtin_amdgcn_logf(E);
-    float lo, up;
     if (!residual) {
       lo = y - l2e - kEta;
       up = y - l2e + kEta;
-    } else {
-      if (!(y + 2.0e-4f - l2e + kEta >= best_lo)) return;  // even with q = 0
-      const float p32 = exp2f(y);
-      const float q = qrow[v];
-      const float rhi = p32 * (1.0f + kRelP) - q;
-      if (!(rhi > 0.0f)) return;
-      const float rlo = p32 * (1.0f - kRelP) - q;
-      up = log2f(rhi) - l2e + kEta;
-      lo = rlo > 0.0f ? log2f(rlo) - l2e - kEta : kNegInf;
+      return true;
     }
+    if (!(y + 2.0e-4f - l2e + kEta >= bl)) return false;  // even with q = 0
+    const float p32 = exp2f(y);
+    const float rhi = p32 * (1.0f + kRelP) - q;
+    if (!(rhi > 0.0f)) return false;
+    const float rlo = p32 * (1.0f - kRelP) - q;
+    up = log2f(rhi) - l2e + kEta;
+    lo = rlo > 0.0f ? log2f(rlo) - l2e - kEta : kNegInf;
+    return true;
+  }
+};
+
+// Exact fp64 race key of element v (value x) of a full or range row.
+__device__ __forceinline__ void race_exact(float x, int v, float m, double zn, double Td,
+                                           const float* qrow, bool residual, uint64_t seed,
+                                           uint32_t rid, uint32_t pos, RaceBest& b) {
+  double wgt = exp(((double)x - (double)m) / Td) / zn;
+  if (residual) wgt = wgt - (double)qrow[v];
+  if (!(wgt > 0.0)) return;
+  const double key = wgt / race_e(seed, rid, pos, (uint32_t)v);
+  if (race_better(key, v, b.key, b.id)) {
+    b.key = key;
+    b.id = v;
+  }
+}
+
+// Candidates of one thread while streaming: its two best upper bounds, the
+// largest upper bound it dropped, and its best lower bound.
+struct RaceTop2 {
+  float best_lo, up1, up2, dropped;
+  int id1, id2;
+  __device__ __forceinline__ RaceTop2()
+      : best_lo(-__builtin_huge_valf()), up1(-__builtin_huge_valf()),
+        up2(-__builtin_huge_valf()), dropped(-__builtin_huge_valf()), id1(-1), id2(-1) {}
+  __device__ __forceinline__ void add(float lo, float up, int v) {
     best_lo = fmaxf(best_lo, lo);
     if (up > up1) {
       dropped = fmaxf(dropped, up2);
-      up2 = up1; id2 = id1;
-      up1 = up; id1 = v;
+      up2 = up1;
+      id2 = id1;
+      up1 = up;
+      id1 = v;
     } else if (up > up2) {
       dropped = fmaxf(dropped, up2);
-      up2 = up; id2 = v;
+      up2 = up;
+      id2 = v;
     } else {
       dropped = fmaxf(dropped, up);
     }
+  }
+};
+
+// Race over every element of an all-mode row (or a range row) by one
+// workgroup.  When every dropped bound is below the block's best lower bound
+// B, the winner is among the kept candidates with upper bound >= B, which are
+// evaluated exactly in fp64.  Returns -2 when that does not hold (the caller
+// falls back).
+template <int DT>
+__device__ int stream_race_all(const void* row, int V, float m, double zn, uint32_t kmin,
+                               int tie_cut, float T, const float* qrow, bool residual,
+                               uint64_t seed, uint32_t rid, uint32_t pos, RowShared& sh) {
+  constexpr int P = Vec<DT>::kEpv;
+  constexpr float kNegInf = -__builtin_huge_valf();
+  RaceBounds rb(m, zn, T, kmin, tie_cut, residual, qrow, seed, rid, pos);
+  RaceTop2 t2;
+  auto elem = [&](float x, int v) {
+    float lo, up;
+    if (rb.bounds(x, v, t2.best_lo, lo, up)) t2.add(lo, up, v);
   };
   const RowSplit<DT> sp(row, V);
   const int tid = threadIdx.x;
@@ -1421,32 +1696,212 @@ __device__ int stream_race_all(const void* row, int V, float m, double zn, uint3
     float x[P];
     Vec<DT>::unpack(__ldg(sp.vbase + vi), x);
     // whole vectors below the bound skip their uniforms
-    const float ym = (vec_max<P>(x) - m) * c - l2zn;
-    if (!(ym + 24.0f + 2.0f * kEta >= best_lo)) continue;
+    if (!rb.vector_may_reach(vec_max<P>(x), t2.best_lo)) continue;
     const int b = sp.head + vi * P;
 #pragma unroll
     for (int e = 0; e < P; ++e) elem(x[e], b + e);
   }
   if (sp.tail0 + tid < V) elem(Vec<DT>::load1(row, sp.tail0 + tid), sp.tail0 + tid);
-  const float B = block_max_f(best_lo, sh.fscr);
-  const float D = block_max_f(dropped, sh.fscr);
+  const float B = block_max_f(t2.best_lo, sh.fscr);
+  const float D = block_max_f(t2.dropped, sh.fscr);
   if (D > kNegInf && !(D < B)) return -2;
-  const double Td = T;
   RaceBest b = {-1.0, 0x7FFFFFFF};
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    const int v = t == 0 ? id1 : id2;
-    const float u = t == 0 ? up1 : up2;
+    const int v = t == 0 ? t2.id1 : t2.id2;
+    const float u = t == 0 ? t2.up1 : t2.up2;
     if (v < 0 || !(u >= B)) continue;
-    const double x = (double)Vec<DT>::load1(row, v);
-    double wgt = exp((x - (double)m) / Td) / zn;
-    if (residual) wgt = wgt - (double)qrow[v];
-    if (!(wgt > 0.0)) continue;
-    const double key = wgt / race_e(seed, rid, pos, (uint32_t)v);
-    if (race_better(key, v, b.key, b.id)) { b.key = key; b.id = v; }
+    race_exact(Vec<DT>::load1(row, v), v, m, zn, (double)T, qrow, residual, seed, rid, pos, b);
   }
   const RaceBest w = block_race_best(b, sh);
   return w.key > 0.0 ? w.id : -1;
+}
+
+// One segment of a full-vocabulary race: item (r, s) of the race grid (a
+// grid-stride loop over requests x segments; items of requests without a
+// race end at once).  The same bounds as stream_race_all, with the next three
+// vectors (and the next vector's draft probabilities) in flight while one is
+// screened; the segment's exact winner goes to race_part[r, s].  When a
+// dropped bound reaches the segment's best lower bound B, a second pass over
+// the segment evaluates exactly every element whose upper bound reaches B.
+template <int DT>
+__device__ void race_segment(const VerifyArgs& A, int r, int sg, RowShared& sh) {
+  constexpr int P = Vec<DT>::kEpv;
+  constexpr float kNegInf = -__builtin_huge_valf();
+  const int S = A.race_segs;
+  const int job = A.race_job[r];
+  const int is = job >> 1;
+  const bool residual = (job & 1) != 0;
+  const RowRec rr = A.rec[is];
+  const int V = A.vocab;
+  const float T = A.temperature[r];
+  const uint32_t rid = A.request_id ? A.request_id[r] : (uint32_t)r;
+  const uint32_t pos = (A.position0 ? A.position0[r] : 0u) + (uint32_t)(is - A.qo[r]);
+  const uint64_t seed = A.seed;
+  const void* row = (const char*)A.logits + (size_t)is * (size_t)A.ld_logits * (DT == 1 ? 2 : 4);
+  const float* qrow = A.draft_probs + (size_t)is * (size_t)A.ld_q;
+  const bool range = rr.mode == kModeRange;
+  RaceBounds rb(rr.m, rr.zn, T, range ? rr.bkey : 0u, range ? rr.tie_cut : 0x7FFFFFFF,
+                residual, qrow, seed, rid, pos);
+  const RowSplit<DT> sp(row, V);
+  const int v0 = (int)((long long)sp.nvec * sg / S);
+  const int v1 = (int)((long long)sp.nvec * (sg + 1) / S);
+  const int tid = threadIdx.x;
+  const double Td = T;
+  RaceTop2 t2;
+  RaceBest b = {-1.0, 0x7FFFFFFF};
+  float B = kNegInf;
+  bool second = false;
+  // first pass: bounds against the thread's best lower bound; second pass:
+  // the ids of the elements whose upper bound reaches B, listed in LDS
+  int* cand = (int*)sh.buf;
+  constexpr int kCandCap = 2 * kCap;
+  auto visit = [&](float x, int v, float q) {
+    float lo, up;
+    if (!second) {
+      if (rb.bounds(x, v, q, t2.best_lo, lo, up)) t2.add(lo, up, v);
+    } else if (rb.bounds(x, v, q, B, lo, up) && up >= B) {
+      const int slot = atomicAdd(&sh.count, 1);
+      if (slot < kCandCap) cand[slot] = v;
+    }
+  };
+  auto qload = [&](int vi, float* q) {
+#pragma unroll
+    for (int e = 0; e < P; ++e) q[e] = (residual && vi < v1) ? qrow[sp.head + vi * P + e] : 0.0f;
+  };
+  for (int pass = 0; pass < 2; ++pass) {
+    if (sg == 0 && tid < sp.head)
+      visit(Vec<DT>::load1(row, tid), tid, residual ? qrow[tid] : 0.0f);
+    const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+    int vi = v0 + tid;
+    uint4 w0 = vi < v1 ? __ldg(sp.vbase + vi) : z;
+    uint4 w1 = vi + kBlock < v1 ? __ldg(sp.vbase + vi + kBlock) : z;
+    uint4 w2 = vi + 2 * kBlock < v1 ? __ldg(sp.vbase + vi + 2 * kBlock) : z;
+    float q0[P];
+    qload(vi, q0);
+    for (; vi < v1; vi += kBlock) {
+      const uint4 w3 = vi + 3 * kBlock < v1 ? __ldg(sp.vbase + vi + 3 * kBlock) : z;
+      float q1[P];
+      qload(vi + kBlock, q1);
+      float x[P];
+      Vec<DT>::unpack(w0, x);
+      if (rb.vector_may_reach(vec_max<P>(x), second ? B : t2.best_lo)) {
+        const int e0 = sp.head + vi * P;
+        // one 32-bit word at a time (fewer live registers than all P at once)
+#pragma unroll 1
+        for (int h = 0; h < 4; ++h) {
+          const uint32_t wd = h == 0 ? w0.x : (h == 1 ? w0.y : (h == 2 ? w0.z : w0.w));
+          if (DT == 1) {
+            const float qa = h == 0 ? q0[0] : (h == 1 ? q0[2] : (h == 2 ? q0[4] : q0[6 % P]));
+            const float qb = h == 0 ? q0[1] : (h == 1 ? q0[3] : (h == 2 ? q0[5] : q0[7 % P]));
+            visit(bf16_lo(wd), e0 + 2 * h, qa);
+            visit(bf16_hi(wd), e0 + 2 * h + 1, qb);
+          } else {
+            const float qa = h == 0 ? q0[0] : (h == 1 ? q0[1 % P] : (h == 2 ? q0[2 % P] : q0[3 % P]));
+            visit(__uint_as_float(wd), e0 + h, qa);
+          }
+        }
+      }
+      w0 = w1;
+      w1 = w2;
+      w2 = w3;
+#pragma unroll
+      for (int e = 0; e < P; ++e) q0[e] = q1[e];
+    }
+    if (sg == S - 1 && sp.tail0 + tid < V)
+      visit(Vec<DT>::load1(row, sp.tail0 + tid), sp.tail0 + tid,
+            residual ? qrow[sp.tail0 + tid] : 0.0f);
+    if (pass == 1) {
+      __syncthreads();
+      const int nc = sh.count;
+      if (nc <= kCandCap) {
+        for (int t = tid; t < nc; t += kBlock) {
+          const int v = cand[t];
+          race_exact(Vec<DT>::load1(row, v), v, rr.m, rr.zn, Td, qrow, residual, seed, rid, pos, b);
+        }
+      } else {
+        // more candidates than the list holds: every element of the segment
+        // whose bound reaches B, evaluated in place
+        const int e_lo = sg == 0 ? 0 : sp.head + v0 * P;
+        const int e_hi = sg == S - 1 ? V : sp.head + v1 * P;
+        rb.gcache = 0xFFFFFFFFu;
+        for (int v = e_lo + tid; v < e_hi; v += kBlock) {
+          const float x = Vec<DT>::load1(row, v);
+          float lo, up;
+          if (rb.bounds(x, v, B, lo, up) && up >= B)
+            race_exact(x, v, rr.m, rr.zn, Td, qrow, residual, seed, rid, pos, b);
+        }
+      }
+      break;
+    }
+    B = block_max_f(t2.best_lo, sh.fscr);
+    const float D = block_max_f(t2.dropped, sh.fscr);
+    if (D > kNegInf && !(D < B)) {
+      second = true;  // a dropped candidate may win: go over the segment again
+      rb.gcache = 0xFFFFFFFFu;
+      if (tid == 0) sh.count = 0;
+      __syncthreads();
+      continue;
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int v = t == 0 ? t2.id1 : t2.id2;
+      const float u = t == 0 ? t2.up1 : t2.up2;
+      if (v < 0 || !(u >= B)) continue;
+      race_exact(Vec<DT>::load1(row, v), v, rr.m, rr.zn, Td, qrow, residual, seed, rid, pos, b);
+    }
+    break;
+  }
+  const RaceBest w = block_race_best(b, sh);
+  if (tid == 0) {
+    RacePart pt;
+    pt.key = w.key;
+    pt.id = w.id;
+    pt.pad = 0;
+    A.race_part[(size_t)r * S + sg] = pt;
+  }
+}
+
+// Winner of a split race: the best segment (ties to the lower id).  A residual
+// that is zero everywhere falls back to p, raced by this workgroup.
+template <int DT>
+__device__ void race_finish(const VerifyArgs& A, RowShared& sh) {
+  const int r = blockIdx.x;
+  const int job = A.race_job[r];
+  if (job < 0) return;
+  const int is = job >> 1;
+  const bool residual = (job & 1) != 0;
+  const int S = A.race_segs;
+  RaceBest b = {-1.0, 0x7FFFFFFF};
+  for (int t = threadIdx.x; t < S; t += kBlock) {
+    const RacePart pt = A.race_part[(size_t)r * S + t];
+    if (pt.key > 0.0 && race_better(pt.key, pt.id, b.key, b.id)) {
+      b.key = pt.key;
+      b.id = pt.id;
+    }
+  }
+  const RaceBest w = block_race_best(b, sh);
+  int sample = w.key > 0.0 ? w.id : -1;
+  bool empty = false;
+  if (residual && sample < 0) {
+    empty = true;
+    const RowRec rr = A.rec[is];
+    const float T = A.temperature[r];
+    const uint32_t rid = A.request_id ? A.request_id[r] : (uint32_t)r;
+    const uint32_t pos = (A.position0 ? A.position0[r] : 0u) + (uint32_t)(is - A.qo[r]);
+    const void* row = (const char*)A.logits + (size_t)is * (size_t)A.ld_logits * (DT == 1 ? 2 : 4);
+    const bool range = rr.mode == kModeRange;
+    sample = stream_race_all<DT>(row, A.vocab, rr.m, rr.zn, range ? rr.bkey : 0u,
+                                 range ? rr.tie_cut : 0x7FFFFFFF, T, nullptr, false, A.seed, rid,
+                                 pos, sh);
+    if (sample == -2)
+      sample = stream_race<DT>(row, A.vocab, rr, T, nullptr, false, A.seed, rid, pos, sh);
+  }
+  if (threadIdx.x == 0) {
+    A.out_tokens[is] = sample;
+    A.next_token[r] = sample;
+    if (A.row_flags) A.row_flags[is] = (uint8_t)(2 | (empty ? 32 : 0));
+  }
 }
 
 // Race over an explicit kept list (kModeList), fp64 throughout.
@@ -1477,6 +1932,7 @@ __device__ void finalize(const VerifyArgs& A, RowShared& sh) {
     if (tid == 0) {
       A.accept_len[r] = 0;
       A.next_token[r] = -1;
+      if (A.race_segs > 0) A.race_job[r] = -1;
     }
     return;
   }
@@ -1518,7 +1974,10 @@ __device__ void finalize(const VerifyArgs& A, RowShared& sh) {
           A.next_token[r] = smp;
         }
       }
-      if (j == 0) sh.sel_exact = fast ? 1 : 0;
+      if (j == 0) {
+        sh.sel_exact = fast ? 1 : 0;
+        if (fast && A.race_segs > 0) A.race_job[r] = -1;
+      }
     }
     __syncthreads();
     if (sh.sel_exact) return;
@@ -1553,6 +2012,7 @@ __device__ void finalize(const VerifyArgs& A, RowShared& sh) {
   const uint32_t pos = (A.position0 ? A.position0[r] : 0u) + (uint32_t)L;
   int sample;
   bool resid_empty = false;
+  int job = -1;  // a full-vocabulary race left to the split race kernels
   if (rr.mode == kModeGreedy) {
     sample = rr.a;
   } else {
@@ -1566,6 +2026,10 @@ __device__ void finalize(const VerifyArgs& A, RowShared& sh) {
         resid_empty = true;
         sample = list_race(Lst, rr, T, qrow, false, A.seed, rid, pos, sh);
       }
+    } else if (A.race_segs > 0 &&
+               (rr.mode == kModeAll || (rr.mode == kModeRange && (rr.flags & kRecTieCut)))) {
+      job = 2 * is + (residual ? 1 : 0);
+      sample = -1;
     } else {
       auto race = [&](bool resid) {
         int smp = -2;
@@ -1599,6 +2063,7 @@ __device__ void finalize(const VerifyArgs& A, RowShared& sh) {
   if (tid == 0) {
     A.accept_len[r] = L;
     A.next_token[r] = sample;
+    if (A.race_segs > 0) A.race_job[r] = job;
   }
 }
 
@@ -1606,6 +2071,27 @@ __global__ __launch_bounds__(kBlock) void finalize_kernel(VerifyArgs A) {
   __shared__ RowShared sh;
   if (A.dtype == 1) finalize<1>(A, sh);
   else finalize<0>(A, sh);
+}
+
+// Grid-stride over (request, segment) items; the race_job read decides for
+// the whole workgroup.
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) void race_segment_kernel(VerifyArgs A) {
+  __shared__ RowShared sh;
+  const int S = A.race_segs;
+  const int n = A.num_requests * S;
+  for (int it = blockIdx.x; it < n; it += gridDim.x) {
+    const int r = it / S;
+    if (A.race_job[r] < 0) continue;
+    if (A.dtype == 1) race_segment<1>(A, r, it - r * S, sh);
+    else race_segment<0>(A, r, it - r * S, sh);
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void race_finish_kernel(VerifyArgs A) {
+  __shared__ RowShared sh;
+  if (A.dtype == 1) race_finish<1>(A, sh);
+  else race_finish<0>(A, sh);
 }
 
 // ---------------------------------------------------- build outputs kernel

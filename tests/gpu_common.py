@@ -41,9 +41,10 @@ def dev_f32(a) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda()
 
 
-def params_for(w, all_greedy=False) -> B.Params:
+def params_for(w, all_greedy=False, list_bounded=None) -> B.Params:
     return B.Params(dev_f32(w.temperature), dev_i32(w.top_k), dev_f32(w.top_p),
-                    dev_i32(w.request_id), dev_i32(w.position0), w.seed, all_greedy)
+                    dev_i32(w.request_id), dev_i32(w.position0), w.seed, all_greedy,
+                    list_bounded)
 
 
 def make_drafts(w, qo, threads=None):
@@ -63,10 +64,11 @@ def oracle_verify(w, qo, drafts, q, verify_cap=None, requests=None, threads=None
                                            threads=threads)
 
 
-def gpu_verify(w, qo, drafts, q, verify_cap=None, all_greedy=False):
+def gpu_verify(w, qo, drafts, q, verify_cap=None, all_greedy=False, list_bounded=None):
     lg = dev_logits(w.logits)
     qt = dev_f32(q) if q is not None else None
-    out = B.rejection_sample(lg, dev_i32(qo), dev_i32(drafts), qt, params_for(w, all_greedy),
+    out = B.rejection_sample(lg, dev_i32(qo), dev_i32(drafts), qt,
+                             params_for(w, all_greedy, list_bounded),
                              dev_i32(verify_cap) if verify_cap is not None else None)
     torch.cuda.synchronize()
     return {k: v.cpu().numpy() for k, v in out.items()}

@@ -98,3 +98,42 @@ def test_workspace_query_grows_with_rows(lib):
     b = lib.spec_verify_workspace_bytes(1000, 1000, 2, 0)
     c = lib.spec_verify_workspace_bytes(10, 1000, 256, 16)
     assert 0 < a < b and a < c and a % 256 == 0
+
+
+def test_sampling_block_layout_matches_header():
+    """The binding's ctypes mirror of sv_sampling has the header's fields in
+    the header's order."""
+    import torch  # noqa: F401  (the binding imports it)
+    from rejection_sampling_amd import binding as B
+    hdr = open(os.path.join(ROOT, "include", "spec_verify.h")).read()
+    body = hdr[hdr.index("typedef struct {", hdr.index("SV_ROW_RESID_EMPTY")):]
+    body = re.sub(r"/\*.*?\*/", "", body[: body.index("} sv_sampling;")], flags=re.S)
+    names = re.findall(r"(\w+);", body)
+    assert names == [f for f, _ in B.Sampling._fields_]
+
+
+def test_row_order_puts_heavy_requests_first():
+    """Host-side row schedule: a permutation of the rows with every row of a
+    heavy request (sampled, top-k off, top-p on; or top-k above the
+    single-pass limit) ahead of the others, each group in natural order."""
+    import torch
+    from rejection_sampling_amd import binding as B
+    V = 1000
+    T = torch.tensor([0.0, 0.8, 1.0, 0.7, 0.9, 1.1])
+    k = torch.tensor([0, 0, 20, 0, 300, 0], dtype=torch.int32)
+    P = torch.tensor([0.9, 0.9, 0.9, 1.0, 1.0, 0.5])
+    heavy = [False, True, False, False, True, True]
+    qo = torch.tensor([0, 3, 5, 5, 9, 10, 13], dtype=torch.int32)
+    p = B.Params.__new__(B.Params)
+    p._host = (T, k, P)
+    assert p.heavy_requests(V).tolist() == heavy
+    order = B.row_order(qo, p, V)
+    rows_of = [list(range(int(qo[r]), int(qo[r + 1]))) for r in range(6)]
+    first = [i for r in range(6) if heavy[r] for i in rows_of[r]]
+    rest = [i for r in range(6) if not heavy[r] for i in rows_of[r]]
+    assert order.tolist() == first + rest
+    # nothing to reorder when no request (or every request) is heavy
+    p._host = (T, torch.full((6,), 20, dtype=torch.int32), P)
+    assert B.row_order(qo, p, V) is None
+    p._host = (torch.ones(6), torch.zeros(6, dtype=torch.int32), torch.full((6,), 0.9))
+    assert B.row_order(qo, p, V) is None

@@ -83,6 +83,46 @@ def test_small_grid_peaked_bf16():
     _run_small(_small(6, 50000, sigma=4.0, peak=8.0), label="peaked bf16 grid")
 
 
+def test_split_race_and_one_workgroup_race():
+    """Rows sampled over the whole vocabulary (top-k off): split over
+    workgroups by default, and raced by one workgroup each when the
+    bounded-list hint is given although it does not hold.  Both match the
+    oracle."""
+    w = _small(12, 40000, R=24)
+    qo = w.qo_indptr()
+    q, d = make_drafts(w, qo, THREADS)
+    ref = oracle_verify(w, qo, d, q, threads=THREADS)
+    assert np.any((w.top_k == 0) & (w.temperature > 0))
+    for bounded in (False, True):
+        progress(f"race split, list_bounded={bounded}")
+        gpu = gpu_verify(w, qo, d, q, list_bounded=bounded)
+        compare_verify(gpu, ref, qo, label=f"list_bounded={bounded}")
+
+
+def test_row_order_hint_changes_nothing():
+    """Rows of heavy requests scheduled first give the same outputs, bit for
+    bit, as the natural order (every result is keyed by request and position),
+    and both match the oracle."""
+    from rejection_sampling_amd import binding as B
+    w = _small(13, 40000, R=24)
+    qo = w.qo_indptr()
+    q, d = make_drafts(w, qo, THREADS)
+    ref = oracle_verify(w, qo, d, q, threads=THREADS)
+    prm = params_for(w)
+    assert B.row_order(dev_i32(qo), prm, w.vocab) is not None
+    outs = []
+    for reorder in (False, True):
+        progress(f"row order hint, reorder={reorder}")
+        call = B.PreparedRejectionSample(dev_logits(w.logits), dev_i32(qo), dev_i32(d), dev_f32(q),
+                                         prm, reorder=reorder)
+        o = call()
+        torch.cuda.synchronize()
+        outs.append({k: v.cpu().numpy() for k, v in o.items()})
+    for key in outs[0]:
+        assert np.array_equal(outs[0][key], outs[1][key]), key
+    compare_verify(outs[1], ref, qo, label="row order")
+
+
 def test_verify_cap():
     w = _small(7, 12003)
     g = np.random.default_rng(1)
