@@ -88,7 +88,7 @@ __global__ void accept_prefix_kernel(const uint8_t* accepted, const int32_t* qo,
 constexpr int kRowBlock = SV_BLOCK;
 constexpr int kPlanBlock = 1024;
 constexpr size_t kRowRecBytes = 64;
-constexpr int kRaceSegElems = 8192;  // vocabulary elements per race segment
+constexpr int kRaceSegElems = 4096;  // vocabulary elements per race segment
 constexpr int kMaxRaceSegs = 64;
 constexpr int kRaceGrid = 768;      // race-segment workgroups (three per CU resident)
 

@@ -892,15 +892,17 @@ __device__ __forceinline__ void for_each_element_lean(const void* row, int V, F&
   if (sp.tail0 + tid < V) f(Vec<DT>::load1(row, sp.tail0 + tid), sp.tail0 + tid);
 }
 
-// As for_each_element_lean with up to 2U vectors in flight per thread (the
-// next group of U is loaded while the current one is visited): a pass that
-// one workgroup makes over a whole row is bound by load latency otherwise.
-template <int DT, int U, class F>
-__device__ __forceinline__ void for_each_element_deep(const void* row, int V, F&& f) {
+// Every element of a row for a pass that one workgroup makes over the whole
+// row: vec(x, id0) gets each 16-byte vector unpacked (P elements, ids id0..),
+// elem(x, id) the scalar head and tail elements.  Up to 2U vectors are in
+// flight per thread (the next group of U is loaded while the current one is
+// visited): such a pass is bound by load latency otherwise.
+template <int DT, int U, class FV, class FE>
+__device__ __forceinline__ void for_each_vector_deep(const void* row, int V, FV&& vec, FE&& elem) {
   constexpr int P = Vec<DT>::kEpv;
   const RowSplit<DT> sp(row, V);
   const int tid = threadIdx.x;
-  if (tid < sp.head) f(Vec<DT>::load1(row, tid), tid);
+  if (tid < sp.head) elem(Vec<DT>::load1(row, tid), tid);
   auto load = [&](int v0, uint4* w) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -913,17 +915,9 @@ __device__ __forceinline__ void for_each_element_deep(const void* row, int V, F&
     for (int u = 0; u < U; ++u) {
       const int vi = v0 + u * kBlock;
       if (vi >= sp.nvec) break;
-      const int b = sp.head + vi * P;
-#pragma unroll 1
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t x = q == 0 ? w[u].x : (q == 1 ? w[u].y : (q == 2 ? w[u].z : w[u].w));
-        if (DT == 1) {
-          f(bf16_lo(x), b + 2 * q);
-          f(bf16_hi(x), b + 2 * q + 1);
-        } else {
-          f(__uint_as_float(x), b + q);
-        }
-      }
+      float x[P];
+      Vec<DT>::unpack(w[u], x);
+      vec(x, sp.head + vi * P);
     }
   };
   constexpr int G = kBlock * U;  // vectors per group
@@ -936,7 +930,7 @@ __device__ __forceinline__ void for_each_element_deep(const void* row, int V, F&
     if (v0 + 2 * G < sp.nvec) load(v0 + 2 * G, wa);
     visit(v0 + G, wb);
   }
-  if (sp.tail0 + tid < V) f(Vec<DT>::load1(row, sp.tail0 + tid), sp.tail0 + tid);
+  if (sp.tail0 + tid < V) elem(Vec<DT>::load1(row, sp.tail0 + tid), sp.tail0 + tid);
 }
 
 // Visit every element in tiles of increasing ids with a block-wide rank of the

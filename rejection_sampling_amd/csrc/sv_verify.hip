@@ -264,17 +264,37 @@ __device__ __forceinline__ bool exact_topp_codes(const void* row, int V, float m
   if (tid == 0) sh.sel_digit = -1;
   __syncthreads();
   const uint32_t mk16 = fkey(m) >> 16;
-  const uint32_t keyd = d >= 0 ? fkey(xd) : 0u;
-  uint64_t below = 0;
+  // the lowest binned value: elements below it are summed, not binned
+  const float x_lo = mk16 >= (uint32_t)(kNbCodes - 1)
+                         ? bf16_code_value(mk16 - (uint32_t)(kNbCodes - 1)) : -INFINITY;
+  double below = 0.0;  // sum of the fp32 weights of the unbinned elements
   int amin = 0x7FFFFFFF, tied = 0;
-  for_each_element_deep<DT, 4>(row, V, [&](float x, int i) {
-    const uint32_t key = fkey(x);
-    const uint32_t bin = mk16 - (key >> 16);
-    if (bin < (uint32_t)kNbCodes) atomicAdd(&cnt[bin], 1u);
-    else below += fx(x);
-    if (x == m && i < amin) amin = i;
-    if (d >= 0 && i < d && key == keyd) ++tied;
-  });
+  auto count = [&](float x, int i) {
+    if (x >= x_lo) {
+      atomicAdd(&cnt[mk16 - (fkey(x) >> 16)], 1u);
+      if (x == m && i < amin) amin = i;
+    } else {
+      below += (double)exp2f((x - m) * c);
+    }
+  };
+  auto elem = [&](float x, int i) {
+    count(x, i);
+    if (i < d && x == xd) ++tied;
+  };
+  for_each_vector_deep<DT, 2>(row, V, [&](const float* x, int i0) {
+    const float vmax = vec_max<8>(x);
+    if (vmax < x_lo) {  // the common case: no element is binned
+#pragma unroll
+      for (int e = 0; e < 8; ++e) below += (double)exp2f((x[e] - m) * c);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) count(x[e], i0 + e);
+    }
+    if (i0 < d && vmax >= xd) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) tied += (i0 + e < d && x[e] == xd) ? 1 : 0;
+    }
+  }, elem);
   __syncthreads();
   // masses of this thread's four bins (from the top), then a block scan
   uint32_t cb[4];
@@ -300,18 +320,18 @@ __device__ __forceinline__ bool exact_topp_codes(const void* row, int V, float m
       cincl += yc;
     }
   }
-  uint64_t bsum = below;
-#pragma unroll
-  for (int s = 32; s >= 1; s >>= 1) bsum += shfl_xor_u64(bsum, s);
-  uint64_t* wtot = (uint64_t*)sh.mhist;  // [0..3] bin masses, [4..7] counts, [8..11] below
+  const double bsum = wave_sum_d(below);
+  uint64_t* wtot = (uint64_t*)sh.mhist;  // [0..3] bin masses, [4..7] counts
+  double* wbl = (double*)(sh.mhist + 8);  // [0..3] unbinned weight sums
   if (lane_id() == 63) {
     wtot[wave_id()] = incl;
     wtot[4 + wave_id()] = cincl;
-    wtot[8 + wave_id()] = bsum;
+    wbl[wave_id()] = bsum;
   }
   __syncthreads();
-  uint64_t base = 0, tot = 0, blw = 0;
+  uint64_t base = 0, tot = 0;
   uint32_t cbase = 0;
+  double blw = 0.0;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) {
     if (w < wave_id()) {
@@ -319,9 +339,12 @@ __device__ __forceinline__ bool exact_topp_codes(const void* row, int V, float m
       cbase += (uint32_t)wtot[4 + w];
     }
     tot += wtot[w];
-    blw += wtot[8 + w];
+    blw += wbl[w];  // fixed order: deterministic
   }
-  const uint64_t zk_fx = tot + blw;
+  // the unbinned elements in the same fixed-point units (their weights are
+  // summed in fp64 from fp32 values: within one unit per element of the
+  // per-element truncation)
+  const uint64_t zk_fx = tot + (uint64_t)(blw * scale);
   const double target = (double)P * (double)zk_fx;
   {
     uint64_t above = base + incl - loc;
@@ -373,17 +396,21 @@ __device__ __forceinline__ bool exact_topp_codes(const void* row, int V, float m
     sh.found = V;
   }
   __syncthreads();
-  for_each_element_deep<DT, 4>(row, V, [&](float x, int i) {
-    const uint32_t k16 = fkey(x) >> 16;
-    if (k16 < bp16) return;
-    if (k16 == bp16 && want_ties) {
+  auto elem2 = [&](float x, int i) {
+    if (x < xb) return;
+    if (x == xb && want_ties) {
       const int t = atomicAdd(&sh.wcount[0], 1);
       if (t < kTieBuf) tie_ids[t] = i;
     } else if (want_list) {
       const int slot = atomicAdd(&sh.count, 1);
       if (slot < kCap) sh.buf[slot] = make_entry(x, i);
     }
-  });
+  };
+  for_each_vector_deep<DT, 2>(row, V, [&](const float* x, int i0) {
+    if (vec_max<8>(x) < xb) return;  // the whole vector below the boundary
+#pragma unroll
+    for (int e = 0; e < 8; ++e) elem2(x[e], i0 + e);
+  }, elem2);
   __syncthreads();
   if (want_ties) {
     const int nt = sh.wcount[0];
@@ -1610,6 +1637,12 @@ struct RaceBounds {
     }
     const uint32_t ln = (uint32_t)v & 3u;
     const uint32_t wv = ln == 0 ? oc.x : (ln == 1 ? oc.y : (ln == 2 ? oc.z : oc.w));
+    // E = -ln U >= 1 - U = D 2^-24 (D an integer in [1, 2^24)), so log2 E >=
+    // floor(log2 D) - 24: an element that cannot reach bl even then is done
+    // without the logarithms
+    const uint32_t Dlt = 0x1000000u - (2u * (wv >> 9) + 1u);
+    const float e_lo = (float)(7 - (int)__clz(Dlt));
+    if (!(y + (residual ? 2.0e-4f : 0.0f) - e_lo + 2.0f * kEta >= bl)) return false;
     // log2 E, E = -ln U, within far less than kEta: a short series for U near 1
     const float U = (float)(2u * (wv >> 9) + 1u) * 0x1.0p-24f;
     const float dlt = 1.0f - U;  // exact
@@ -2073,17 +2106,37 @@ __global__ __launch_bounds__(kBlock) void finalize_kernel(VerifyArgs A) {
   else finalize<0>(A, sh);
 }
 
-// Grid-stride over (request, segment) items; the race_job read decides for
-// the whole workgroup.
+// Grid-stride over the (request, segment) items of the requests that have a
+// race: every workgroup first lists those requests in LDS (in request order),
+// so the items spread evenly over the grid.  With more requests than the list
+// holds it strides over every item instead, skipping those without a race.
+constexpr int kRaceJobList = 2048;
+
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) void race_segment_kernel(VerifyArgs A) {
   __shared__ RowShared sh;
+  __shared__ int jobs[kRaceJobList];
   const int S = A.race_segs;
-  const int n = A.num_requests * S;
-  for (int it = blockIdx.x; it < n; it += gridDim.x) {
-    const int r = it / S;
-    if (A.race_job[r] < 0) continue;
-    if (A.dtype == 1) race_segment<1>(A, r, it - r * S, sh);
-    else race_segment<0>(A, r, it - r * S, sh);
+  const int R = A.num_requests;
+  const bool listed = R <= kRaceJobList;
+  int nj = 0;
+  if (listed) {
+    for (int base = 0; base < R; base += kBlock) {
+      const int r = base + (int)threadIdx.x;
+      const int has = (r < R && A.race_job[r] >= 0) ? 1 : 0;
+      int total;
+      const int off = block_exclusive_sum(has, sh.iscr, &total);
+      if (has) jobs[nj + off] = r;
+      nj += total;
+    }
+    __syncthreads();
+  }
+  const int items = (listed ? nj : R) * S;
+  for (int it = blockIdx.x; it < items; it += gridDim.x) {
+    const int j = it / S;
+    const int r = listed ? jobs[j] : j;
+    if (!listed && A.race_job[r] < 0) continue;
+    if (A.dtype == 1) race_segment<1>(A, r, it - j * S, sh);
+    else race_segment<0>(A, r, it - j * S, sh);
     __syncthreads();
   }
 }
