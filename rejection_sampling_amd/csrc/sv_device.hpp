@@ -31,7 +31,7 @@ constexpr int kBlock = SV_BLOCK;          // threads per row workgroup
 constexpr int kWaves = kBlock / 64;
 constexpr int kCap = 4096;                // LDS candidate buffer (64-bit entries)
 constexpr int kKeepTopP = 384;            // candidates kept per wave for top-k-off rows
-constexpr int kThreshTopP = 640;          // per-wave compaction limit for those rows
+constexpr int kThreshTopP = 768;          // per-wave compaction limit for those rows
 constexpr int kTopPEnd = 512;             // top-p vector candidates per wave after the stream
 constexpr int kTopkFast = 256;            // largest k on the buffer path
 constexpr int kTopkVec = 64;              // largest k on the vector-candidate path

@@ -773,6 +773,49 @@ __device__ __forceinline__ void stream_row(const void* row, int V, float c, int 
     wave_tile_end_vec(wb, seg, dat, hist, sh);
     v0 = U * kBlock;
   }
+  if (VEC == 2 && sp.nvec >= U * kBlock) {
+    // first tile of a top-p row: the starting threshold is the key that
+    // about 3/2 keep of the wave's vectors reach, estimated from this tile's
+    // vector maxima (the wave's 64 U of them); the tile's vectors at or above
+    // it are admitted.  A low estimate costs compactions later, a high one
+    // only a smaller certified prefix.
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = load_stream(sp.vbase + u * kBlock + tid);
+    float x[U * P], um[U];
+    int ids[U];
+    const float cm = unpack(v, 0, x, um, ids);
+    tile_stats<SUM, ARG, U, P>(x, ids, cm, c, a);
+    const long long vpw = sp.nvec / kWaves;  // vectors this wave sees
+    long long kr = (64LL * U * (3 * keep / 2) + vpw - 1) / vpw;
+    const int k = kr < 1 ? 1 : (kr > 64 * U ? 64 * U : (int)kr);
+    uint32_t key[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) key[u] = fkey(um[u]);
+    uint32_t tk = 0u;  // k-th largest of the wave's keys, bit by bit
+    for (int b = 31; b >= 0; --b) {
+      const uint32_t cand = tk | (1u << b);
+      int cnt = 0;
+#pragma unroll
+      for (int u = 0; u < U; ++u) cnt += __popcll(__ballot(key[u] >= cand));
+      if (cnt >= k) tk = cand;
+    }
+    const float t0 = key_to_float(tk);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool pass = um[u] >= t0;
+      const uint64_t m = __ballot(pass);
+      if (pass) {
+        const int slot = wb.count + lanes_below(m);
+        if (slot < kWaveCap) seg[slot] = make_entry(um[u], u * kBlock + tid);
+      }
+      wb.count += __popcll(m);
+    }
+    wb.tau = t0;  // later vectors with max equal to t0 have larger ids: strict from here
+    if (lane_id() == 0) sh.wtau[w] = t0;
+    wave_tile_end_vec(wb, seg, nullptr, hist, sh);
+    v0 = U * kBlock;
+  }
   if (BUF) {
     // smaller tiles first, so the segment cannot overflow before tau settles
     auto small = [&](auto Ut) {

@@ -1356,7 +1356,7 @@ __device__ __forceinline__ void row_pass(const VerifyArgs& A, RowShared& sh) {
   if (tid == 0) *rec = out;
 }
 
-__global__ __launch_bounds__(kBlock) void row_pass_kernel(VerifyArgs A) {
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) void row_pass_kernel(VerifyArgs A) {
   __shared__ RowShared sh;
   if (A.dtype == 1) row_pass<1>(A, sh);
   else row_pass<0>(A, sh);
