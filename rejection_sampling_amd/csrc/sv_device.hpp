@@ -287,8 +287,15 @@ __device__ __forceinline__ double block_exclusive_sum_d(double v, double* scratc
   return base + (incl - v);
 }
 
-// Upper bound search: request of packed row i (qo non-decreasing, qo[0]=0).
-__device__ __forceinline__ int row_to_request(const int32_t* qo, int R, int i) {
+// Request of packed row i: the r with qo[r] <= i < qo[r + 1] (qo
+// non-decreasing, qo[0] = 0, qo[R] = rows).  Evenly packed windows resolve
+// from the proportional guess in one load round; otherwise an upper-bound
+// search.
+__device__ __forceinline__ int row_to_request(const int32_t* qo, int R, int rows, int i) {
+  if (rows > 0) {
+    const int g = (int)(((long long)i * R) / rows);
+    if (g < R && __ldg(qo + g) <= i && i < __ldg(qo + g + 1)) return g;
+  }
   int lo = 0, hi = R;  // find last r with qo[r] <= i, among requests with rows
   while (lo < hi) {
     int mid = (lo + hi + 1) >> 1;

@@ -550,13 +550,11 @@ __device__ __forceinline__ int wave_shrink(uint64_t* src, int* srci, int n, int 
   return n;
 }
 
-// Top-k rows with k <= 64, run by wave 0 once the block's streaming is done:
-// the best k vectors among the wave candidates, their elements (and the
-// unvectorised head and tail) at or above the k-th vector max, the best k of
-// those in order, then the fp64 weights relative to the row max m, the top-p
-// walk over the k-set (Top-k sampling, then nucleus sampling on the
-// truncated distribution) and the kept list.  Returns false when the row
-// needs the exact path (fewer than k finite elements).
+// Top-k rows with k <= 64 are finished by wave 0 once the block's streaming
+// is done: the best k vectors among the wave candidates, their elements (and
+// the unvectorised head and tail) at or above the k-th vector max, the best k
+// of those in order (vec_topk_select), then the kept set (vec_kept).
+
 // One kept entry per lane of wave 0 after the vector-candidate finish.
 struct VecKept {
   float x;    // logit
@@ -567,11 +565,13 @@ struct VecKept {
   double zn;
 };
 
+// The best min(k, #finite) elements of the vector candidates (wave 0), sorted
+// by (value desc, id asc) into sh.buf[kVecSortOff, +n).  Returns n, or -1 when
+// the candidates cannot certify them (a pile of ties beyond the element area)
+// or, with need_k, when fewer than k elements are finite.
 template <int DT>
-__device__ __forceinline__ bool topk_vec_finish(int V, int k, float m, float T, bool topp_on,
-                                                float P, int d, const RowSplit<DT>& sp,
-                                                const float* qrow, RowShared& sh, RowRec& out,
-                                                double& pd, ListEntry* L, VecKept& kk) {
+__device__ __forceinline__ int vec_topk_select(int V, int k, bool need_k, const RowSplit<DT>& sp,
+                                               RowShared& sh) {
   constexpr int PE = Vec<DT>::kEpv;
   constexpr float kNegInf = -__builtin_huge_valf();
   const int l = lane_id();
@@ -593,7 +593,7 @@ __device__ __forceinline__ bool topk_vec_finish(int V, int k, float m, float T, 
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) {
     cnt[w] = sh.wcount[w];
-    if (cnt[w] > 128) return false;  // not reached: segments end at or below kThreshVec
+    if (cnt[w] > 128) return -1;  // not reached: segments end at or below kThreshVec
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int e = r * 64 + l;
@@ -675,7 +675,7 @@ __device__ __forceinline__ bool topk_vec_finish(int V, int k, float m, float T, 
   ecnt += sp_in ? 1 : 0;
   const int eincl = wave_inclusive_sum(ecnt);
   const int ne = __shfl(eincl, 63, 64);
-  if (ne < k || ne > kVecElemCap) return false;  // too few finite, or a pile of ties
+  if ((need_k && ne < k) || ne > kVecElemCap) return -1;  // too few finite, or a pile of ties
   {
     int slot = eincl - ecnt;
 #pragma unroll
@@ -692,10 +692,21 @@ __device__ __forceinline__ bool topk_vec_finish(int V, int k, float m, float T, 
     wave_compact(E, hist, nel, k);
     nel = k;
   }
-  wave_rank_top(E, nullptr, nel, k, S, nullptr);
-  const uint64_t el = l < k ? S[l] : 0ull;
-  if (!(entry_val(S[k - 1]) > kNegInf)) return false;  // fewer than k finite elements
+  const int nt = wave_rank_top(E, nullptr, nel, k, S, nullptr);
+  const uint64_t fin = __ballot(l < nt && entry_val(S[l < nt ? l : 0]) > kNegInf);
+  const int nf = __popcll(fin);  // sorted: the finite ones come first
+  if (need_k && nf < k) return -1;  // fewer than k finite elements
+  return nf;
+}
 
+// Kept set of a top-k row from its k best elements (lane l < k holds the
+// l-th, `el`): fp64 weights relative to the row max m, the top-p walk over the
+// k-set (top-k sampling, then nucleus sampling on the truncated
+// distribution), p(d), the kept list and the per-lane kept entries.
+__device__ __forceinline__ void vec_kept(uint64_t el, int k, float m, float T, bool topp_on,
+                                         float P, int d, const float* qrow, RowRec& out,
+                                         double& pd, ListEntry* L, VecKept& kk) {
+  const int l = lane_id();
   const bool valid = l < k;
   const float xv = entry_val(el);
   const int idv = entry_idx(el);
@@ -730,6 +741,18 @@ __device__ __forceinline__ bool topk_vec_finish(int V, int k, float m, float T, 
   kk.q = qv;
   kk.nkeep = nkeep;
   kk.zn = zn;
+}
+
+// Both steps on one row; false when the row needs the exact path (fewer than
+// k finite elements, or ties the candidates cannot certify).
+template <int DT>
+__device__ __forceinline__ bool topk_vec_finish(int V, int k, float m, float T, bool topp_on,
+                                                float P, int d, const RowSplit<DT>& sp,
+                                                const float* qrow, RowShared& sh, RowRec& out,
+                                                double& pd, ListEntry* L, VecKept& kk) {
+  if (vec_topk_select<DT>(V, k, true, sp, sh) < 0) return false;
+  const uint64_t el = lane_id() < k ? sh.buf[kVecSortOff + lane_id()] : 0ull;
+  vec_kept(el, k, m, T, topp_on, P, d, qrow, out, pd, L, kk);
   return true;
 }
 
@@ -1051,13 +1074,52 @@ __device__ __forceinline__ int block_kept_race(int nkeep, float m, double zn, fl
   return b.key > 0.0 ? b.id : -1;
 }
 
+// Per-request sampling parameters after the device-side clamps: T <= 0 or
+// NaN is greedy, k <= 0 or >= V is off, P >= 1 is off, P <= 0 keeps the top
+// token only.
+struct RowParams {
+  float T, P;
+  int k_eff;
+  bool greedy, topp_on;
+};
+__device__ __forceinline__ RowParams row_params(const VerifyArgs& A, int r) {
+  RowParams p;
+  const int V = A.vocab;
+  p.T = A.temperature ? A.temperature[r] : 0.0f;
+  p.greedy = !(p.T > 0.0f);
+  const int k = A.top_k ? A.top_k[r] : 0;
+  p.P = A.top_p ? A.top_p[r] : 1.0f;
+  p.k_eff = (k > 0 && k < V) ? k : V;
+  p.topp_on = p.P < 1.0f;
+  if (!(p.P > 0.0f) && !(p.P != p.P)) {  // P <= 0: keep only the top token
+    p.k_eff = 1;
+    p.topp_on = false;
+  }
+  return p;
+}
+// Greedy verify with every tested draft: accept iff it equals the argmax.
+__device__ __forceinline__ void greedy_record(RowRec& out, float m, int a, bool tested, int d,
+                                              bool d_ok) {
+  out.m = m;
+  out.a = a;
+  out.mode = kModeGreedy;
+  out.nkeep = 1;
+  out.zn = out.zk = 1.0;
+  if (tested) {
+    out.flags |= kRecTested;
+    if (!d_ok) out.flags |= kRecBadDraft;
+    if (d == a) out.flags |= kRecAccept;
+    out.pd = d == a ? 1.0f : 0.0f;
+  }
+}
+
 template <int DT>
 __device__ __forceinline__ void row_pass(const VerifyArgs& A, RowShared& sh) {
   const int i = A.row_order ? A.row_order[blockIdx.x] : (int)blockIdx.x;
   if (i < 0 || i >= A.num_rows) return;
   const int tid = threadIdx.x;
   const int V = A.vocab;
-  const int r = row_to_request(A.qo, A.num_requests, i);
+  const int r = row_to_request(A.qo, A.num_requests, A.num_rows, i);
   const int s = A.qo[r], e = A.qo[r + 1];
   const int j = i - s;
   const int gamma = e - s - 1;
@@ -1077,16 +1139,12 @@ __device__ __forceinline__ void row_pass(const VerifyArgs& A, RowShared& sh) {
     }
     return;
   }
-  const float T = A.temperature ? A.temperature[r] : 0.0f;
-  const bool greedy = !(T > 0.0f);
-  int k = A.top_k ? A.top_k[r] : 0;
-  const float P = A.top_p ? A.top_p[r] : 1.0f;
-  int k_eff = (k > 0 && k < V) ? k : V;
-  bool topp_on = P < 1.0f;
-  if (!(P > 0.0f) && !(P != P)) {  // P <= 0: keep only the top token
-    k_eff = 1;
-    topp_on = false;
-  }
+  const RowParams rp = row_params(A, r);
+  const float T = rp.T;
+  const bool greedy = rp.greedy;
+  const float P = rp.P;
+  int k_eff = rp.k_eff;
+  bool topp_on = rp.topp_on;
   const float teff = greedy ? 1.0f : T;
   const float c = kLog2e / teff;
   const void* row = (const char*)A.logits + (size_t)i * (size_t)A.ld_logits * (DT == 1 ? 2 : 4);
@@ -1120,17 +1178,7 @@ __device__ __forceinline__ void row_pass(const VerifyArgs& A, RowShared& sh) {
       const double Z = block_sum_d(part, sh.dscr);
       out.lse = (float)((double)m / (double)teff + log(Z));
     }
-    out.m = m;
-    out.a = a;
-    out.mode = kModeGreedy;
-    out.nkeep = 1;
-    out.zn = out.zk = 1.0;
-    if (tested) {
-      out.flags |= kRecTested;
-      if (!d_ok) out.flags |= kRecBadDraft;
-      if (d == a) out.flags |= kRecAccept;
-      out.pd = d == a ? 1.0f : 0.0f;
-    }
+    greedy_record(out, m, a, tested, d, d_ok);
     if (tid == 0) *rec = out;
     return;
   }
@@ -1758,7 +1806,7 @@ __device__ int stream_race_all(const void* row, int V, float m, double zn, uint3
 // dropped bound reaches the segment's best lower bound B, a second pass over
 // the segment evaluates exactly every element whose upper bound reaches B.
 template <int DT>
-__device__ void race_segment(const VerifyArgs& A, int r, int sg, RowShared& sh) {
+__device__ __forceinline__ void race_segment(const VerifyArgs& A, int r, int sg, RowShared& sh) {
   constexpr int P = Vec<DT>::kEpv;
   constexpr float kNegInf = -__builtin_huge_valf();
   const int S = A.race_segs;
@@ -1898,7 +1946,7 @@ __device__ void race_segment(const VerifyArgs& A, int r, int sg, RowShared& sh) 
 // Winner of a split race: the best segment (ties to the lower id).  A residual
 // that is zero everywhere falls back to p, raced by this workgroup.
 template <int DT>
-__device__ void race_finish(const VerifyArgs& A, RowShared& sh) {
+__device__ __forceinline__ void race_finish(const VerifyArgs& A, RowShared& sh) {
   const int r = blockIdx.x;
   const int job = A.race_job[r];
   if (job < 0) return;
@@ -1956,7 +2004,7 @@ __device__ int list_race(const ListEntry* L, const RowRec& rr, float T, const fl
 
 // ------------------------------------------------------- finalize kernel
 template <int DT>
-__device__ void finalize(const VerifyArgs& A, RowShared& sh) {
+__device__ __forceinline__ void finalize(const VerifyArgs& A, RowShared& sh) {
   const int r = blockIdx.x;
   const int tid = threadIdx.x;
   const int s = A.qo[r], e = A.qo[r + 1];
@@ -2149,11 +2197,11 @@ __global__ __launch_bounds__(kBlock) void race_finish_kernel(VerifyArgs A) {
 
 // ---------------------------------------------------- build outputs kernel
 template <int DT>
-__device__ void build_out(const VerifyArgs& A, const BuildOutArgs& B, RowShared& sh) {
+__device__ __forceinline__ void build_out(const VerifyArgs& A, const BuildOutArgs& B, RowShared& sh) {
   const int i = blockIdx.x;
   const int tid = threadIdx.x;
   const int V = A.vocab;
-  const int r = row_to_request(A.qo, A.num_requests, i);
+  const int r = row_to_request(A.qo, A.num_requests, A.num_rows, i);
   if (A.rec[i].mode == kModePending) resolve_pending<DT>(A, i, r, i - A.qo[r], false, false, sh);
   const RowRec rr = A.rec[i];
   const float T = A.temperature ? A.temperature[r] : 0.0f;
