@@ -3,6 +3,7 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdio>
 #include <cstring>
 #include <mutex>
@@ -106,6 +107,20 @@ int32_t check_launch(const char* what) {
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Row-pass workgroups resident at once on the current device.
+int resident_row_workgroups() {
+  static std::atomic<int> cached[64];  // CU count per device (0: not read yet)
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  int cus = dev < 64 ? cached[dev].load(std::memory_order_relaxed) : 0;
+  if (cus == 0) {
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    if (dev < 64) cached[dev].store(cus, std::memory_order_relaxed);
+  }
+  return cus * sv::kRowPassPerCU;
+}
 
 }  // namespace
 
@@ -252,6 +267,7 @@ int32_t spec_verify_rejection_sample(const void* target_logits, sv_dtype dt, int
   A.row_flags = row_flags;
   if (!draft_probs) A.temperature = nullptr;  // SV_ALL_GREEDY: every request greedy
   A.race_segs = draft_probs ? race_segments(vocab, sp->flags) : 0;
+  A.level = num_rows <= resident_row_workgroups() ? 1 : 0;
   if (num_rows > 0) launch(0, sv::row_pass_kernel, dim3(num_rows), dim3(sv::kRowBlock), s, A);
   if ((rc = check_launch("row pass"))) return rc;
   launch(1, sv::finalize_kernel, dim3(num_requests), dim3(sv::kRowBlock), s, A);

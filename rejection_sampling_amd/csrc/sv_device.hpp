@@ -168,6 +168,44 @@ __device__ __forceinline__ T wave_inclusive_sum(T v) {
   }
   return v;
 }
+// Inclusive sum over the lanes of a fully active wave by DPP row shifts and
+// row broadcasts (register moves, no LDS round trips).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_from(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROWS, 0xF, false);
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double dpp_from_d(double v) {
+  const int lo = dpp_from<CTRL, ROWS>(__double2loint(v));
+  const int hi = dpp_from<CTRL, ROWS>(__double2hiint(v));
+  return __hiloint2double(hi, lo);
+}
+__device__ __forceinline__ int wave_scan_dpp(int v) {
+  v += dpp_from<0x111, 0xF>(v);  // row_shr:1
+  v += dpp_from<0x112, 0xF>(v);  // row_shr:2
+  v += dpp_from<0x114, 0xF>(v);  // row_shr:4
+  v += dpp_from<0x118, 0xF>(v);  // row_shr:8
+  v += dpp_from<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_from<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  return v;
+}
+__device__ __forceinline__ double wave_scan_dpp(double v) {
+  v += dpp_from_d<0x111, 0xF>(v);
+  v += dpp_from_d<0x112, 0xF>(v);
+  v += dpp_from_d<0x114, 0xF>(v);
+  v += dpp_from_d<0x118, 0xF>(v);
+  v += dpp_from_d<0x142, 0xA>(v);
+  v += dpp_from_d<0x143, 0xC>(v);
+  return v;
+}
+// Value of lane l - 1 (0 in lane 0): DPP wave_shr:1.
+__device__ __forceinline__ double wave_prev_d(double v) { return dpp_from_d<0x138, 0xF>(v); }
+__device__ __forceinline__ double readlane_d(double v, int lane) {
+  const int lo = __builtin_amdgcn_readlane(__double2loint(v), lane);
+  const int hi = __builtin_amdgcn_readlane(__double2hiint(v), lane);
+  return __hiloint2double(hi, lo);
+}
+
 __device__ __forceinline__ double wave_sum_d(double v) {
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);

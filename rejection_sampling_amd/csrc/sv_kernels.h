@@ -50,6 +50,9 @@ struct VerifyArgs {
   int32_t race_segs;
   int32_t* race_job;      // [num_requests]: 2 * row + residual, or -1
   RacePart* race_part;    // [num_requests, race_segs]
+  // every row-pass workgroup is resident at once: rows on one CU are kept
+  // level by progress-based wave priorities
+  int32_t level;
 };
 
 struct BuildOutArgs {
@@ -86,6 +89,7 @@ __global__ void accept_prefix_kernel(const uint8_t* accepted, const int32_t* qo,
 
 // sizes shared with the host
 constexpr int kRowBlock = SV_BLOCK;
+constexpr int kRowPassPerCU = 4;     // row-pass workgroups resident per CU (LDS and VGPR bound)
 constexpr int kPlanBlock = 1024;
 constexpr size_t kRowRecBytes = 64;
 constexpr int kRaceSegElems = 4096;  // vocabulary elements per race segment

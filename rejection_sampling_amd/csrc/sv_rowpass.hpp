@@ -354,40 +354,35 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
                                         __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
+// k-th largest of the keys a and b of every lane (absent keys are 0), or 0
+// when fewer than k keys are nonzero: a radix select two bits at a time with
+// three independent ballot counts per step, from the top bit down to bit
+// `lo`.  Keys of bf16 values pass lo = 16: their low 16 bits follow from the
+// sign bit (0 for a positive value, all ones for a negative one), so key
+// order is the order of the high halves.
+__device__ __forceinline__ uint32_t wave_kth_key(uint32_t a, uint32_t b, int k, int lo) {
+  uint32_t t = 0u;
+  for (int bit = 30; bit >= lo; bit -= 2) {
+    const uint32_t c1 = t | (1u << bit), c2 = t | (2u << bit), c3 = t | (3u << bit);
+    const int n3 = __popcll(__ballot(a >= c3)) + __popcll(__ballot(b >= c3));
+    const int n2 = __popcll(__ballot(a >= c2)) + __popcll(__ballot(b >= c2));
+    const int n1 = __popcll(__ballot(a >= c1)) + __popcll(__ballot(b >= c1));
+    t = n3 >= k ? c3 : (n2 >= k ? c2 : (n1 >= k ? c1 : t));
+  }
+  if (lo == 16 && t != 0u && !(t & 0x80000000u)) t |= 0xFFFFu;
+  return t;
+}
+
 // Largest lane key k such that at least `keep` lanes (keep <= 64) hold a key
 // >= k: those lanes' entries are `keep` entries at least as good as k.
 __device__ __forceinline__ uint32_t wave_kth_lane_key(uint32_t lk, int keep) {
-  int ge = 0;
-#pragma unroll 4
-  for (int u = 0; u < 64; ++u) ge += (uint32_t)__builtin_amdgcn_readlane((int)lk, u) >= lk ? 1 : 0;
-  uint32_t cand = ge >= keep ? lk : 0u;
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) {
-    const uint32_t o = (uint32_t)__shfl_xor((int)cand, d, 64);
-    cand = o > cand ? o : cand;
-  }
-  return cand;
+  return wave_kth_key(lk, 0u, keep, 0);
 }
 
 // As wave_kth_lane_key over two keys per lane (best b1, second b2; 0 when
 // absent), for keep <= 128.
 __device__ __forceinline__ uint32_t wave_kth_lane_key2(uint32_t b1, uint32_t b2, int keep) {
-  int ge1 = 0, ge2 = 0;
-#pragma unroll 4
-  for (int u = 0; u < 64; ++u) {
-    const uint32_t c1 = (uint32_t)__builtin_amdgcn_readlane((int)b1, u);
-    const uint32_t c2 = (uint32_t)__builtin_amdgcn_readlane((int)b2, u);
-    ge1 += (c1 >= b1 ? 1 : 0) + (c2 >= b1 ? 1 : 0);
-    ge2 += (c1 >= b2 ? 1 : 0) + (c2 >= b2 ? 1 : 0);
-  }
-  uint32_t cand = ge1 >= keep ? b1 : 0u;
-  if (ge2 >= keep && b2 > cand) cand = b2;
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) {
-    const uint32_t o = (uint32_t)__shfl_xor((int)cand, d, 64);
-    cand = o > cand ? o : cand;
-  }
-  return cand;
+  return wave_kth_key(b1, b2, keep, 0);
 }
 
 // Threshold key for `keep` <= 64 from per-lane best and second-best keys.
@@ -395,15 +390,10 @@ __device__ __forceinline__ uint32_t wave_threshold_key(uint32_t b1, uint32_t b2,
   return keep <= 32 ? wave_kth_lane_key(b1, keep) : wave_kth_lane_key2(b1, b2, keep);
 }
 
-// k-th largest of one key per lane (lanes with ok == false hold none), by a
-// ballot radix over the 32 key bits; 0 when fewer than k keys are held.
+// k-th largest of one key per lane (lanes with ok == false hold none); 0
+// when fewer than k keys are held.
 __device__ __forceinline__ uint32_t wave_kth_key_ballot(uint32_t key, bool ok, int k) {
-  uint32_t t = 0u;
-  for (int b = 31; b >= 0; --b) {
-    const uint32_t cand = t | (1u << b);
-    if (__popcll(__ballot(ok && key >= cand)) >= k) t = cand;
-  }
-  return t;
+  return wave_kth_key(ok ? key : 0u, 0u, k, 0);
 }
 
 // A key t such that lo <= #(entries of seg[0, n) with key >= t) <= hi,
@@ -648,13 +638,32 @@ __device__ __forceinline__ void tile_buffer_vec(Raw&& raw, const float* um, floa
   }
 }
 
+// Wave priority from a row's progress.  Waves of older workgroups win the
+// CU's instruction arbitration, so rows streamed side by side on one CU would
+// finish far apart and leave the CU short of loads in flight at the end; a
+// wave's priority instead falls from 3 to 0 as its row advances, which keeps
+// the CU's rows level until they end together.
+__device__ __forceinline__ void progress_priority(int t, int ntile, int& cur) {
+  const int lvl = 3 - (4 * t) / (ntile + 1);
+  if (lvl == cur) return;
+  cur = lvl;
+  switch (lvl) {
+    case 3: __builtin_amdgcn_s_setprio(3); break;
+    case 2: __builtin_amdgcn_s_setprio(2); break;
+    case 1: __builtin_amdgcn_s_setprio(1); break;
+    default: __builtin_amdgcn_s_setprio(0); break;
+  }
+}
+
 // Full tiles of U vectors per thread from vector v0 on, two load buffers in
 // turn so the next tile is in flight while one is consumed (the scheduling
 // barrier keeps the compiler from sinking the loads below the consumer).
 // Returns the first vector not consumed.
 template <int DT, int U, class F>
-__device__ __forceinline__ int stream_tiles(const RowSplit<DT>& sp, int v0, F&& consume) {
+__device__ __forceinline__ int stream_tiles(const RowSplit<DT>& sp, int v0, bool level,
+                                            F&& consume) {
   const int ntile = (sp.nvec - v0) / (U * kBlock);
+  int prio = level ? -1 : 0;
   uint4 A[U], B[U];
   auto ld = [&](uint4* v, int t) {
 #pragma unroll
@@ -665,6 +674,7 @@ __device__ __forceinline__ int stream_tiles(const RowSplit<DT>& sp, int v0, F&& 
   if (ntile >= 1) ld(A, 0);
   int t = 0;
   for (; t + 3 <= ntile; t += 2) {
+    if (level) progress_priority(t, ntile, prio);
     ld(B, t + 1);
     consume(A, v0 + t * U * kBlock);
     ld(A, t + 2);
@@ -677,6 +687,7 @@ __device__ __forceinline__ int stream_tiles(const RowSplit<DT>& sp, int v0, F&& 
   } else if (t + 1 == ntile) {
     consume(A, v0 + t * U * kBlock);
   }
+  if (prio > 0) __builtin_amdgcn_s_setprio(0);
   return v0 + ntile * U * kBlock;
 }
 
@@ -689,7 +700,8 @@ __device__ __forceinline__ int stream_tiles(const RowSplit<DT>& sp, int v0, F&& 
 // buffered in VEC mode.
 template <int DT, bool BUF, bool SUM, bool ARG, int VEC = 0>
 __device__ __forceinline__ void stream_row(const void* row, int V, float c, int keep, int thresh,
-                                           int ramp, RowShared& sh, StreamAcc& a) {
+                                           int ramp, RowShared& sh, StreamAcc& a,
+                                           bool level = false) {
   constexpr int P = Vec<DT>::kEpv;
   constexpr int U = SV_UNROLL;
   constexpr float kNegInf = -__builtin_huge_valf();
@@ -841,7 +853,7 @@ __device__ __forceinline__ void stream_row(const void* row, int V, float c, int 
     for (int r = 0; r < ramp; ++r)
       if (v0 + 2 * kBlock <= sp.nvec) small(std::integral_constant<int, 2>{});
   }
-  v0 = stream_tiles<DT, U>(sp, v0, [&](const uint4* v, int vb) {
+  v0 = stream_tiles<DT, U>(sp, v0, level, [&](const uint4* v, int vb) {
     float x[U * P], um[U];
     int ids[U];
     const float cm = unpack(v, vb, x, um, ids);

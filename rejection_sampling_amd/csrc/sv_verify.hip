@@ -637,15 +637,10 @@ __device__ __forceinline__ int vec_topk_select(int V, int k, bool need_k, const 
     vent[r] = has[r] ? C[r * 64 + l] : 0ull;
     di[r] = has[r] ? CI[r * 64 + l] : 0;
   }
-  uint32_t tk = 0u;
-  if (nc >= k) {
-    for (int b = 31; b >= 0; --b) {
-      const uint32_t cand = tk | (1u << b);
-      const int cnt = __popcll(__ballot(has[0] && (uint32_t)(vent[0] >> 32) >= cand)) +
-                      __popcll(__ballot(has[1] && (uint32_t)(vent[1] >> 32) >= cand));
-      if (cnt >= k) tk = cand;
-    }
-  }
+  const uint32_t tk =
+      nc >= k ? wave_kth_key(has[0] ? (uint32_t)(vent[0] >> 32) : 0u,
+                             has[1] ? (uint32_t)(vent[1] >> 32) : 0u, k, DT == 1 ? 16 : 0)
+              : 0u;
   // every vector at or above the k-th key (ties included) holds the top-k;
   // at least k elements reach its value
   const float tv = tk != 0u ? key_to_float(tk) : kNegInf;
@@ -673,8 +668,8 @@ __device__ __forceinline__ int vec_topk_select(int V, int k, bool need_k, const 
     for (int e = 0; e < PE; ++e) ecnt += (has[r] && x[r][e] >= tv) ? 1 : 0;
   const bool sp_in = (hs || ts) && xs >= tv;
   ecnt += sp_in ? 1 : 0;
-  const int eincl = wave_inclusive_sum(ecnt);
-  const int ne = __shfl(eincl, 63, 64);
+  const int eincl = wave_scan_dpp(ecnt);
+  const int ne = __builtin_amdgcn_readlane(eincl, 63);
   if ((need_k && ne < k) || ne > kVecElemCap) return -1;  // too few finite, or a pile of ties
   {
     int slot = eincl - ecnt;
@@ -713,18 +708,17 @@ __device__ __forceinline__ void vec_kept(uint64_t el, int k, float m, float T, b
   // q on the kept candidates, issued early: a rejected row races over p - q
   const double qv = (qrow && valid) ? (double)qrow[idv] : 0.0;
   const double wgt = valid ? exp(((double)xv - (double)m) / (double)T) : 0.0;
-  const double incl = wave_inclusive_sum(wgt);
-  double excl = __shfl_up(incl, 1, 64);
-  if (l == 0) excl = 0.0;
-  const double zk = __shfl(incl, k - 1, 64);
+  const double incl = wave_scan_dpp(wgt);
+  const double excl = wave_prev_d(incl);
+  const double zk = readlane_d(incl, k - 1);
   const double target = topp_on ? (double)P * zk : 2.0 * zk + 1.0;
   const uint64_t stop = __ballot(valid && !(excl < target));
   int nkeep = stop ? __ffsll((unsigned long long)stop) - 1 : k;
   if (nkeep < 1) nkeep = 1;
-  const double zn = __shfl(incl, nkeep - 1, 64);
+  const double zn = readlane_d(incl, nkeep - 1);
   const uint64_t fm = __ballot(l < nkeep && idv == d);
-  pd = fm ? __shfl(wgt, __ffsll((unsigned long long)fm) - 1, 64) / zn : 0.0;
-  out.a = __shfl(idv, 0, 64);
+  pd = fm ? readlane_d(wgt, __ffsll((unsigned long long)fm) - 1) / zn : 0.0;
+  out.a = __builtin_amdgcn_readlane(idv, 0);
   out.zk = zk;
   out.zn = zn;
   out.nkeep = nkeep;
@@ -1168,8 +1162,8 @@ __device__ __forceinline__ void row_pass(const VerifyArgs& A, RowShared& sh) {
 
   // ------------------------------------------------ greedy rows
   if (greedy) {
-    if (need_sum_build) stream_row<DT, false, true, true>(row, V, c, 1, 1, 0, sh, acc);
-    else stream_row<DT, false, false, true>(row, V, c, 1, 1, 0, sh, acc);
+    if (need_sum_build) stream_row<DT, false, true, true>(row, V, c, 1, 1, 0, sh, acc, A.level != 0);
+    else stream_row<DT, false, false, true>(row, V, c, 1, 1, 0, sh, acc, A.level != 0);
     const float m = block_max_f(acc.mx, sh.fscr);
     const uint64_t cand = acc.mx == m ? (uint64_t)(uint32_t)(0x7FFFFFFF - acc.bi) : 0ull;
     const int a = 0x7FFFFFFF - (int)(uint32_t)block_max_u64(cand, sh.uscr);
@@ -1203,18 +1197,18 @@ __device__ __forceinline__ void row_pass(const VerifyArgs& A, RowShared& sh) {
     ramp = 2;
   }
   if (vec_mode) {
-    stream_row<DT, false, false, false, 1>(row, V, c, k_eff, kThreshVec, 0, sh, acc);
+    stream_row<DT, false, false, false, 1>(row, V, c, k_eff, kThreshVec, 0, sh, acc, A.level != 0);
   } else if (all_mode) {
-    if (need_sum_build) stream_row<DT, false, true, true>(row, V, c, 1, 1, 0, sh, acc);
-    else stream_row<DT, false, true, false>(row, V, c, 1, 1, 0, sh, acc);
+    if (need_sum_build) stream_row<DT, false, true, true>(row, V, c, 1, 1, 0, sh, acc, A.level != 0);
+    else stream_row<DT, false, true, false>(row, V, c, 1, 1, 0, sh, acc, A.level != 0);
   } else if (topp_mode) {
-    stream_row<DT, false, true, false, 2>(row, V, c, keep, thresh, 0, sh, acc);
+    stream_row<DT, false, true, false, 2>(row, V, c, keep, thresh, 0, sh, acc, A.level != 0);
   } else if (buf_mode) {
-    if (need_sum) stream_row<DT, true, true, false>(row, V, c, keep, thresh, ramp, sh, acc);
-    else stream_row<DT, true, false, false>(row, V, c, keep, thresh, ramp, sh, acc);
+    if (need_sum) stream_row<DT, true, true, false>(row, V, c, keep, thresh, ramp, sh, acc, A.level != 0);
+    else stream_row<DT, true, false, false>(row, V, c, keep, thresh, ramp, sh, acc, A.level != 0);
   } else {
-    if (need_sum) stream_row<DT, false, true, false>(row, V, c, 1, 1, 0, sh, acc);
-    else stream_row<DT, false, false, false>(row, V, c, 1, 1, 0, sh, acc);
+    if (need_sum) stream_row<DT, false, true, false>(row, V, c, 1, 1, 0, sh, acc, A.level != 0);
+    else stream_row<DT, false, false, false>(row, V, c, 1, 1, 0, sh, acc, A.level != 0);
   }
   const float m = block_max_f(acc.mx, sh.fscr);
   double Z = 0.0;

@@ -123,6 +123,86 @@ def test_row_order_hint_changes_nothing():
     compare_verify(outs[1], ref, qo, label="row order")
 
 
+def _bounded(seed, V, R=32, dtype=W.BF16):
+    """Requests whose kept sets are all bounded lists (0 < top-k <= 4096) or
+    greedy, with ragged windows."""
+    g = np.random.default_rng(seed)
+    gam = g.integers(0, 9, size=R)
+    T = np.where(g.random(R) < 0.25, 0.0, g.uniform(0.4, 1.3, size=R)).astype(np.float32)
+    k = g.choice(np.array([1, 5, 20, 50, 64, 65, 300, 2000], np.int32), size=R)
+    P = g.choice(np.array([1.0, 0.95, 0.9, 0.5], np.float32), size=R)
+    return W.small_prob_workload(seed, R, gam, V, T=T, k=k, P=P, dtype=dtype)
+
+
+@pytest.mark.parametrize("V,dtype", [(20007, W.BF16), (9001, W.F32)])
+def test_list_bounded_hint_changes_nothing(V, dtype):
+    """A batch whose kept sets are all bounded lists (or greedy) gives the same
+    outputs, bit for bit, with the list-bounded hint (no split-race launches)
+    as without it, with and without a verify cap, and matches the oracle."""
+    w = _bounded(31 + V, V, dtype=dtype)
+    qo = w.qo_indptr()
+    q, d = make_drafts(w, qo, THREADS)
+    g = np.random.default_rng(5)
+    for cap in (None, np.array([g.integers(-1, x + 2) for x in w.rows_per_request], np.int32)):
+        progress(f"list-bounded hint V={V} dtype={dtype} cap={'yes' if cap is not None else 'no'}")
+        hinted = gpu_verify(w, qo, d, q, cap, list_bounded=True)
+        plain = gpu_verify(w, qo, d, q, cap, list_bounded=False)
+        for key in hinted:
+            assert np.array_equal(hinted[key], plain[key]), key
+        ref = oracle_verify(w, qo, d, q, cap, threads=THREADS)
+        compare_verify(hinted, ref, qo, cap=cap, label="list-bounded hint")
+
+
+def test_wrong_list_bounded_hint():
+    """The list-bounded hint claimed for requests with top-k off: their
+    correction or bonus token is raced over the whole kept set by one
+    workgroup, and matches the oracle and the call without the hint (which
+    splits that race over workgroups)."""
+    g = np.random.default_rng(77)
+    R = 16
+    T = g.uniform(0.5, 1.2, size=R).astype(np.float32)
+    k = np.where(np.arange(R) % 2 == 0, 0, 20).astype(np.int32)
+    P = np.where(np.arange(R) % 4 < 2, 1.0, 0.9).astype(np.float32)
+    w = W.small_prob_workload(91, R, g.integers(0, 6, size=R), 12007, T=T, k=k, P=P)
+    qo = w.qo_indptr()
+    q, d = make_drafts(w, qo, THREADS)
+    progress("wrong list-bounded hint")
+    hinted = gpu_verify(w, qo, d, q, list_bounded=True)
+    plain = gpu_verify(w, qo, d, q, list_bounded=False)
+    for key in hinted:
+        assert np.array_equal(hinted[key], plain[key]), key
+    ref = oracle_verify(w, qo, d, q, threads=THREADS)
+    compare_verify(hinted, ref, qo, label="wrong hint")
+
+
+def test_empty_requests():
+    """Requests without rows (leading, between others and trailing) get
+    accept_len 0 and next_token -1, with and without the list-bounded hint;
+    the other requests match the oracle."""
+    import dataclasses
+    base = _bounded(55, 9001, R=6)
+    layout = [None, 0, None, None, 1, 2, None, 3, 4, 5, None, None]  # None: no rows
+    pick = lambda a, fill: np.array([a[x] if x is not None else fill for x in layout], a.dtype)
+    w = dataclasses.replace(
+        base, num_requests=len(layout),
+        temperature=pick(base.temperature, np.float32(0.8)), top_k=pick(base.top_k, np.int32(20)),
+        top_p=pick(base.top_p, np.float32(1.0)),
+        request_id=np.arange(len(layout), dtype=np.uint32),
+        position0=pick(base.position0, np.uint32(0)),
+        rows_per_request=pick(base.rows_per_request, np.int32(0)))
+    qo = w.qo_indptr()
+    q, d = make_drafts(w, qo, THREADS)
+    progress("empty requests")
+    hinted = gpu_verify(w, qo, d, q, list_bounded=True)
+    plain = gpu_verify(w, qo, d, q, list_bounded=False)
+    for key in hinted:
+        assert np.array_equal(hinted[key], plain[key]), key
+    empty = [i for i, x in enumerate(layout) if x is None]
+    assert np.all(hinted["accept_len"][empty] == 0) and np.all(hinted["next_token"][empty] == -1)
+    ref = oracle_verify(w, qo, d, q, threads=THREADS)
+    compare_verify(hinted, ref, qo, label="empty requests")
+
+
 def test_verify_cap():
     w = _small(7, 12003)
     g = np.random.default_rng(1)
