@@ -482,6 +482,35 @@ __device__ inline RaceBest block_race_best(RaceBest b, RowShared& sh) {
   return r;
 }
 
+// One step of the wave arg-max below: the (key, id) of the lane CTRL reads,
+// taken when better (lanes without a source read key -1).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ void best_step_dpp(double& key, int& id) {
+  const int klo = __builtin_amdgcn_update_dpp(0, __double2loint(key), CTRL, ROWS, 0xF, false);
+  const int khi =
+      __builtin_amdgcn_update_dpp(__double2hiint(-1.0), __double2hiint(key), CTRL, ROWS, 0xF, false);
+  const int oi = __builtin_amdgcn_update_dpp(0x7FFFFFFF, id, CTRL, ROWS, 0xF, false);
+  const double ok = __hiloint2double(khi, klo);
+  if (race_better(ok, oi, key, id)) {
+    key = ok;
+    id = oi;
+  }
+}
+// Best (key desc, id asc) over a fully active wave, returned in every lane:
+// a prefix arg-max by DPP row shifts and row broadcasts, read at lane 63.
+__device__ __forceinline__ RaceBest wave_best_dpp(RaceBest b) {
+  best_step_dpp<0x111, 0xF>(b.key, b.id);
+  best_step_dpp<0x112, 0xF>(b.key, b.id);
+  best_step_dpp<0x114, 0xF>(b.key, b.id);
+  best_step_dpp<0x118, 0xF>(b.key, b.id);
+  best_step_dpp<0x142, 0xA>(b.key, b.id);
+  best_step_dpp<0x143, 0xC>(b.key, b.id);
+  RaceBest r;
+  r.key = readlane_d(b.key, 63);
+  r.id = __builtin_amdgcn_readlane(b.id, 63);
+  return r;
+}
+
 __device__ __forceinline__ double race_e(uint64_t seed, uint32_t rid, uint32_t pos, uint32_t v) {
   return -log(race_uniform(seed, rid, pos, 1u, v));
 }
@@ -761,13 +790,7 @@ __device__ __forceinline__ int wave_kept_race(const VecKept& kk, bool residual, 
   auto best = [&](double wgt) {
     RaceBest b = {-1.0, 0x7FFFFFFF};
     if (valid && wgt > 0.0) { b.key = wgt / e; b.id = kk.id; }
-#pragma unroll
-    for (int dd = 32; dd >= 1; dd >>= 1) {
-      const double ok = __shfl_xor(b.key, dd, 64);
-      const int oi = __shfl_xor(b.id, dd, 64);
-      if (race_better(ok, oi, b.key, b.id)) { b.key = ok; b.id = oi; }
-    }
-    return b;
+    return wave_best_dpp(b);
   };
   empty = false;
   RaceBest b = best(residual ? p - kk.q : p);
@@ -1113,6 +1136,7 @@ __device__ __forceinline__ void row_pass(const VerifyArgs& A, RowShared& sh) {
   if (i < 0 || i >= A.num_rows) return;
   const int tid = threadIdx.x;
   const int V = A.vocab;
+  const void* row = (const char*)A.logits + (size_t)i * (size_t)A.ld_logits * (DT == 1 ? 2 : 4);
   const int r = row_to_request(A.qo, A.num_requests, A.num_rows, i);
   const int s = A.qo[r], e = A.qo[r + 1];
   const int j = i - s;
@@ -1141,7 +1165,6 @@ __device__ __forceinline__ void row_pass(const VerifyArgs& A, RowShared& sh) {
   bool topp_on = rp.topp_on;
   const float teff = greedy ? 1.0f : T;
   const float c = kLog2e / teff;
-  const void* row = (const char*)A.logits + (size_t)i * (size_t)A.ld_logits * (DT == 1 ? 2 : 4);
   const int d = tested ? A.draft_tokens[i] : -1;
   const bool d_ok = d >= 0 && d < V;
   // q(d) is read now so its latency hides behind the stream
