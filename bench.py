@@ -303,8 +303,9 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     # pass 2: the same steps with each kernel's dispatch stamping HIP events on
-    # the call's stream (begin and end of the kernel); the completion signals
-    # add gaps between kernels, so this pass gives kernel durations only
+    # the call's stream (begin and end of the kernel), the library draining the
+    # stream before each timed launch so a pair brackets one kernel alone; the
+    # drains add gaps between kernels, so this pass gives kernel durations only
     print(f"[bench] timing {args.steps} steps with kernel events", file=sys.stderr, flush=True)
     B.profile_enable(True)
     B.profile_reset()

@@ -174,9 +174,10 @@ const char* spec_verify_status_string(int32_t code);
 const char* spec_verify_last_error(void);
 
 /* Per-kernel timing for measurement: while enabled, every launch of the
- * library records a pair of HIP events on the call's stream; read() waits for
- * them and returns, per kernel id, the launch count and the summed
- * milliseconds since the last reset.  Kernel ids: 0 row pass, 1 request
+ * library first waits for its stream to drain (the host blocks), then
+ * records a pair of HIP events around the kernel on the call's stream;
+ * read() waits for them and returns, per kernel id, the launch count and the
+ * summed milliseconds since the last reset.  Kernel ids: 0 row pass, 1 request
  * finalize, 2 target-probs writer, 3 planner, 4 accept prefix, 5 race
  * segments, 6 race finish. */
 int32_t spec_verify_profile_enable(int32_t on);

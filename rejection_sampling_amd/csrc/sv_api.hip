@@ -86,6 +86,10 @@ void launch(int id, void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t
     }
   }
   if (ev[0] && ev[1]) {
+    // the start stamp is taken when the dispatch is processed, which may be
+    // while the previous kernel on the stream still runs: let the stream
+    // drain first so the pair brackets this kernel alone
+    (void)hipStreamSynchronize(s);
     hipExtLaunchKernelGGL(kernel, grid, block, 0, s, ev[0], ev[1], 0, args...);
     std::lock_guard<std::mutex> g(p.mu);
     p.pending.push_back({id, ev[0], ev[1]});
