@@ -986,16 +986,13 @@ __device__ __forceinline__ bool topp_select(RowShared& sh, int n, float m, float
   __syncthreads();
   constexpr int kTieCap = (kWaves - 1) * 256;
   if (nb < avail && avail <= kTieCap) {
+    // the tie ids in any order (they are ranked among themselves next)
     int* tie_id = (int*)sh.whist[1];
-    int pos0 = 0;
-    for (int b0 = 0; b0 < n; b0 += kBlock) {
-      const int t = b0 + tid;
-      const uint64_t e = t < n ? sh.buf[t] : 0ull;
-      const bool tie = t < n && (uint32_t)(e >> 32) == bkey;
-      int total;
-      const int off = block_exclusive_sum(tie ? 1 : 0, sh.iscr, &total);
-      if (tie) tie_id[pos0 + off] = entry_idx(e);
-      pos0 += total;
+    if (tid == 0) sh.count = 0;
+    __syncthreads();
+    for (int t = tid; t < n; t += kBlock) {
+      const uint64_t e = sh.buf[t];
+      if ((uint32_t)(e >> 32) == bkey) tie_id[atomicAdd(&sh.count, 1)] = entry_idx(e);
     }
     __syncthreads();
     for (int t = tid; t < avail; t += kBlock) {
@@ -1019,26 +1016,37 @@ __device__ __forceinline__ bool topp_select(RowShared& sh, int n, float m, float
   }
   __syncthreads();
   const int cut = sh.found;
-  // compact the kept entries to the front, one round of kBlock at a time
+  // compact the kept entries to the front: every entry is read first (at most
+  // kCap / kBlock per thread), then the kept ones are appended.  Their order
+  // in the buffer is not used (sorted below when asked; the race over them
+  // reduces by key and id), while the weight sums keep each thread's fixed
+  // order of entries.
+  constexpr int kPer = kCap / kBlock;
+  uint64_t ev[kPer];
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    const int t = q * kBlock + tid;
+    ev[q] = t < n ? sh.buf[t] : 0ull;
+  }
+  if (tid == 0) sh.count = 0;
+  __syncthreads();  // every entry read
   double zloc = 0.0, pdl = 0.0;
   uint64_t best = 0ull;
-  int pos0 = 0;
-  for (int b0 = 0; b0 < n; b0 += kBlock) {
-    const int t = b0 + tid;
-    const uint64_t e = t < n ? sh.buf[t] : 0ull;
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    const int t = q * kBlock + tid;
+    const uint64_t e = ev[q];
     const uint32_t key = (uint32_t)(e >> 32);
-    const bool k = t < n && (key > bkey || (key == bkey && entry_idx(e) < cut));
-    int total;
-    const int off = block_exclusive_sum(k ? 1 : 0, sh.iscr, &total);  // reads of the round done
-    if (k) {
-      sh.buf[pos0 + off] = e;
+    if (t < n && (key > bkey || (key == bkey && entry_idx(e) < cut))) {
+      sh.buf[atomicAdd(&sh.count, 1)] = e;
       const double w = exp(((double)entry_val(e) - (double)m) / (double)T);
       zloc += w;
       if (entry_idx(e) == d) pdl = w;
       best = e > best ? e : best;
     }
-    pos0 += total;
   }
+  __syncthreads();
+  const int pos0 = sh.count;
   const double zn = block_sum_d(zloc, sh.dscr);
   const double pdw = block_sum_d(pdl, sh.dscr);
   o.a = entry_idx(block_max_u64(best, sh.uscr));
