@@ -134,9 +134,10 @@ def make_inputs(torch, B, nsets: int, workload: str = "c3"):
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for _ in range(20):
-            _, qo, _ = B.plan_windows(conf, budget, want_survival=False)
+            vl, qo, _ = B.plan_windows(conf, budget, want_survival=False)
         torch.cuda.synchronize()
         extra["planner_us"] = round((time.perf_counter() - t0) / 20 * 1e6, 2)
+        extra["_verify_len"] = vl  # the windows, for the step's acceptance statistics
         rows = min(budget, R * (nb - 1)) + R
     else:
         qo = (torch.arange(R + 1, device=dev, dtype=torch.int32) * nb).contiguous()
@@ -271,6 +272,7 @@ def main():
     R, _, V, desc = WORKLOADS[wl]
     print(f"[bench] building {wl} inputs ({args.sets} logits sets)", file=sys.stderr, flush=True)
     sets, qo, params, rows, V, extra = make_inputs(torch, B, args.sets, wl)
+    windows = extra.pop("_verify_len", None)
     out = {
         "accept_len": torch.empty(R, dtype=torch.int32, device="cuda"),
         "out_tokens": torch.empty(rows, dtype=torch.int32, device="cuda"),
@@ -323,6 +325,20 @@ def main():
     kern_ms = ms_rp / max(n_rp, 1)
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
     acc = out["accept_len"].float().mean().item()   # of the last step's set
+    if windows is not None:
+        # acceptance and trim statistics of the last step over the planner's windows
+        nb = WORKLOADS[wl][1] - 1
+        st = B.acceptance_stats(out["accept_len"], windows, nb)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(20):
+            st = B.acceptance_stats(out["accept_len"], windows, nb)
+        torch.cuda.synchronize()
+        extra["acceptance_stats_us"] = round((time.perf_counter() - t0) / 20 * 1e6, 2)
+        s_ = st.cpu().tolist()
+        extra["trimmed"] = s_[1]
+        extra["trim_regret_rate"] = round(s_[2] / max(s_[1], 1), 4)
+        extra["acceptance_per_verified_token"] = round(s_[3] / max(s_[4], 1), 4)
 
     cpu = cpu_baseline(args.cpu_requests) if (args.cpu_requests > 0 and wl == "c3") else None
     config = {"workload": f"{wl}: {R} requests, {rows} rows x {V} vocab; {desc}",

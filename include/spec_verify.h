@@ -169,6 +169,26 @@ int32_t spec_verify_accept_prefix(const uint8_t* accepted, const int32_t* qo_ind
                                   int32_t num_requests, const int32_t* verify_cap,
                                   int32_t* accept_len, sv_stream_t stream);
 
+/* Acceptance and trim statistics of one verify step (TensorRT-LLM PR #17056,
+ * commit note on the trim-regret metric: a trimmed request that accepted its
+ * entire window was still alive at the cut, so the cut cost acceptance;
+ * per-position acceptance as the consolidation study's section 1 reports it,
+ * the share of drafts whose first j+1 tokens survived).  Request r verified
+ * w_r = verify_len[r] (e.g. the planner's window) of the block's B drafted
+ * positions and accepted L_r = accept_len[r] (e.g. spec_verify_rejection_sample's
+ * output); device data is clamped: w_r to [0, B], L_r to [0, w_r].
+ *   stats [5 + 2B] int64, device:
+ *     [0] requests, [1] trimmed (w_r < B), [2] trim regret (trimmed and
+ *     L_r == w_r), [3] sum of L_r, [4] sum of w_r,
+ *     [5 + j] offered at position j = #{r : w_r > j},
+ *     [5 + B + j] accepted at position j = #{r : L_r > j}, for j < B.
+ *   The trim-regret rate is stats[2] / stats[1]; the acceptance per draft
+ *   token stats[3] / stats[4].  Exact integer counts; one workgroup, no
+ *   workspace.  Requires 0 <= B <= 1024 and R * B < 2^31. */
+int32_t spec_verify_acceptance_stats(const int32_t* accept_len, const int32_t* verify_len,
+                                     int32_t num_requests, int32_t block, int64_t* stats,
+                                     sv_stream_t stream);
+
 /* Diagnostics. */
 const char* spec_verify_status_string(int32_t code);
 const char* spec_verify_last_error(void);
@@ -179,7 +199,7 @@ const char* spec_verify_last_error(void);
  * read() waits for them and returns, per kernel id, the launch count and the
  * summed milliseconds since the last reset.  Kernel ids: 0 row pass, 1 request
  * finalize, 2 target-probs writer, 3 planner, 4 accept prefix, 5 race
- * segments, 6 race finish. */
+ * segments, 6 race finish, 7 acceptance statistics. */
 int32_t spec_verify_profile_enable(int32_t on);
 int32_t spec_verify_profile_read(int32_t kernel_id, int64_t* launches, double* total_ms);
 int32_t spec_verify_profile_reset(void);

@@ -470,6 +470,32 @@ int32_t svref_accept_prefix(const uint8_t* accepted, const int32_t* qo_indptr,
   return 0;
 }
 
+// Acceptance and trim statistics: each request counted once, each position
+// j of its window offered once and accepted when its accepted prefix is
+// longer than j.
+int32_t svref_acceptance_stats(const int32_t* accept_len, const int32_t* verify_len,
+                               int32_t num_requests, int32_t block, int64_t* stats) {
+  if (num_requests < 0 || block < 0 || !stats) return -1;
+  if (num_requests > 0 && (!accept_len || !verify_len)) return -1;
+  const int64_t n = 5 + 2 * (int64_t)block;
+  for (int64_t t = 0; t < n; ++t) stats[t] = 0;
+  stats[0] = num_requests;
+  for (int32_t r = 0; r < num_requests; ++r) {
+    const int32_t w = std::min(std::max(verify_len[r], 0), block);
+    const int32_t L = std::min(std::max(accept_len[r], 0), w);
+    const bool trimmed = w < block;
+    if (trimmed) stats[1] += 1;
+    if (trimmed && L == w) stats[2] += 1;
+    stats[3] += L;
+    stats[4] += w;
+    for (int32_t j = 0; j < block; ++j) {
+      if (w > j) stats[5 + j] += 1;
+      if (L > j) stats[5 + block + j] += 1;
+    }
+  }
+  return 0;
+}
+
 int32_t svref_sample_probs(const float* probs, int64_t ld_probs, int32_t num_rows, int32_t vocab,
                            const int32_t* qo_indptr, int32_t num_requests,
                            const uint32_t* request_id, const uint32_t* position0, uint64_t seed,

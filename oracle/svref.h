@@ -109,6 +109,20 @@ int32_t svref_plan_windows(const float* confidence, int64_t ld_conf, int32_t num
 int32_t svref_accept_prefix(const uint8_t* accepted, const int32_t* qo_indptr,
                             int32_t num_requests, const int32_t* verify_cap, int32_t* accept_len);
 
+/* Acceptance and trim statistics of one verify step (TensorRT-LLM PR #17056,
+ * commit note on the trim-regret metric: a trimmed request that accepted its
+ * whole window lost acceptance to the cut; the consolidation study, section 1:
+ * per-position acceptance is the share of drafts whose first j+1 tokens
+ * survived).  Request r verified w_r = verify_len[r] of the block's B drafted
+ * positions and accepted L_r = accept_len[r]; w_r is clamped to [0, B] and L_r
+ * to [0, w_r].  stats (int64):
+ *   [0] requests, [1] trimmed (w_r < B), [2] regret (trimmed and L_r == w_r),
+ *   [3] sum L_r, [4] sum w_r,
+ *   [5 + j] offered at position j = #{r : w_r > j},
+ *   [5 + B + j] accepted at position j = #{r : L_r > j},   j < B. */
+int32_t svref_acceptance_stats(const int32_t* accept_len, const int32_t* verify_len,
+                               int32_t num_requests, int32_t block, int64_t* stats);
+
 /* Harness helper: one exponential-race sample per row from dense fp32
  * probability rows, keyed (seed, request id, position0 + j, tag). */
 int32_t svref_sample_probs(const float* probs, int64_t ld_probs, int32_t num_rows, int32_t vocab,

@@ -76,6 +76,8 @@ def lib():
         L.svref_plan_windows.restype = i32
         L.svref_accept_prefix.argtypes = [P, P, i32, P, P]
         L.svref_accept_prefix.restype = i32
+        L.svref_acceptance_stats.argtypes = [P, P, i32, i32, P]
+        L.svref_acceptance_stats.restype = i32
         L.svref_sample_probs.argtypes = [P, i64, i32, i32, P, i32, P, P, u64, u32, P]
         L.svref_sample_probs.restype = i32
         _lib = L
@@ -193,6 +195,18 @@ def plan_windows(conf, budget):
     if rc != 0:
         raise ValueError(f"svref_plan_windows returned {rc}")
     return vl, qo, surv
+
+
+def acceptance_stats(accept_len, verify_len, block):
+    """Acceptance and trim statistics (svref_acceptance_stats): int64 array
+    [requests, trimmed, regret, sum accepted, sum window, offered[B], accepted[B]]."""
+    L = _c(accept_len, np.int32)
+    w = _c(verify_len, np.int32)
+    out = np.zeros(5 + 2 * int(block), np.int64)
+    rc = lib().svref_acceptance_stats(_p(L), _p(w), int(L.size), int(block), _p(out))
+    if rc != 0:
+        raise ValueError(f"svref_acceptance_stats returned {rc}")
+    return out
 
 
 def accept_prefix(accepted, qo, verify_cap=None):

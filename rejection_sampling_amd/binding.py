@@ -24,13 +24,13 @@ LIST_CAP = 4096  # kept-set entries a row can list (top-k bound of SV_LIST_BOUND
 TOPK_SINGLE_PASS = 256  # largest top-k the streaming pass selects by itself
 ROW_ACCEPT, ROW_SAMPLED, ROW_RESID_EMPTY = 1, 2, 32
 KERNEL_IDS = {"row_pass": 0, "finalize": 1, "build_out": 2, "planner": 3, "accept_prefix": 4,
-              "race_segment": 5, "race_finish": 6}
+              "race_segment": 5, "race_finish": 6, "acceptance_stats": 7}
 
 EXPORTS = [
     "spec_verify_workspace_bytes", "spec_verify_build_target_probs",
     "spec_verify_rejection_sample", "spec_verify_plan_windows", "spec_verify_accept_prefix",
     "spec_verify_status_string", "spec_verify_last_error", "spec_verify_profile_enable",
-    "spec_verify_profile_read", "spec_verify_profile_reset",
+    "spec_verify_profile_read", "spec_verify_profile_reset", "spec_verify_acceptance_stats",
 ]
 
 
@@ -67,6 +67,8 @@ def load(path: str = LIB_PATH):
     L.spec_verify_plan_windows.restype = i32
     L.spec_verify_accept_prefix.argtypes = [P, P, i32, P, P, P]
     L.spec_verify_accept_prefix.restype = i32
+    L.spec_verify_acceptance_stats.argtypes = [P, P, i32, i32, P, P]
+    L.spec_verify_acceptance_stats.restype = i32
     L.spec_verify_status_string.argtypes = [i32]
     L.spec_verify_status_string.restype = ctypes.c_char_p
     L.spec_verify_last_error.argtypes = []
@@ -318,6 +320,21 @@ def accept_prefix(accepted: torch.Tensor, qo_indptr: torch.Tensor,
     R = qo.numel() - 1
     out = torch.empty(R, dtype=torch.int32, device=qo.device)
     rc = load().spec_verify_accept_prefix(_ptr(acc), _ptr(qo), R, _ptr(cap), _ptr(out), _stream())
+    _check(rc)
+    return out
+
+
+def acceptance_stats(accept_len: torch.Tensor, verify_len: torch.Tensor, block: int):
+    """Acceptance and trim statistics of one verify step: an int64 device
+    tensor [requests, trimmed, regret, sum accepted, sum window, offered[B],
+    accepted[B]] (spec_verify_acceptance_stats)."""
+    L = _dev(accept_len, torch.int32, "accept_len")
+    w = _dev(verify_len, torch.int32, "verify_len")
+    if L.numel() != w.numel():
+        raise ValueError("accept_len and verify_len differ in length")
+    out = torch.empty(5 + 2 * int(block), dtype=torch.int64, device=L.device)
+    rc = load().spec_verify_acceptance_stats(_ptr(L), _ptr(w), L.numel(), int(block), _ptr(out),
+                                             _stream())
     _check(rc)
     return out
 

@@ -329,6 +329,22 @@ int32_t spec_verify_accept_prefix(const uint8_t* accepted, const int32_t* qo_ind
   return check_launch("accept prefix");
 }
 
+int32_t spec_verify_acceptance_stats(const int32_t* accept_len, const int32_t* verify_len,
+                                     int32_t num_requests, int32_t block, int64_t* stats,
+                                     sv_stream_t stream) {
+  if (num_requests < 0 || block < 0) return fail(SV_ERR_SHAPE, "negative size");
+  if (block > sv::kPlanBlock) return fail(SV_ERR_SHAPE, "block must be <= 1024");
+  if ((int64_t)num_requests * (int64_t)block >= (int64_t)1 << 31)
+    return fail(SV_ERR_SHAPE, "num_requests * block must be < 2^31");
+  if (!stats) return fail(SV_ERR_NULL, "stats is NULL");
+  if (num_requests > 0 && (!accept_len || !verify_len))
+    return fail(SV_ERR_NULL, "accept_len / verify_len are NULL");
+  hipStream_t s = (hipStream_t)stream;
+  launch(7, sv::acceptance_stats_kernel, dim3(1), dim3(sv::kPlanBlock), s, accept_len, verify_len,
+         num_requests, block, stats);
+  return check_launch("acceptance statistics");
+}
+
 int32_t spec_verify_profile_enable(int32_t on) {
   Prof& p = prof();
   std::lock_guard<std::mutex> g(p.mu);

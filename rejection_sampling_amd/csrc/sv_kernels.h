@@ -86,6 +86,8 @@ __global__ void build_out_kernel(VerifyArgs A, BuildOutArgs B);
 __global__ void plan_kernel(PlanArgs A);
 __global__ void accept_prefix_kernel(const uint8_t* accepted, const int32_t* qo, int32_t R,
                                      const int32_t* verify_cap, int32_t* accept_len);
+__global__ void acceptance_stats_kernel(const int32_t* accept_len, const int32_t* verify_len,
+                                        int32_t R, int32_t B, int64_t* stats);
 
 // sizes shared with the host
 constexpr int kRowBlock = SV_BLOCK;

@@ -145,4 +145,61 @@ __global__ __launch_bounds__(256) void accept_prefix_kernel(const uint8_t* accep
   if (lane_id() == 0) accept_len[r] = L;
 }
 
+// Acceptance and trim statistics of one verify step (TensorRT-LLM PR #17056,
+// commit note on the trim-regret metric; per-position acceptance as in the
+// consolidation study, section 1).  One workgroup: each thread counts its
+// requests (trimmed: window below the block; regret: trimmed with the whole
+// window accepted) and bins their windows and accepted lengths in LDS; the
+// per-position counts are suffix sums of those bins (positions j < w are
+// offered, j < L accepted).  Integer counts only, so the result is exact.
+__global__ __launch_bounds__(kPlanBlock) void acceptance_stats_kernel(
+    const int32_t* accept_len, const int32_t* verify_len, int32_t R, int32_t B, int64_t* stats) {
+  __shared__ uint32_t hw[kPB + 1], hl[kPB + 1];  // bins 0..B of windows and accepted lengths
+  __shared__ uint32_t tot[4];
+  const int tid = threadIdx.x;
+  for (int v = tid; v <= B; v += kPB) { hw[v] = 0u; hl[v] = 0u; }
+  if (tid < 4) tot[tid] = 0u;
+  __syncthreads();
+  uint32_t trimmed = 0u, regret = 0u, sum_l = 0u, sum_w = 0u;
+  for (int r = tid; r < R; r += kPB) {
+    int w = verify_len[r];
+    w = w < 0 ? 0 : (w > B ? B : w);
+    int L = accept_len[r];
+    L = L < 0 ? 0 : (L > w ? w : L);
+    if (w < B) {
+      trimmed += 1u;
+      if (L == w) regret += 1u;
+    }
+    sum_l += (uint32_t)L;
+    sum_w += (uint32_t)w;
+    atomicAdd(&hw[w], 1u);
+    atomicAdd(&hl[L], 1u);
+  }
+  atomicAdd(&tot[0], trimmed);
+  atomicAdd(&tot[1], regret);
+  atomicAdd(&tot[2], sum_l);
+  atomicAdd(&tot[3], sum_w);
+  __syncthreads();
+  // suffix sums over bins 1..B in place: after them hw[v] = #{w >= v}
+  for (int d = 1; d < B; d <<= 1) {
+    uint32_t a = 0u, b = 0u;
+    const int v = tid + 1;
+    if (v <= B && v + d <= B) { a = hw[v + d]; b = hl[v + d]; }
+    __syncthreads();
+    if (v <= B) { hw[v] += a; hl[v] += b; }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    stats[0] = R;
+    stats[1] = tot[0];
+    stats[2] = tot[1];
+    stats[3] = tot[2];
+    stats[4] = tot[3];
+  }
+  for (int j = tid; j < B; j += kPB) {
+    stats[5 + j] = hw[j + 1];      // offered: w > j
+    stats[5 + B + j] = hl[j + 1];  // accepted: L > j
+  }
+}
+
 }  // namespace sv

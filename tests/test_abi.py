@@ -91,6 +91,12 @@ def test_host_validation_without_gpu(lib):
     assert rc == -2
     # empty batches are no-ops
     assert lib.spec_verify_accept_prefix(None, None, 0, None, None, None) == 0
+    # acceptance statistics: block above 1024, NULL stats, NULL inputs
+    lib.spec_verify_acceptance_stats.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                                 ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    assert lib.spec_verify_acceptance_stats(fake, fake, 4, 1025, fake, None) == -2
+    assert lib.spec_verify_acceptance_stats(fake, fake, 4, 16, None, None) == -1
+    assert lib.spec_verify_acceptance_stats(None, fake, 4, 16, fake, None) == -1
 
 
 def test_workspace_query_grows_with_rows(lib):

@@ -360,7 +360,14 @@ def test_workload5_planner_and_verify():
     assert np.array_equal(surv_g.cpu().numpy().view(np.uint32), surv.view(np.uint32))
     assert qo[-1] == w.num_rows
     sample = np.random.default_rng(5).choice(w.num_requests, 24, replace=False)
-    _big(w, qo, sample, "workload 5 ragged 1792 rows V=248320")
+    gpu, _, _ = _big(w, qo, sample, "workload 5 ragged 1792 rows V=248320")
+    # the step's acceptance and trim statistics over the planner's windows
+    Bk = w.confidence.shape[1]
+    st_g = B.acceptance_stats(dev_i32(gpu["accept_len"]), vl_g, Bk).cpu().numpy()
+    st = svref.acceptance_stats(gpu["accept_len"], vl, Bk)
+    assert np.array_equal(st_g, st)
+    progress(f"workload 5 statistics: trimmed {st[1]}/{st[0]}, regret {st[2]}, "
+             f"acceptance per verified token {st[3] / max(st[4], 1):.3f}")
 
 
 # -------------------------------------------------------------- planner
@@ -382,6 +389,23 @@ def test_planner_matches_oracle(R, Bk):
     vl_g, qo_g, _ = B.plan_windows(dev_f32(conf), (R * Bk) // 2 + 1)
     vl, qo, _ = svref.plan_windows(conf, (R * Bk) // 2 + 1)
     assert np.array_equal(vl_g.cpu().numpy(), vl)
+
+
+@pytest.mark.parametrize("R,Bk", [(0, 5), (1, 0), (3, 1), (256, 16), (5000, 7), (300, 1024)])
+def test_acceptance_stats_match_oracle(R, Bk):
+    """Acceptance and trim statistics bit-exact against the oracle, with
+    out-of-range device values (clamped alike on both sides)."""
+    from rejection_sampling_amd import binding as B
+    g = np.random.default_rng(R + 7 * Bk)
+    w = g.integers(-2, Bk + 3, R).astype(np.int32)
+    L = g.integers(-2, Bk + 3, R).astype(np.int32)
+    full = g.random(R) < 0.3                      # some requests accept their whole window
+    L[full] = w[full]
+    progress(f"acceptance statistics R={R} B={Bk}")
+    st_g = B.acceptance_stats(dev_i32(L) if R else torch.empty(0, dtype=torch.int32, device="cuda"),
+                              dev_i32(w) if R else torch.empty(0, dtype=torch.int32, device="cuda"),
+                              Bk).cpu().numpy()
+    assert np.array_equal(st_g, svref.acceptance_stats(L, w, Bk))
 
 
 def test_accept_prefix_matches_oracle():

@@ -48,6 +48,12 @@ CASES = [
     ("bonus row not counted in qo_indptr", "qo_indptr[r] + verify_len[r] + 1;",
      "qo_indptr[r] + verify_len[r];",
      ["test_oracle_planner.py::test_rank_allocation_matches_counting"]),
+    ("trim regret counts a request one short of its window", "if (trimmed && L == w) stats[2] += 1;",
+     "if (trimmed && L + 1 >= w) stats[2] += 1;",
+     ["test_oracle_stats.py::test_every_small_case_matches_explicit_flags"]),
+    ("per-position acceptance off by one", "if (L > j) stats[5 + block + j] += 1;",
+     "if (L >= j) stats[5 + block + j] += 1;",
+     ["test_oracle_stats.py::test_printed_section1_figures"]),
 ]
 
 
