@@ -257,7 +257,8 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the verify step "
-              "shards by request with no exchange, see DESIGN.md", file=sys.stderr)
+              "would shard by request with no exchange, which this benchmark does not run",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch

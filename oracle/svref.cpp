@@ -6,7 +6,7 @@
  * reordered beyond what the definitions below state, so each step can be read
  * against the pages.  Built with g++ -O2 -ffp-contract=off and no fast-math.
  *
- * Readings taken where the pages are silent (each one is listed in the design doc):
+ * Readings taken where the pages are silent:
  *  - logits are converted exactly to fp64; a bf16 value is its bit pattern
  *    shifted into the high half of an fp32.
  *  - ties: the order of a row is (value descending, index ascending); the
