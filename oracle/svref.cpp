@@ -496,6 +496,114 @@ int32_t svref_acceptance_stats(const int32_t* accept_len, const int32_t* verify_
   return 0;
 }
 
+// ------------------------------------------------------------ estimator
+int32_t svref_est_init(svref_estimator* est, int32_t block) {
+  if (!est || block < 1 || block > SVREF_EST_MAXB) return -1;
+  std::memset(est, 0, sizeof(*est));
+  est->block = block;
+  est->slope = 0.5;
+  for (int32_t k = 0; k < block; ++k) est->bias[k] = -0.2;
+  return 0;
+}
+
+int32_t svref_est_feature(const float* row_max, const float* row_lse, const float* t_eff,
+                          int32_t num_rows, double* x) {
+  if (num_rows < 0 || (num_rows > 0 && (!row_max || !row_lse || !t_eff || !x))) return -1;
+  for (int32_t i = 0; i < num_rows; ++i) {
+    const double T = t_eff[i] > 0.0f ? (double)t_eff[i] : 1.0;
+    const double lq = (double)row_max[i] / T - (double)row_lse[i];  // log q_max <= 0
+    // logit(q) = log q - log(1 - q)
+    double v = lq - std::log1p(-std::exp(lq));
+    if (!(v <= 40.0)) v = 40.0;  // q_max = 1 (or NaN) saturates
+    if (v < -40.0) v = -40.0;
+    x[i] = v;
+  }
+  return 0;
+}
+
+static double sigmoid(double z) { return 1.0 / (1.0 + std::exp(-z)); }
+
+int32_t svref_est_predict(const svref_estimator* est, const double* x, const int32_t* pos,
+                          int32_t n, double* p) {
+  if (!est || n < 0 || (n > 0 && (!x || !pos || !p))) return -1;
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t k = std::min(std::max(pos[i], 0), est->block - 1);
+    p[i] = sigmoid(est->slope * x[i] + est->bias[k]);
+  }
+  return 0;
+}
+
+// Newton step of the logistic log-likelihood in (slope, bias_0..bias_{B-1}).
+// The Hessian is an arrowhead: a dense slope row and column, a diagonal over
+// the intercepts (an observation touches one intercept); with the ridge on the
+// diagonal the slope direction is the Schur complement's solution and each
+// intercept's direction follows from it.
+static void est_refit(svref_estimator* e) {
+  const double ridge = 1e-3;
+  const int32_t B = e->block;
+  double a = e->h_ss + ridge, g = e->g_s;
+  for (int32_t k = 0; k < B; ++k) {
+    const double d = e->h_kk[k] + ridge;
+    a -= e->h_sk[k] * e->h_sk[k] / d;
+    g -= e->h_sk[k] * e->g_k[k] / d;
+  }
+  const double ds = g / a;
+  e->last_ds = ds;
+  // slope: damped, non-finite dropped, halved while it would turn negative
+  double step = ds * (e->n_s / (e->n_s + 50.0));
+  if (!std::isfinite(step)) step = 0.0;
+  int32_t halvings = 0;
+  while (e->slope + step < 0.0 && halvings < 8) {
+    step *= 0.5;
+    ++halvings;
+  }
+  if (e->slope + step < 0.0) step = 0.0;
+  // intercepts: their Newton step given the slope step taken, damped alike
+  for (int32_t k = 0; k < B; ++k) {
+    const double d = e->h_kk[k] + ridge;
+    const double db = (e->g_k[k] - e->h_sk[k] * step) / d;
+    e->last_db[k] = db;
+    double sb = db * (e->n_k[k] / (e->n_k[k] + 50.0));
+    if (!std::isfinite(sb)) sb = 0.0;
+    e->bias[k] += sb;
+  }
+  e->slope += step;
+  e->h_ss = e->g_s = e->n_s = 0.0;
+  for (int32_t k = 0; k < B; ++k) e->h_sk[k] = e->h_kk[k] = e->g_k[k] = e->n_k[k] = 0.0;
+  e->refits += 1;
+}
+
+int32_t svref_est_observe(svref_estimator* est, const double* x, const int32_t* accept_len,
+                          const int32_t* verify_len, int32_t num_requests) {
+  if (!est || num_requests < 0 || (num_requests > 0 && (!x || !accept_len || !verify_len)))
+    return -1;
+  const int32_t B = est->block;
+  for (int32_t r = 0; r < num_requests; ++r) {
+    const int32_t w = std::min(std::max(verify_len[r], 0), B);
+    const int32_t L = std::min(std::max(accept_len[r], 0), w);
+    const int32_t last = L < w ? L : L - 1;  // the accepted drafts, then the first rejected one
+    for (int32_t k = 0; k <= last; ++k) {
+      const double xv = x[(size_t)r * B + k];
+      const double y = k < L ? 1.0 : 0.0;
+      const double p = sigmoid(est->slope * xv + est->bias[k]);
+      const double wt = p * (1.0 - p);
+      est->h_ss += wt * xv * xv;
+      est->h_sk[k] += wt * xv;
+      est->h_kk[k] += wt;
+      est->g_s += (y - p) * xv;
+      est->g_k[k] += y - p;
+      est->n_s += 1.0;
+      est->n_k[k] += 1.0;
+    }
+  }
+  est->calls += 1;
+  if (est->calls >= SVREF_EST_REFIT) {
+    est_refit(est);
+    est->calls = 0;
+  }
+  return 0;
+}
+
 int32_t svref_sample_probs(const float* probs, int64_t ld_probs, int32_t num_rows, int32_t vocab,
                            const int32_t* qo_indptr, int32_t num_requests,
                            const uint32_t* request_id, const uint32_t* position0, uint64_t seed,

@@ -123,6 +123,51 @@ int32_t svref_accept_prefix(const uint8_t* accepted, const int32_t* qo_indptr,
 int32_t svref_acceptance_stats(const int32_t* accept_len, const int32_t* verify_len,
                                int32_t num_requests, int32_t block, int64_t* stats);
 
+/* Online acceptance estimator (SGLang PR "Adaptive verification for DFLASH",
+ * commit notes adding OnlineAcceptanceEstimator and fixing its slope refit):
+ * a logistic model p_k = sigmoid(slope * x_k + bias_k) of the acceptance of
+ * the drafted token at position k, calibrated while serving.  x_k =
+ * logit(q_max) of the temperature-scaled draft distribution at that position
+ * (greedy rows at T = 1), clamped to +-40.  One slope shared by all positions,
+ * one intercept per position, starting at 0.5 and -0.2.  observe() labels the
+ * accepted drafts 1 and the first rejected one 0 and adds them to the Newton
+ * (IRLS) statistics at the current coefficients; every SVREF_EST_REFIT calls
+ * the arrowhead Newton system is solved with a ridge, each update damped by
+ * n / (n + 50), non-finite steps dropped, a slope step that would make the
+ * slope negative halved (at most 8 times, dropped if it still crosses zero),
+ * the intercepts stepped given the slope step taken, and the statistics
+ * cleared. */
+#define SVREF_EST_MAXB 64
+#define SVREF_EST_REFIT 100
+typedef struct {
+  int32_t block;                    /* positions per request, <= SVREF_EST_MAXB */
+  int32_t calls;                    /* observe calls since the last refit       */
+  int32_t refits;                   /* refits so far                            */
+  int32_t pad;
+  double slope;
+  double bias[SVREF_EST_MAXB];
+  /* IRLS statistics since the last refit: Hessian (arrowhead), gradient, counts */
+  double h_ss, g_s, n_s;
+  double h_sk[SVREF_EST_MAXB], h_kk[SVREF_EST_MAXB], g_k[SVREF_EST_MAXB], n_k[SVREF_EST_MAXB];
+  /* the last refit's Newton direction before damping (for inspection) */
+  double last_ds, last_db[SVREF_EST_MAXB];
+} svref_estimator;
+
+int32_t svref_est_init(svref_estimator* est, int32_t block);
+/* Feature per row from the draft build's row max m and lse (at T_eff = T, or 1
+ * for greedy rows): x = logit(exp(m / T_eff - lse)), clamped to [-40, 40]. */
+int32_t svref_est_feature(const float* row_max, const float* row_lse, const float* t_eff,
+                          int32_t num_rows, double* x);
+/* p = sigmoid(slope * x + bias[k]) for the rows' positions k. */
+int32_t svref_est_predict(const svref_estimator* est, const double* x, const int32_t* pos,
+                          int32_t n, double* p);
+/* One step's observations: request r drafted positions 0..B-1 with features
+ * x[r * B + k]; it verified w_r = verify_len[r] (clamped to [0, B]) and
+ * accepted L_r = accept_len[r] (clamped to [0, w_r]).  Positions k < L_r are
+ * labelled 1 and k = L_r < w_r is labelled 0. */
+int32_t svref_est_observe(svref_estimator* est, const double* x, const int32_t* accept_len,
+                          const int32_t* verify_len, int32_t num_requests);
+
 /* Harness helper: one exponential-race sample per row from dense fp32
  * probability rows, keyed (seed, request id, position0 + j, tag). */
 int32_t svref_sample_probs(const float* probs, int64_t ld_probs, int32_t num_rows, int32_t vocab,

@@ -78,6 +78,14 @@ def lib():
         L.svref_accept_prefix.restype = i32
         L.svref_acceptance_stats.argtypes = [P, P, i32, i32, P]
         L.svref_acceptance_stats.restype = i32
+        L.svref_est_init.argtypes = [P, i32]
+        L.svref_est_init.restype = i32
+        L.svref_est_feature.argtypes = [P, P, P, i32, P]
+        L.svref_est_feature.restype = i32
+        L.svref_est_predict.argtypes = [P, P, P, i32, P]
+        L.svref_est_predict.restype = i32
+        L.svref_est_observe.argtypes = [P, P, P, P, i32]
+        L.svref_est_observe.restype = i32
         L.svref_sample_probs.argtypes = [P, i64, i32, i32, P, i32, P, P, u64, u32, P]
         L.svref_sample_probs.restype = i32
         _lib = L
@@ -206,6 +214,67 @@ def acceptance_stats(accept_len, verify_len, block):
     rc = lib().svref_acceptance_stats(_p(L), _p(w), int(L.size), int(block), _p(out))
     if rc != 0:
         raise ValueError(f"svref_acceptance_stats returned {rc}")
+    return out
+
+
+EST_MAXB = 64
+EST_REFIT = 100
+
+
+class EstimatorState(ctypes.Structure):
+    """Mirror of svref_estimator (oracle/svref.h)."""
+    _fields_ = [("block", ctypes.c_int32), ("calls", ctypes.c_int32),
+                ("refits", ctypes.c_int32), ("pad", ctypes.c_int32),
+                ("slope", ctypes.c_double), ("bias", ctypes.c_double * EST_MAXB),
+                ("h_ss", ctypes.c_double), ("g_s", ctypes.c_double), ("n_s", ctypes.c_double),
+                ("h_sk", ctypes.c_double * EST_MAXB), ("h_kk", ctypes.c_double * EST_MAXB),
+                ("g_k", ctypes.c_double * EST_MAXB), ("n_k", ctypes.c_double * EST_MAXB),
+                ("last_ds", ctypes.c_double), ("last_db", ctypes.c_double * EST_MAXB)]
+
+
+class Estimator:
+    """The oracle's online acceptance estimator (svref_est_*)."""
+
+    def __init__(self, block: int):
+        self.st = EstimatorState()
+        if lib().svref_est_init(ctypes.byref(self.st), int(block)) != 0:
+            raise ValueError("bad block")
+        self.block = int(block)
+
+    @property
+    def slope(self) -> float:
+        return self.st.slope
+
+    @property
+    def bias(self) -> np.ndarray:
+        return np.array(self.st.bias[: self.block])
+
+    def predict(self, x, pos):
+        x = _c(x, np.float64)
+        pos = _c(pos, np.int32)
+        out = np.zeros(x.size, np.float64)
+        rc = lib().svref_est_predict(ctypes.byref(self.st), _p(x), _p(pos), int(x.size), _p(out))
+        if rc != 0:
+            raise ValueError(f"svref_est_predict returned {rc}")
+        return out
+
+    def observe(self, x, accept_len, verify_len):
+        x = _c(x, np.float64)
+        L = _c(accept_len, np.int32)
+        w = _c(verify_len, np.int32)
+        rc = lib().svref_est_observe(ctypes.byref(self.st), _p(x), _p(L), _p(w), int(L.size))
+        if rc != 0:
+            raise ValueError(f"svref_est_observe returned {rc}")
+
+
+def est_feature(row_max, row_lse, t_eff):
+    m = _c(row_max, np.float32)
+    lse = _c(row_lse, np.float32)
+    t = _c(t_eff, np.float32)
+    out = np.zeros(m.size, np.float64)
+    rc = lib().svref_est_feature(_p(m), _p(lse), _p(t), int(m.size), _p(out))
+    if rc != 0:
+        raise ValueError(f"svref_est_feature returned {rc}")
     return out
 
 

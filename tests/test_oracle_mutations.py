@@ -54,6 +54,15 @@ CASES = [
     ("per-position acceptance off by one", "if (L > j) stats[5 + block + j] += 1;",
      "if (L >= j) stats[5 + block + j] += 1;",
      ["test_oracle_stats.py::test_printed_section1_figures"]),
+    ("estimator labels the first rejected draft accepted", "const double y = k < L ? 1.0 : 0.0;",
+     "const double y = 1.0;",
+     ["test_oracle_estimator.py::test_recovers_the_generating_coefficients"]),
+    ("estimator Schur complement with the wrong sign", "a -= e->h_sk[k] * e->h_sk[k] / d;",
+     "a += e->h_sk[k] * e->h_sk[k] / d;",
+     ["test_oracle_estimator.py::test_newton_direction_matches_dense_solve"]),
+    ("estimator drops a slope step instead of halving it",
+     "while (e->slope + step < 0.0 && halvings < 8) {", "while (false) {",
+     ["test_oracle_estimator.py::test_halving_keeps_the_slope_non_negative"]),
 ]
 
 
