@@ -340,6 +340,22 @@ def main():
         extra["trimmed"] = s_[1]
         extra["trim_regret_rate"] = round(s_[2] / max(s_[1], 1), 4)
         extra["acceptance_per_verified_token"] = round(s_[3] / max(s_[4], 1), 4)
+        # the online acceptance estimator per step: predict from the draft
+        # rows' max and lse, then observe the step's outcome
+        est = B.AcceptanceEstimator(nb)
+        g2 = torch.Generator(device="cuda")
+        g2.manual_seed(SEED + 99)
+        dmax = torch.randn(R * nb, generator=g2, device="cuda") * 4 + 14
+        dlse = dmax + torch.rand(R * nb, generator=g2, device="cuda") * 3
+        feat, _ = est.predict(dmax, dlse, params.T)
+        est.observe(feat, out["accept_len"], windows)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(20):
+            feat, _ = est.predict(dmax, dlse, params.T)
+            est.observe(feat, out["accept_len"], windows)
+        torch.cuda.synchronize()
+        extra["estimator_us"] = round((time.perf_counter() - t0) / 20 * 1e6, 2)
 
     cpu = cpu_baseline(args.cpu_requests) if (args.cpu_requests > 0 and wl == "c3") else None
     config = {"workload": f"{wl}: {R} requests, {rows} rows x {V} vocab; {desc}",

@@ -189,6 +189,43 @@ int32_t spec_verify_acceptance_stats(const int32_t* accept_len, const int32_t* v
                                      int32_t num_requests, int32_t block, int64_t* stats,
                                      sv_stream_t stream);
 
+/* Online acceptance estimator (SGLang PR "Adaptive verification for DFLASH
+ * ... built on upstream DSpark", commit notes adding OnlineAcceptanceEstimator
+ * and fixing its slope refit): the planner's confidence source for drafts
+ * without a trained confidence head.  p_k = sigmoid(slope * x_k + bias_k),
+ * x_k = logit(q_max) of the temperature-scaled draft distribution at position
+ * k (T = 1 for greedy requests), clamped to +-40; one slope, one intercept per
+ * position, starting at 0.5 and -0.2.
+ *   state: device doubles, spec_verify_estimator_state_doubles(block) of them,
+ *   caller-owned, written by spec_verify_estimator_init; it holds the
+ *   coefficients, the IRLS statistics since the last refit and the refit
+ *   counter, so no call synchronizes with the host.  Calls on one state must
+ *   be ordered (one stream).  block (drafted positions per request) in [1, 64].
+ * predict: the draft rows of request r are rows r * block + k of the draft
+ *   build's row_max / row_lse (spec_verify_build_target_probs on the draft
+ *   logits); temperature [R] or NULL (greedy).  Writes feature [R, block]
+ *   fp64 (or NULL) and confidence [R, block] fp32 (or NULL), the planner's
+ *   input.
+ * observe: after verification, labels positions k < L_r accepted and k = L_r
+ *   rejected when L_r < w_r (w_r = verify_len[r] clamped to [0, block], L_r =
+ *   accept_len[r] clamped to [0, w_r]), adds them to the Newton statistics at
+ *   the current coefficients; every 100th call solves the arrowhead Newton
+ *   system with ridge 1e-3, damps each update by n / (n + 50) (n: the labels
+ *   behind that coefficient), drops non-finite steps, halves a slope step that
+ *   would make the slope negative (at most 8 times, dropped if it still
+ *   does), steps the intercepts given the slope step taken, and clears the
+ *   statistics.  One workgroup in a fixed order: the same inputs give the
+ *   same coefficients. */
+size_t spec_verify_estimator_state_doubles(int32_t block);
+int32_t spec_verify_estimator_init(double* state, int32_t block, sv_stream_t stream);
+int32_t spec_verify_estimator_predict(const float* row_max, const float* row_lse,
+                                      const float* temperature, int32_t num_requests,
+                                      int32_t block, const double* state, double* feature,
+                                      float* confidence, sv_stream_t stream);
+int32_t spec_verify_estimator_observe(const double* feature, const int32_t* accept_len,
+                                      const int32_t* verify_len, int32_t num_requests,
+                                      int32_t block, double* state, sv_stream_t stream);
+
 /* Diagnostics. */
 const char* spec_verify_status_string(int32_t code);
 const char* spec_verify_last_error(void);
@@ -199,7 +236,7 @@ const char* spec_verify_last_error(void);
  * read() waits for them and returns, per kernel id, the launch count and the
  * summed milliseconds since the last reset.  Kernel ids: 0 row pass, 1 request
  * finalize, 2 target-probs writer, 3 planner, 4 accept prefix, 5 race
- * segments, 6 race finish, 7 acceptance statistics. */
+ * segments, 6 race finish, 7 acceptance statistics and estimator. */
 int32_t spec_verify_profile_enable(int32_t on);
 int32_t spec_verify_profile_read(int32_t kernel_id, int64_t* launches, double* total_ms);
 int32_t spec_verify_profile_reset(void);

@@ -31,6 +31,8 @@ EXPORTS = [
     "spec_verify_rejection_sample", "spec_verify_plan_windows", "spec_verify_accept_prefix",
     "spec_verify_status_string", "spec_verify_last_error", "spec_verify_profile_enable",
     "spec_verify_profile_read", "spec_verify_profile_reset", "spec_verify_acceptance_stats",
+    "spec_verify_estimator_state_doubles", "spec_verify_estimator_init",
+    "spec_verify_estimator_predict", "spec_verify_estimator_observe",
 ]
 
 
@@ -69,6 +71,14 @@ def load(path: str = LIB_PATH):
     L.spec_verify_accept_prefix.restype = i32
     L.spec_verify_acceptance_stats.argtypes = [P, P, i32, i32, P, P]
     L.spec_verify_acceptance_stats.restype = i32
+    L.spec_verify_estimator_state_doubles.argtypes = [i32]
+    L.spec_verify_estimator_state_doubles.restype = sz
+    L.spec_verify_estimator_init.argtypes = [P, i32, P]
+    L.spec_verify_estimator_init.restype = i32
+    L.spec_verify_estimator_predict.argtypes = [P, P, P, i32, i32, P, P, P, P]
+    L.spec_verify_estimator_predict.restype = i32
+    L.spec_verify_estimator_observe.argtypes = [P, P, P, i32, i32, P, P]
+    L.spec_verify_estimator_observe.restype = i32
     L.spec_verify_status_string.argtypes = [i32]
     L.spec_verify_status_string.restype = ctypes.c_char_p
     L.spec_verify_last_error.argtypes = []
@@ -337,6 +347,51 @@ def acceptance_stats(accept_len: torch.Tensor, verify_len: torch.Tensor, block: 
                                              _stream())
     _check(rc)
     return out
+
+
+class AcceptanceEstimator:
+    """The online acceptance estimator on the device: a state tensor of
+    doubles, initialised on construction; predict() gives the planner's
+    confidences from the draft build's row max and lse, observe() feeds a
+    verified step back (spec_verify_estimator_*)."""
+
+    def __init__(self, block: int, device=None):
+        self.block = int(block)
+        n = int(load().spec_verify_estimator_state_doubles(self.block))
+        if n == 0:
+            raise ValueError("block must be in [1, 64]")
+        self.state = torch.empty(n, dtype=torch.float64, device=device or "cuda")
+        _check(load().spec_verify_estimator_init(_ptr(self.state), self.block, _stream()))
+
+    def predict(self, row_max: torch.Tensor, row_lse: torch.Tensor,
+                temperature: Optional[torch.Tensor] = None):
+        m = _dev(row_max, torch.float32, "row_max")
+        lse = _dev(row_lse, torch.float32, "row_lse")
+        T = _dev(temperature, torch.float32, "temperature")
+        if m.numel() % self.block or lse.numel() != m.numel():
+            raise ValueError("row_max / row_lse must hold num_requests * block rows")
+        R = m.numel() // self.block
+        feat = torch.empty((R, self.block), dtype=torch.float64, device=m.device)
+        conf = torch.empty((R, self.block), dtype=torch.float32, device=m.device)
+        _check(load().spec_verify_estimator_predict(_ptr(m), _ptr(lse), _ptr(T), R, self.block,
+                                                    _ptr(self.state), _ptr(feat), _ptr(conf),
+                                                    _stream()))
+        return feat, conf
+
+    def observe(self, feature: torch.Tensor, accept_len: torch.Tensor, verify_len: torch.Tensor):
+        f = _dev(feature, torch.float64, "feature")
+        L = _dev(accept_len, torch.int32, "accept_len")
+        w = _dev(verify_len, torch.int32, "verify_len")
+        if L.numel() != w.numel() or f.numel() != L.numel() * self.block:
+            raise ValueError("feature must be [num_requests, block]")
+        _check(load().spec_verify_estimator_observe(_ptr(f), _ptr(L), _ptr(w), L.numel(),
+                                                    self.block, _ptr(self.state), _stream()))
+
+    def coefficients(self):
+        """(slope, intercepts, refits) read back to the host (synchronizes)."""
+        st = self.state.cpu().numpy()
+        B = self.block
+        return float(st[0]), st[1:1 + B].copy(), int(st[5 + 5 * B])
 
 
 def profile_enable(on: bool = True):

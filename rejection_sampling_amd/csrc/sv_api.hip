@@ -345,6 +345,59 @@ int32_t spec_verify_acceptance_stats(const int32_t* accept_len, const int32_t* v
   return check_launch("acceptance statistics");
 }
 
+size_t spec_verify_estimator_state_doubles(int32_t block) {
+  return block < 1 ? 0 : (size_t)sv::kEstStateBase + 5 * (size_t)block;
+}
+
+static int32_t check_est_block(int32_t block) {
+  if (block < 1 || block > sv::kEstMaxBlock) return fail(SV_ERR_SHAPE, "block must be in [1, 64]");
+  return SV_OK;
+}
+
+int32_t spec_verify_estimator_init(double* state, int32_t block, sv_stream_t stream) {
+  int32_t rc = check_est_block(block);
+  if (rc) return rc;
+  if (!state) return fail(SV_ERR_NULL, "state is NULL");
+  launch(7, sv::est_init_kernel, dim3(1), dim3(64), (hipStream_t)stream, state, block);
+  return check_launch("estimator init");
+}
+
+int32_t spec_verify_estimator_predict(const float* row_max, const float* row_lse,
+                                      const float* temperature, int32_t num_requests,
+                                      int32_t block, const double* state, double* feature,
+                                      float* confidence, sv_stream_t stream) {
+  int32_t rc = check_est_block(block);
+  if (rc) return rc;
+  if (num_requests < 0) return fail(SV_ERR_SHAPE, "negative request count");
+  if ((int64_t)num_requests * (int64_t)block >= (int64_t)1 << 31)
+    return fail(SV_ERR_SHAPE, "num_requests * block must be < 2^31");
+  if (!state) return fail(SV_ERR_NULL, "state is NULL");
+  if (num_requests == 0) return SV_OK;
+  if (!row_max || !row_lse) return fail(SV_ERR_NULL, "row_max / row_lse are NULL");
+  const int64_t n = (int64_t)num_requests * block;
+  const int64_t grid = (n + 255) / 256;
+  launch(7, sv::est_predict_kernel, dim3((unsigned)(grid < 4096 ? grid : 4096)), dim3(256),
+         (hipStream_t)stream, row_max, row_lse, temperature, num_requests, block, state, feature,
+         confidence);
+  return check_launch("estimator predict");
+}
+
+int32_t spec_verify_estimator_observe(const double* feature, const int32_t* accept_len,
+                                      const int32_t* verify_len, int32_t num_requests,
+                                      int32_t block, double* state, sv_stream_t stream) {
+  int32_t rc = check_est_block(block);
+  if (rc) return rc;
+  if (num_requests < 0) return fail(SV_ERR_SHAPE, "negative request count");
+  if ((int64_t)num_requests * (int64_t)block >= (int64_t)1 << 31)
+    return fail(SV_ERR_SHAPE, "num_requests * block must be < 2^31");
+  if (!state) return fail(SV_ERR_NULL, "state is NULL");
+  if (num_requests > 0 && (!feature || !accept_len || !verify_len))
+    return fail(SV_ERR_NULL, "feature / accept_len / verify_len are NULL");
+  launch(7, sv::est_observe_kernel, dim3(1), dim3(sv::kPlanBlock), (hipStream_t)stream, feature,
+         accept_len, verify_len, num_requests, block, state);
+  return check_launch("estimator observe");
+}
+
 int32_t spec_verify_profile_enable(int32_t on) {
   Prof& p = prof();
   std::lock_guard<std::mutex> g(p.mu);

@@ -88,12 +88,21 @@ __global__ void accept_prefix_kernel(const uint8_t* accepted, const int32_t* qo,
                                      const int32_t* verify_cap, int32_t* accept_len);
 __global__ void acceptance_stats_kernel(const int32_t* accept_len, const int32_t* verify_len,
                                         int32_t R, int32_t B, int64_t* stats);
+__global__ void est_init_kernel(double* st, int32_t B);
+__global__ void est_predict_kernel(const float* row_max, const float* row_lse,
+                                   const float* temperature, int32_t R, int32_t B,
+                                   const double* st, double* feature, float* confidence);
+__global__ void est_observe_kernel(const double* feature, const int32_t* accept_len,
+                                   const int32_t* verify_len, int32_t R, int32_t B, double* st);
 
 // sizes shared with the host
 constexpr int kRowBlock = SV_BLOCK;
 constexpr int kRowPassPerCU = 4;     // row-pass workgroups resident per CU (LDS and VGPR bound)
 constexpr int kPlanBlock = 1024;
 constexpr size_t kRowRecBytes = 64;
+constexpr int kEstMaxBlock = 64;     // estimator positions per request
+constexpr int kEstRefit = 100;       // estimator observe calls per refit
+constexpr int kEstStateBase = 6;     // estimator state doubles: 6 + 5 * block
 constexpr int kRaceSegElems = 4096;  // vocabulary elements per race segment
 constexpr int kMaxRaceSegs = 64;
 constexpr int kRaceGrid = 768;      // race-segment workgroups (three per CU resident)

@@ -202,4 +202,155 @@ __global__ __launch_bounds__(kPlanBlock) void acceptance_stats_kernel(
   }
 }
 
+// ------------------------------------------------------------ estimator
+// Online acceptance estimator (SGLang PR "Adaptive verification for DFLASH",
+// commit notes adding OnlineAcceptanceEstimator and fixing its slope refit):
+// p_k = sigmoid(slope * x_k + bias_k), x_k = logit(q_max) of the draft
+// distribution at position k.  The state is one device array of doubles (see
+// EstLayout); a single workgroup applies every update in a fixed order, so
+// the same inputs always give the same coefficients, and the refit counter
+// lives in the state, so nothing waits on the host.
+struct EstLayout {
+  int B;
+  __device__ __forceinline__ explicit EstLayout(int b) : B(b) {}
+  __device__ __forceinline__ int slope() const { return 0; }
+  __device__ __forceinline__ int bias(int k) const { return 1 + k; }
+  __device__ __forceinline__ int h_ss() const { return 1 + B; }
+  __device__ __forceinline__ int g_s() const { return 2 + B; }
+  __device__ __forceinline__ int n_s() const { return 3 + B; }
+  __device__ __forceinline__ int h_sk(int k) const { return 4 + B + k; }
+  __device__ __forceinline__ int h_kk(int k) const { return 4 + 2 * B + k; }
+  __device__ __forceinline__ int g_k(int k) const { return 4 + 3 * B + k; }
+  __device__ __forceinline__ int n_k(int k) const { return 4 + 4 * B + k; }
+  __device__ __forceinline__ int calls() const { return 4 + 5 * B; }
+  __device__ __forceinline__ int refits() const { return 5 + 5 * B; }
+};
+
+__device__ __forceinline__ double est_sigmoid(double z) { return 1.0 / (1.0 + exp(-z)); }
+
+__global__ void est_init_kernel(double* st, int32_t B) {
+  const EstLayout L(B);
+  for (int t = threadIdx.x; t < kEstStateBase + 5 * B; t += blockDim.x) st[t] = 0.0;
+  __syncthreads();
+  if (threadIdx.x == 0) st[L.slope()] = 0.5;
+  for (int k = threadIdx.x; k < B; k += blockDim.x) st[L.bias(k)] = -0.2;
+}
+
+// Feature and prediction of every drafted position (row r * B + k of the
+// draft build): x = logit(exp(m / T - lse)) clamped to [-40, 40], with T = 1
+// for greedy requests; confidence = sigmoid(slope * x + bias_k) in fp32, the
+// planner's input.
+__global__ void est_predict_kernel(const float* row_max, const float* row_lse,
+                                   const float* temperature, int32_t R, int32_t B,
+                                   const double* st, double* feature, float* confidence) {
+  const EstLayout L(B);
+  const long long n = (long long)R * B;
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (long long)gridDim.x * blockDim.x) {
+    const int r = (int)(i / B), k = (int)(i - (long long)r * B);
+    const float t = temperature ? temperature[r] : 0.0f;
+    const double T = t > 0.0f ? (double)t : 1.0;
+    const double lq = (double)row_max[i] / T - (double)row_lse[i];
+    double x = lq - log1p(-exp(lq));
+    if (!(x <= 40.0)) x = 40.0;
+    if (x < -40.0) x = -40.0;
+    if (feature) feature[i] = x;
+    if (confidence) confidence[i] = (float)est_sigmoid(st[L.slope()] * x + st[L.bias(k)]);
+  }
+}
+
+// One step's observations (labels 1 for the accepted drafts, 0 for the first
+// rejected one) added to the IRLS statistics at the current coefficients;
+// every kEstRefit calls the refit.  One workgroup: per position, each wave
+// sums its lanes by a DPP scan and the waves' sums are added in wave order.
+__global__ __launch_bounds__(kPlanBlock) void est_observe_kernel(
+    const double* feature, const int32_t* accept_len, const int32_t* verify_len, int32_t R,
+    int32_t B, double* st) {
+  const EstLayout L(B);
+  __shared__ double part[kPW][4];
+  __shared__ double tot[kPW][3];
+  const int tid = threadIdx.x, w = wave_id(), l = lane_id();
+  const double slope = st[L.slope()];
+  double h_ss = 0.0, g_s = 0.0, n_s = 0.0;
+  for (int k = 0; k < B; ++k) {
+    const double bk = st[L.bias(k)];
+    double hsk = 0.0, hkk = 0.0, gk = 0.0, nk = 0.0;
+    for (int r = tid; r < R; r += kPB) {
+      int wr = verify_len[r];
+      wr = wr < 0 ? 0 : (wr > B ? B : wr);
+      int lr = accept_len[r];
+      lr = lr < 0 ? 0 : (lr > wr ? wr : lr);
+      const int last = lr < wr ? lr : lr - 1;
+      if (k > last) continue;
+      const double x = feature[(size_t)r * B + k];
+      const double y = k < lr ? 1.0 : 0.0;
+      const double p = est_sigmoid(slope * x + bk);
+      const double wt = p * (1.0 - p);
+      h_ss += wt * x * x;
+      hsk += wt * x;
+      hkk += wt;
+      g_s += (y - p) * x;
+      gk += y - p;
+      n_s += 1.0;
+      nk += 1.0;
+    }
+    hsk = readlane_d(wave_scan_dpp(hsk), 63);
+    hkk = readlane_d(wave_scan_dpp(hkk), 63);
+    gk = readlane_d(wave_scan_dpp(gk), 63);
+    nk = readlane_d(wave_scan_dpp(nk), 63);
+    if (l == 0) { part[w][0] = hsk; part[w][1] = hkk; part[w][2] = gk; part[w][3] = nk; }
+    __syncthreads();
+    if (tid == 0) {
+      double a = 0.0, b = 0.0, c = 0.0, d = 0.0;
+      for (int q = 0; q < kPW; ++q) { a += part[q][0]; b += part[q][1]; c += part[q][2]; d += part[q][3]; }
+      st[L.h_sk(k)] += a;
+      st[L.h_kk(k)] += b;
+      st[L.g_k(k)] += c;
+      st[L.n_k(k)] += d;
+    }
+    __syncthreads();
+  }
+  h_ss = readlane_d(wave_scan_dpp(h_ss), 63);
+  g_s = readlane_d(wave_scan_dpp(g_s), 63);
+  n_s = readlane_d(wave_scan_dpp(n_s), 63);
+  if (l == 0) { tot[w][0] = h_ss; tot[w][1] = g_s; tot[w][2] = n_s; }
+  __syncthreads();
+  if (tid != 0) return;
+  {
+    double a = 0.0, b = 0.0, c = 0.0;
+    for (int q = 0; q < kPW; ++q) { a += tot[q][0]; b += tot[q][1]; c += tot[q][2]; }
+    st[L.h_ss()] += a;
+    st[L.g_s()] += b;
+    st[L.n_s()] += c;
+  }
+  st[L.calls()] += 1.0;
+  if (st[L.calls()] < (double)kEstRefit) return;
+  // refit: arrowhead Newton solve with a ridge (Schur complement on the slope)
+  const double ridge = 1e-3;
+  double a = st[L.h_ss()] + ridge, g = st[L.g_s()];
+  for (int k = 0; k < B; ++k) {
+    const double dk = st[L.h_kk(k)] + ridge;
+    a -= st[L.h_sk(k)] * st[L.h_sk(k)] / dk;
+    g -= st[L.h_sk(k)] * st[L.g_k(k)] / dk;
+  }
+  const double ns = st[L.n_s()];
+  double step = (g / a) * (ns / (ns + 50.0));
+  if (!isfinite(step)) step = 0.0;
+  const double s0 = st[L.slope()];
+  for (int h = 0; h < 8 && s0 + step < 0.0; ++h) step *= 0.5;
+  if (s0 + step < 0.0) step = 0.0;
+  for (int k = 0; k < B; ++k) {
+    const double dk = st[L.h_kk(k)] + ridge;
+    const double nk = st[L.n_k(k)];
+    double sb = ((st[L.g_k(k)] - st[L.h_sk(k)] * step) / dk) * (nk / (nk + 50.0));
+    if (!isfinite(sb)) sb = 0.0;
+    st[L.bias(k)] += sb;
+  }
+  st[L.slope()] = s0 + step;
+  st[L.h_ss()] = st[L.g_s()] = st[L.n_s()] = 0.0;
+  for (int k = 0; k < B; ++k) st[L.h_sk(k)] = st[L.h_kk(k)] = st[L.g_k(k)] = st[L.n_k(k)] = 0.0;
+  st[L.calls()] = 0.0;
+  st[L.refits()] += 1.0;
+}
+
 }  // namespace sv

@@ -97,6 +97,14 @@ def test_host_validation_without_gpu(lib):
     assert lib.spec_verify_acceptance_stats(fake, fake, 4, 1025, fake, None) == -2
     assert lib.spec_verify_acceptance_stats(fake, fake, 4, 16, None, None) == -1
     assert lib.spec_verify_acceptance_stats(None, fake, 4, 16, fake, None) == -1
+    # estimator: block outside [1, 64], NULL state
+    lib.spec_verify_estimator_init.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
+    lib.spec_verify_estimator_state_doubles.argtypes = [ctypes.c_int32]
+    lib.spec_verify_estimator_state_doubles.restype = ctypes.c_size_t
+    assert lib.spec_verify_estimator_init(fake, 0, None) == -2
+    assert lib.spec_verify_estimator_init(fake, 65, None) == -2
+    assert lib.spec_verify_estimator_init(None, 8, None) == -1
+    assert lib.spec_verify_estimator_state_doubles(8) == 6 + 5 * 8
 
 
 def test_workspace_query_grows_with_rows(lib):

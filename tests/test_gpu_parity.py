@@ -408,6 +408,72 @@ def test_acceptance_stats_match_oracle(R, Bk):
     assert np.array_equal(st_g, svref.acceptance_stats(L, w, Bk))
 
 
+def test_estimator_predict_matches_oracle():
+    """Features and confidences of the online acceptance estimator from the
+    library's own draft build (row max, lse), against the oracle's feature and
+    prediction on the same arrays."""
+    from rejection_sampling_amd import binding as B
+    R, Bk, V = 40, 6, 3001
+    g = np.random.default_rng(21)
+    x = (g.normal(0, 3, (R * Bk, V))).astype(np.float32)
+    x[3, 17] = 60.0                                   # a row with q_max = 1 in fp32 terms
+    T = g.uniform(0.4, 1.3, R).astype(np.float32)
+    T[::4] = 0.0                                      # greedy requests
+    qo = (np.arange(R + 1) * Bk).astype(np.int32)
+    prm = B.Params(dev_f32(T), None, None)
+    built = B.build_target_probs(dev_f32(x), dev_i32(qo), prm)
+    m, lse = built["row_max"], built["row_lse"]
+    est = B.AcceptanceEstimator(Bk)
+    progress(f"estimator predict R={R} B={Bk}")
+    feat_g, conf_g = est.predict(m, lse, dev_f32(T))
+    t_eff = np.repeat(T, Bk)
+    feat = svref.est_feature(m.cpu().numpy(), lse.cpu().numpy(), t_eff)
+    fg = feat_g.cpu().numpy().reshape(-1)
+    # compared as probabilities: logit is ill-conditioned as q_max nears 1, where
+    # one ulp of exp on either side moves x by ~1e-16 / (1 - q_max)
+    expit = lambda v: 1.0 / (1.0 + np.exp(-v))
+    assert np.allclose(expit(fg), expit(feat), rtol=0, atol=1e-13)
+    mid = np.abs(feat) < 20
+    assert np.allclose(fg[mid], feat[mid], rtol=1e-11, atol=1e-11)
+    ref = svref.Estimator(Bk)
+    p = ref.predict(feat, np.tile(np.arange(Bk, dtype=np.int32), R))
+    assert np.allclose(conf_g.cpu().numpy().reshape(-1), p.astype(np.float32), rtol=2e-7, atol=0)
+
+
+def test_estimator_observe_and_refit_match_oracle():
+    """250 observed steps (two refits) on simulated drafts: the device state's
+    coefficients follow the oracle's within rounding (its sums run in another
+    order), and the same inputs give the same device state twice."""
+    from rejection_sampling_amd import binding as B
+    R, Bk = 96, 8
+    g = np.random.default_rng(22)
+    true_b = np.linspace(1.0, -1.5, Bk)
+    steps = []
+    for _ in range(250):
+        xs = g.normal(0, 2, (R, Bk))
+        p = 1 / (1 + np.exp(-(1.0 * xs + true_b)))
+        surv = g.random((R, Bk)) < p
+        L = np.where(surv.all(axis=1), Bk, np.argmin(surv, axis=1)).astype(np.int32)
+        w = g.integers(0, Bk + 1, R).astype(np.int32)
+        steps.append((xs, np.minimum(L, w), w))
+    states = []
+    for rep in range(2):
+        est = B.AcceptanceEstimator(Bk)
+        ref = svref.Estimator(Bk)
+        progress(f"estimator observe, pass {rep}")
+        for c, (xs, L, w) in enumerate(steps):
+            est.observe(torch.from_numpy(xs).cuda(), dev_i32(L), dev_i32(w))
+            ref.observe(xs, L, w)
+            if (c + 1) % 50 == 0:
+                s, b, n = est.coefficients()
+                assert n == ref.st.refits
+                assert s == pytest.approx(ref.slope, rel=1e-9, abs=1e-12)
+                assert np.allclose(b, ref.bias, rtol=1e-9, atol=1e-12)
+        states.append(est.state.cpu().numpy())
+    assert ref.st.refits == 2
+    assert np.array_equal(states[0].view(np.uint64), states[1].view(np.uint64))
+
+
 def test_accept_prefix_matches_oracle():
     from rejection_sampling_amd import binding as B
     g = np.random.default_rng(3)
