@@ -37,11 +37,17 @@ SEED = 3007
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "row_pass_traffic.json")
 
 
+# Sources the row-pass kernel and its launch are built from; sv_plan.hip
+# (planner, statistics and estimator kernels) is a separate translation unit.
+ROW_PASS_SOURCES = ("sv_api.hip", "sv_device.hpp", "sv_kernels.h", "sv_rowpass.hpp",
+                    "sv_verify.hip")
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "rejection_sampling_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".hpp", ".h")):
+        if name in ROW_PASS_SOURCES:
             with open(os.path.join(csrc, name), "rb") as f:
                 h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
