@@ -14,9 +14,10 @@ namespace sv {
 
 constexpr int kPB = kPlanBlock;
 constexpr int kPW = kPB / 64;
+constexpr int kKeyRegs = 8;  // planner keys held per thread (n <= 8192 stays in registers)
 
 __device__ __forceinline__ int pblock_exclusive_sum(int v, int* scr, int* total) {
-  int incl = wave_inclusive_sum(v);
+  int incl = wave_scan_dpp(v);
   __syncthreads();
   if (lane_id() == 63) scr[wave_id()] = incl;
   __syncthreads();
@@ -30,27 +31,46 @@ __device__ __forceinline__ int pblock_exclusive_sum(int v, int* scr, int* total)
 }
 
 __global__ __launch_bounds__(kPB) void plan_kernel(PlanArgs A) {
-  __shared__ uint32_t hist[256];
+  __shared__ uint32_t hist[2][256];  // one counts while the other is cleared
   __shared__ int scr[kPW];
   __shared__ int sel_digit, sel_need, sel_exact;
   const int tid = threadIdx.x;
   const int R = A.num_requests, B = A.block;
   const long n = (long)R * B;
 
-  // survival, fp32, left to right; clamp to [0, 1], NaN -> 0
+  // survival, fp32, left to right; clamp to [0, 1], NaN -> 0 (confidences
+  // loaded eight at a time so their latencies overlap)
   for (int r = tid; r < R; r += kPB) {
     float acc = 1.0f;
-    for (int j = 0; j < B; ++j) {
-      float cf = A.conf[(size_t)r * A.ld_conf + j];
-      cf = (cf > 0.0f) ? (cf < 1.0f ? cf : 1.0f) : 0.0f;
-      acc = (j == 0) ? cf : __fmul_rn(acc, cf);
-      if (A.survival) A.survival[(size_t)r * B + j] = acc;
-      const uint32_t sb = __float_as_uint(acc);  // acc >= +0: bits order = value order
-      A.keys[(size_t)r * B + j] = ((uint64_t)(~sb) << 32) | (uint64_t)(uint32_t)(j * R + r);
+    for (int j0 = 0; j0 < B; j0 += 8) {
+      float c[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        c[u] = j0 + u < B ? A.conf[(size_t)r * A.ld_conf + j0 + u] : 0.0f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = j0 + u;
+        if (j >= B) break;
+        const float cf = (c[u] > 0.0f) ? (c[u] < 1.0f ? c[u] : 1.0f) : 0.0f;
+        acc = (j == 0) ? cf : __fmul_rn(acc, cf);
+        if (A.survival) A.survival[(size_t)r * B + j] = acc;
+        const uint32_t sb = __float_as_uint(acc);  // acc >= +0: bits order = value order
+        A.keys[(size_t)r * B + j] = ((uint64_t)(~sb) << 32) | (uint64_t)(uint32_t)(j * R + r);
+      }
     }
   }
   __threadfence_block();
   __syncthreads();
+
+  // up to kKeyRegs keys per thread (key t in thread t mod kPB) stay in
+  // registers for the select's passes, spread over every wave
+  const bool in_regs = n <= (long)kPB * kKeyRegs;
+  uint64_t kr[kKeyRegs];
+#pragma unroll
+  for (int i = 0; i < kKeyRegs; ++i) {
+    const long t = tid + (long)i * kPB;
+    kr[i] = (in_regs && t < n) ? A.keys[t] : ~0ull;
+  }
 
   long take = A.budget < 0 ? 0 : (long)A.budget;
   if (take > n) take = n;
@@ -58,20 +78,43 @@ __global__ __launch_bounds__(kPB) void plan_kernel(PlanArgs A) {
   bool all = take == n, none = take == 0;
   if (!all && !none) {
     int need = (int)take;
+    for (int b = tid; b < 256; b += kPB) hist[0][b] = 0u;
+    __syncthreads();
+    int hb = 0;
     for (int shift = 56; shift >= 0; shift -= 8) {
-      for (int b = tid; b < 256; b += kPB) hist[b] = 0u;
-      __syncthreads();
-      for (long t = tid; t < n; t += kPB) {
-        const uint64_t k = A.keys[t];
-        if ((k & pmask) == prefix) atomicAdd(&hist[(uint32_t)(k >> shift) & 255u], 1u);
+      uint32_t* h = hist[hb];
+      if (in_regs) {
+#pragma unroll
+        for (int i = 0; i < kKeyRegs; ++i) {
+          const long t = tid + (long)i * kPB;
+          const bool mine = t < n && (kr[i] & pmask) == prefix;
+          const uint32_t dg = (uint32_t)(kr[i] >> shift) & 255u;
+          // a wave whose matching keys share one digit adds them in one atomic
+          const uint64_t act = __ballot(mine);
+          if (act == 0) continue;
+          const int first = __ffsll((unsigned long long)act) - 1;
+          const uint32_t d0 = (uint32_t)__builtin_amdgcn_readlane((int)dg, first);
+          if (__ballot(mine && dg != d0) == 0) {
+            if (lane_id() == first) atomicAdd(&h[d0], (uint32_t)__popcll(act));
+          } else if (mine) {
+            atomicAdd(&h[dg], 1u);
+          }
+        }
+      } else {
+        for (long t = tid; t < n; t += kPB) {
+          const uint64_t k = A.keys[t];
+          if ((k & pmask) == prefix) atomicAdd(&h[(uint32_t)(k >> shift) & 255u], 1u);
+        }
       }
+      // the other buffer was last read before the previous round's second barrier
+      for (int b = tid; b < 256; b += kPB) hist[hb ^ 1][b] = 0u;
       __syncthreads();
       if (wave_id() == 0) {
         const int l = lane_id();  // lane l owns digits 4l .. 4l+3, ascending
-        const int h0 = (int)hist[4 * l], h1 = (int)hist[4 * l + 1];
-        const int h2 = (int)hist[4 * l + 2], h3 = (int)hist[4 * l + 3];
+        const int h0 = (int)h[4 * l], h1 = (int)h[4 * l + 1];
+        const int h2 = (int)h[4 * l + 2], h3 = (int)h[4 * l + 3];
         const int local = h0 + h1 + h2 + h3;
-        const int incl = wave_inclusive_sum(local);
+        const int incl = wave_scan_dpp(local);
         const int excl = incl - local;
         const uint64_t mk = __ballot(excl < need && need <= incl);
         const int src = __ffsll((unsigned long long)mk) - 1;
@@ -92,7 +135,7 @@ __global__ __launch_bounds__(kPB) void plan_kernel(PlanArgs A) {
       const int ex = sel_exact;
       prefix |= (uint64_t)d << shift;
       pmask |= (uint64_t)0xFF << shift;
-      __syncthreads();
+      hb ^= 1;
       if (ex) break;
     }
   }
@@ -103,8 +146,10 @@ __global__ __launch_bounds__(kPB) void plan_kernel(PlanArgs A) {
     const int r = r0 + tid;
     int vl = 0;
     if (r < R) {
-      if (all) vl = B;
+      if (all)
+        vl = B;
       else if (!none)
+#pragma unroll 8
         for (int j = 0; j < B; ++j) vl += ((A.keys[(size_t)r * B + j] & pmask) <= prefix) ? 1 : 0;
       A.verify_len[r] = vl;
     }
@@ -147,58 +192,65 @@ __global__ __launch_bounds__(256) void accept_prefix_kernel(const uint8_t* accep
 
 // Acceptance and trim statistics of one verify step (TensorRT-LLM PR #17056,
 // commit note on the trim-regret metric; per-position acceptance as in the
-// consolidation study, section 1).  One workgroup: each thread counts its
-// requests (trimmed: window below the block; regret: trimmed with the whole
-// window accepted) and bins their windows and accepted lengths in LDS; the
-// per-position counts are suffix sums of those bins (positions j < w are
-// offered, j < L accepted).  Integer counts only, so the result is exact.
+// consolidation study, section 1).  One workgroup, integer counts only, so the
+// result is exact.  Each thread takes its requests (trimmed: window below the
+// block; regret: trimmed with the whole window accepted); per position j the
+// offered count is #{w > j} and the accepted one #{L > j}: each wave counts
+// its 64 requests by a ballot per j (lane j mod 64 keeps the count) until no
+// window reaches j, and adds its counts to LDS, one address per lane.
 __global__ __launch_bounds__(kPlanBlock) void acceptance_stats_kernel(
     const int32_t* accept_len, const int32_t* verify_len, int32_t R, int32_t B, int64_t* stats) {
-  __shared__ uint32_t hw[kPB + 1], hl[kPB + 1];  // bins 0..B of windows and accepted lengths
-  __shared__ uint32_t tot[4];
-  const int tid = threadIdx.x;
-  for (int v = tid; v <= B; v += kPB) { hw[v] = 0u; hl[v] = 0u; }
-  if (tid < 4) tot[tid] = 0u;
+  __shared__ uint32_t cw[kPB], cl[kPB];  // per position: offered, accepted
+  __shared__ uint32_t tot[kPW][4];
+  const int tid = threadIdx.x, wv = wave_id(), l = lane_id();
+  for (int j = tid; j < B; j += kPB) { cw[j] = 0u; cl[j] = 0u; }
   __syncthreads();
-  uint32_t trimmed = 0u, regret = 0u, sum_l = 0u, sum_w = 0u;
-  for (int r = tid; r < R; r += kPB) {
-    int w = verify_len[r];
-    w = w < 0 ? 0 : (w > B ? B : w);
-    int L = accept_len[r];
-    L = L < 0 ? 0 : (L > w ? w : L);
-    if (w < B) {
-      trimmed += 1u;
-      if (L == w) regret += 1u;
+  int trimmed = 0, regret = 0, sum_l = 0, sum_w = 0;
+  for (int r0 = 0; r0 < R; r0 += kPB) {  // the same passes for every wave
+    const int r = r0 + tid;
+    int w = 0, L = 0;
+    if (r < R) {
+      w = verify_len[r];
+      w = w < 0 ? 0 : (w > B ? B : w);
+      L = accept_len[r];
+      L = L < 0 ? 0 : (L > w ? w : L);
+      if (w < B) {
+        trimmed += 1;
+        if (L == w) regret += 1;
+      }
+      sum_l += L;
+      sum_w += w;
     }
-    sum_l += (uint32_t)L;
-    sum_w += (uint32_t)w;
-    atomicAdd(&hw[w], 1u);
-    atomicAdd(&hl[L], 1u);
+    bool more = true;
+    for (int c = 0; more && c < B; c += 64) {
+      uint32_t aw = 0u, al = 0u;
+      const int cend = B - c < 64 ? B - c : 64;
+      for (int jj = 0; jj < cend; ++jj) {
+        const uint64_t bw = __ballot(w > c + jj);
+        if (bw == 0) { more = false; break; }  // L <= w: no accepted count either
+        const uint64_t bl = __ballot(L > c + jj);
+        if (l == jj) { aw = (uint32_t)__popcll(bw); al = (uint32_t)__popcll(bl); }
+      }
+      if (aw) atomicAdd(&cw[c + l], aw);
+      if (al) atomicAdd(&cl[c + l], al);
+    }
   }
-  atomicAdd(&tot[0], trimmed);
-  atomicAdd(&tot[1], regret);
-  atomicAdd(&tot[2], sum_l);
-  atomicAdd(&tot[3], sum_w);
+  trimmed = wave_scan_dpp(trimmed);
+  regret = wave_scan_dpp(regret);
+  sum_l = wave_scan_dpp(sum_l);
+  sum_w = wave_scan_dpp(sum_w);
+  if (l == 63) { tot[wv][0] = trimmed; tot[wv][1] = regret; tot[wv][2] = sum_l; tot[wv][3] = sum_w; }
   __syncthreads();
-  // suffix sums over bins 1..B in place: after them hw[v] = #{w >= v}
-  for (int d = 1; d < B; d <<= 1) {
-    uint32_t a = 0u, b = 0u;
-    const int v = tid + 1;
-    if (v <= B && v + d <= B) { a = hw[v + d]; b = hl[v + d]; }
-    __syncthreads();
-    if (v <= B) { hw[v] += a; hl[v] += b; }
-    __syncthreads();
-  }
-  if (tid == 0) {
+  if (tid < 4) {
+    uint32_t v = 0u;
+    for (int q = 0; q < kPW; ++q) v += tot[q][tid];
+    stats[1 + tid] = v;
+  } else if (tid == 4) {
     stats[0] = R;
-    stats[1] = tot[0];
-    stats[2] = tot[1];
-    stats[3] = tot[2];
-    stats[4] = tot[3];
   }
   for (int j = tid; j < B; j += kPB) {
-    stats[5 + j] = hw[j + 1];      // offered: w > j
-    stats[5 + B + j] = hl[j + 1];  // accepted: L > j
+    stats[5 + j] = cw[j];
+    stats[5 + B + j] = cl[j];
   }
 }
 
@@ -261,96 +313,129 @@ __global__ void est_predict_kernel(const float* row_max, const float* row_lse,
 
 // One step's observations (labels 1 for the accepted drafts, 0 for the first
 // rejected one) added to the IRLS statistics at the current coefficients;
-// every kEstRefit calls the refit.  One workgroup: per position, each wave
-// sums its lanes by a DPP scan and the waves' sums are added in wave order.
+// every kEstRefit calls the refit.  One workgroup: wave w takes positions
+// k = w, w + 16, ... over every request (four requests' inputs loaded per lane
+// at once) and sums its lanes by DPP scans; one thread per position adds the
+// sums to the stored ones, and the refit runs from LDS.  A fixed order
+// throughout, so the same inputs give the same state.
 __global__ __launch_bounds__(kPlanBlock) void est_observe_kernel(
     const double* feature, const int32_t* accept_len, const int32_t* verify_len, int32_t R,
     int32_t B, double* st) {
+  constexpr int kU = 4;
   const EstLayout L(B);
-  __shared__ double part[kPW][4];
-  __shared__ double tot[kPW][3];
+  __shared__ double part[kEstMaxBlock][7];  // per position: h_sk, h_kk, g_k, n_k, h_ss, g_s, n_s
+  __shared__ double fin[kEstMaxBlock][4];   // the statistics after this call
+  __shared__ double coef[kEstMaxBlock + 1]; // slope, intercepts
+  __shared__ double fin_s[4];               // h_ss, g_s, n_s, calls
+  __shared__ double step_s;
   const int tid = threadIdx.x, w = wave_id(), l = lane_id();
-  const double slope = st[L.slope()];
-  double h_ss = 0.0, g_s = 0.0, n_s = 0.0;
-  for (int k = 0; k < B; ++k) {
-    const double bk = st[L.bias(k)];
-    double hsk = 0.0, hkk = 0.0, gk = 0.0, nk = 0.0;
-    for (int r = tid; r < R; r += kPB) {
-      int wr = verify_len[r];
-      wr = wr < 0 ? 0 : (wr > B ? B : wr);
-      int lr = accept_len[r];
-      lr = lr < 0 ? 0 : (lr > wr ? wr : lr);
-      const int last = lr < wr ? lr : lr - 1;
-      if (k > last) continue;
-      const double x = feature[(size_t)r * B + k];
-      const double y = k < lr ? 1.0 : 0.0;
-      const double p = est_sigmoid(slope * x + bk);
-      const double wt = p * (1.0 - p);
-      h_ss += wt * x * x;
-      hsk += wt * x;
-      hkk += wt;
-      g_s += (y - p) * x;
-      gk += y - p;
-      n_s += 1.0;
-      nk += 1.0;
+  if (tid <= B) coef[tid] = st[tid];  // slope at 0, intercepts at 1..B
+  __syncthreads();
+  const double slope = coef[0];
+  for (int k = w; k < B; k += kPW) {
+    const double bk = coef[1 + k];
+    double hss = 0.0, gs = 0.0, hsk = 0.0, hkk = 0.0, gk = 0.0, nk = 0.0;
+    for (int r0 = 0; r0 < R; r0 += 64 * kU) {
+      int wr[kU], lr[kU];
+      double x[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int r = r0 + 64 * u + l;
+        wr[u] = r < R ? verify_len[r] : 0;
+        lr[u] = r < R ? accept_len[r] : 0;
+        x[u] = r < R ? feature[(size_t)r * B + k] : 0.0;
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int wc = wr[u] < 0 ? 0 : (wr[u] > B ? B : wr[u]);
+        const int lc = lr[u] < 0 ? 0 : (lr[u] > wc ? wc : lr[u]);
+        const int last = lc < wc ? lc : lc - 1;  // an empty window gives -1
+        if (k > last) continue;
+        const double y = k < lc ? 1.0 : 0.0;
+        const double p = est_sigmoid(slope * x[u] + bk);
+        const double wt = p * (1.0 - p);
+        hss += wt * x[u] * x[u];
+        hsk += wt * x[u];
+        hkk += wt;
+        gs += (y - p) * x[u];
+        gk += y - p;
+        nk += 1.0;
+      }
     }
     hsk = readlane_d(wave_scan_dpp(hsk), 63);
     hkk = readlane_d(wave_scan_dpp(hkk), 63);
     gk = readlane_d(wave_scan_dpp(gk), 63);
     nk = readlane_d(wave_scan_dpp(nk), 63);
-    if (l == 0) { part[w][0] = hsk; part[w][1] = hkk; part[w][2] = gk; part[w][3] = nk; }
-    __syncthreads();
-    if (tid == 0) {
-      double a = 0.0, b = 0.0, c = 0.0, d = 0.0;
-      for (int q = 0; q < kPW; ++q) { a += part[q][0]; b += part[q][1]; c += part[q][2]; d += part[q][3]; }
-      st[L.h_sk(k)] += a;
-      st[L.h_kk(k)] += b;
-      st[L.g_k(k)] += c;
-      st[L.n_k(k)] += d;
+    hss = readlane_d(wave_scan_dpp(hss), 63);
+    gs = readlane_d(wave_scan_dpp(gs), 63);
+    if (l == 0) {
+      part[k][0] = hsk; part[k][1] = hkk; part[k][2] = gk; part[k][3] = nk;
+      part[k][4] = hss; part[k][5] = gs; part[k][6] = nk;
     }
-    __syncthreads();
   }
-  h_ss = readlane_d(wave_scan_dpp(h_ss), 63);
-  g_s = readlane_d(wave_scan_dpp(g_s), 63);
-  n_s = readlane_d(wave_scan_dpp(n_s), 63);
-  if (l == 0) { tot[w][0] = h_ss; tot[w][1] = g_s; tot[w][2] = n_s; }
   __syncthreads();
-  if (tid != 0) return;
-  {
+  if (tid < B) {
+    const int k = tid;
+    fin[k][0] = st[L.h_sk(k)] + part[k][0];
+    fin[k][1] = st[L.h_kk(k)] + part[k][1];
+    fin[k][2] = st[L.g_k(k)] + part[k][2];
+    fin[k][3] = st[L.n_k(k)] + part[k][3];
+  } else if (tid == kPB - 1) {
     double a = 0.0, b = 0.0, c = 0.0;
-    for (int q = 0; q < kPW; ++q) { a += tot[q][0]; b += tot[q][1]; c += tot[q][2]; }
-    st[L.h_ss()] += a;
-    st[L.g_s()] += b;
-    st[L.n_s()] += c;
+    for (int k = 0; k < B; ++k) { a += part[k][4]; b += part[k][5]; c += part[k][6]; }
+    fin_s[0] = st[L.h_ss()] + a;
+    fin_s[1] = st[L.g_s()] + b;
+    fin_s[2] = st[L.n_s()] + c;
+    fin_s[3] = st[L.calls()] + 1.0;
   }
-  st[L.calls()] += 1.0;
-  if (st[L.calls()] < (double)kEstRefit) return;
+  __syncthreads();
+  const bool refit = fin_s[3] >= (double)kEstRefit;
+  if (!refit) {  // store the statistics and the count
+    if (tid < B) {
+      st[L.h_sk(tid)] = fin[tid][0];
+      st[L.h_kk(tid)] = fin[tid][1];
+      st[L.g_k(tid)] = fin[tid][2];
+      st[L.n_k(tid)] = fin[tid][3];
+    } else if (tid == kPB - 1) {
+      st[L.h_ss()] = fin_s[0];
+      st[L.g_s()] = fin_s[1];
+      st[L.n_s()] = fin_s[2];
+      st[L.calls()] = fin_s[3];
+    }
+    return;
+  }
   // refit: arrowhead Newton solve with a ridge (Schur complement on the slope)
-  const double ridge = 1e-3;
-  double a = st[L.h_ss()] + ridge, g = st[L.g_s()];
-  for (int k = 0; k < B; ++k) {
-    const double dk = st[L.h_kk(k)] + ridge;
-    a -= st[L.h_sk(k)] * st[L.h_sk(k)] / dk;
-    g -= st[L.h_sk(k)] * st[L.g_k(k)] / dk;
+  if (tid == 0) {
+    const double ridge = 1e-3;
+    double a = fin_s[0] + ridge, g = fin_s[1];
+    for (int k = 0; k < B; ++k) {
+      const double dk = fin[k][1] + ridge;
+      a -= fin[k][0] * fin[k][0] / dk;
+      g -= fin[k][0] * fin[k][2] / dk;
+    }
+    const double ns = fin_s[2];
+    double step = (g / a) * (ns / (ns + 50.0));
+    if (!isfinite(step)) step = 0.0;
+    const double s0 = coef[0];
+    for (int h = 0; h < 8 && s0 + step < 0.0; ++h) step *= 0.5;
+    if (s0 + step < 0.0) step = 0.0;
+    step_s = step;
+    st[L.slope()] = s0 + step;
+    st[L.h_ss()] = st[L.g_s()] = st[L.n_s()] = 0.0;
+    st[L.calls()] = 0.0;
+    st[L.refits()] += 1.0;
   }
-  const double ns = st[L.n_s()];
-  double step = (g / a) * (ns / (ns + 50.0));
-  if (!isfinite(step)) step = 0.0;
-  const double s0 = st[L.slope()];
-  for (int h = 0; h < 8 && s0 + step < 0.0; ++h) step *= 0.5;
-  if (s0 + step < 0.0) step = 0.0;
-  for (int k = 0; k < B; ++k) {
-    const double dk = st[L.h_kk(k)] + ridge;
-    const double nk = st[L.n_k(k)];
-    double sb = ((st[L.g_k(k)] - st[L.h_sk(k)] * step) / dk) * (nk / (nk + 50.0));
+  __syncthreads();
+  if (tid < B) {  // intercepts: their Newton step given the slope step taken
+    const int k = tid;
+    const double ridge = 1e-3;
+    const double dk = fin[k][1] + ridge;
+    const double nk = fin[k][3];
+    double sb = ((fin[k][2] - fin[k][0] * step_s) / dk) * (nk / (nk + 50.0));
     if (!isfinite(sb)) sb = 0.0;
-    st[L.bias(k)] += sb;
+    st[L.bias(k)] = coef[1 + k] + sb;
+    st[L.h_sk(k)] = st[L.h_kk(k)] = st[L.g_k(k)] = st[L.n_k(k)] = 0.0;
   }
-  st[L.slope()] = s0 + step;
-  st[L.h_ss()] = st[L.g_s()] = st[L.n_s()] = 0.0;
-  for (int k = 0; k < B; ++k) st[L.h_sk(k)] = st[L.h_kk(k)] = st[L.g_k(k)] = st[L.n_k(k)] = 0.0;
-  st[L.calls()] = 0.0;
-  st[L.refits()] += 1.0;
 }
 
 }  // namespace sv

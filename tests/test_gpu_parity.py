@@ -371,7 +371,7 @@ def test_workload5_planner_and_verify():
 
 
 # -------------------------------------------------------------- planner
-@pytest.mark.parametrize("R,Bk", [(1, 1), (7, 3), (256, 16), (1000, 9)])
+@pytest.mark.parametrize("R,Bk", [(1, 1), (7, 3), (256, 16), (1024, 8), (1000, 9), (3000, 2), (100, 20)])
 def test_planner_matches_oracle(R, Bk):
     from rejection_sampling_amd import binding as B
     g = np.random.default_rng(R)
@@ -389,6 +389,12 @@ def test_planner_matches_oracle(R, Bk):
     vl_g, qo_g, _ = B.plan_windows(dev_f32(conf), (R * Bk) // 2 + 1)
     vl, qo, _ = svref.plan_windows(conf, (R * Bk) // 2 + 1)
     assert np.array_equal(vl_g.cpu().numpy(), vl)
+    # confidences a few ulps below 1: survivals share their leading key bytes
+    conf = (1.0 - g.integers(1, 6, (R, Bk)) * 2.0 ** -24).astype(np.float32)
+    for budget in (1, R * Bk // 2, R * Bk - 1):
+        vl_g, _, _ = B.plan_windows(dev_f32(conf), budget)
+        vl, _, _ = svref.plan_windows(conf, budget)
+        assert np.array_equal(vl_g.cpu().numpy(), vl), budget
 
 
 @pytest.mark.parametrize("R,Bk", [(0, 5), (1, 0), (3, 1), (256, 16), (5000, 7), (300, 1024)])
