@@ -480,6 +480,30 @@ def test_estimator_observe_and_refit_match_oracle():
     assert np.array_equal(states[0].view(np.uint64), states[1].view(np.uint64))
 
 
+def test_estimator_observe_wide_block_matches_oracle():
+    """Blocks wider than the workgroup's 16 waves (several positions per wave)
+    and more requests than one load round: one refit after 100 steps."""
+    from rejection_sampling_amd import binding as B
+    R, Bk = 700, 40
+    g = np.random.default_rng(23)
+    true_b = np.linspace(2.0, -2.0, Bk)
+    est = B.AcceptanceEstimator(Bk)
+    ref = svref.Estimator(Bk)
+    progress(f"estimator observe R={R} B={Bk}")
+    for c in range(110):
+        xs = g.normal(0, 2, (R, Bk))
+        surv = g.random((R, Bk)) < 1 / (1 + np.exp(-(0.8 * xs + true_b)))
+        L = np.where(surv.all(axis=1), Bk, np.argmin(surv, axis=1)).astype(np.int32)
+        w = g.integers(-1, Bk + 2, R).astype(np.int32)
+        L = np.minimum(L, np.maximum(w, 0)).astype(np.int32)
+        est.observe(torch.from_numpy(xs).cuda(), dev_i32(L), dev_i32(w))
+        ref.observe(xs, L, w)
+    s_, b, n = est.coefficients()
+    assert n == ref.st.refits == 1
+    assert s_ == pytest.approx(ref.slope, rel=1e-9, abs=1e-12)
+    assert np.allclose(b, ref.bias, rtol=1e-9, atol=1e-12)
+
+
 def test_accept_prefix_matches_oracle():
     from rejection_sampling_amd import binding as B
     g = np.random.default_rng(3)
