@@ -14,7 +14,9 @@ namespace sv {
 
 constexpr int kPB = kPlanBlock;
 constexpr int kPW = kPB / 64;
-constexpr int kKeyRegs = 8;  // planner keys held per thread (n <= 8192 stays in registers)
+constexpr int kKeyRegs = 8;     // planner keys held per thread (n <= 8192 stays in registers)
+constexpr int kLdsKeys = 4096;  // planner keys staged in LDS instead of the workspace
+constexpr int kConfBatch = 8;   // planner confidences loaded per batch
 
 __device__ __forceinline__ int pblock_exclusive_sum(int v, int* scr, int* total) {
   int incl = wave_scan_dpp(v);
@@ -32,34 +34,38 @@ __device__ __forceinline__ int pblock_exclusive_sum(int v, int* scr, int* total)
 
 __global__ __launch_bounds__(kPB) void plan_kernel(PlanArgs A) {
   __shared__ uint32_t hist[2][256];  // one counts while the other is cleared
+  __shared__ uint64_t lkeys[kLdsKeys];  // n <= kLdsKeys: key of (r, j) at j * R + r
   __shared__ int scr[kPW];
   __shared__ int sel_digit, sel_need, sel_exact;
   const int tid = threadIdx.x;
   const int R = A.num_requests, B = A.block;
   const long n = (long)R * B;
+  const bool in_lds = n <= kLdsKeys;
 
   // survival, fp32, left to right; clamp to [0, 1], NaN -> 0 (confidences
-  // loaded eight at a time so their latencies overlap)
+  // loaded kConfBatch at a time so their latencies overlap)
   for (int r = tid; r < R; r += kPB) {
     float acc = 1.0f;
-    for (int j0 = 0; j0 < B; j0 += 8) {
-      float c[8];
+    for (int j0 = 0; j0 < B; j0 += kConfBatch) {
+      float c[kConfBatch];
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
+      for (int u = 0; u < kConfBatch; ++u)
         c[u] = j0 + u < B ? A.conf[(size_t)r * A.ld_conf + j0 + u] : 0.0f;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < kConfBatch; ++u) {
         const int j = j0 + u;
         if (j >= B) break;
         const float cf = (c[u] > 0.0f) ? (c[u] < 1.0f ? c[u] : 1.0f) : 0.0f;
         acc = (j == 0) ? cf : __fmul_rn(acc, cf);
         if (A.survival) A.survival[(size_t)r * B + j] = acc;
         const uint32_t sb = __float_as_uint(acc);  // acc >= +0: bits order = value order
-        A.keys[(size_t)r * B + j] = ((uint64_t)(~sb) << 32) | (uint64_t)(uint32_t)(j * R + r);
+        const uint64_t key = ((uint64_t)(~sb) << 32) | (uint64_t)(uint32_t)(j * R + r);
+        if (in_lds) lkeys[j * R + r] = key;
+        else A.keys[(size_t)r * B + j] = key;
       }
     }
   }
-  __threadfence_block();
+  if (!in_lds) __threadfence_block();
   __syncthreads();
 
   // up to kKeyRegs keys per thread (key t in thread t mod kPB) stay in
@@ -69,7 +75,7 @@ __global__ __launch_bounds__(kPB) void plan_kernel(PlanArgs A) {
 #pragma unroll
   for (int i = 0; i < kKeyRegs; ++i) {
     const long t = tid + (long)i * kPB;
-    kr[i] = (in_regs && t < n) ? A.keys[t] : ~0ull;
+    kr[i] = (in_regs && t < n) ? (in_lds ? lkeys[t] : A.keys[t]) : ~0ull;
   }
 
   long take = A.budget < 0 ? 0 : (long)A.budget;
@@ -150,7 +156,10 @@ __global__ __launch_bounds__(kPB) void plan_kernel(PlanArgs A) {
         vl = B;
       else if (!none)
 #pragma unroll 8
-        for (int j = 0; j < B; ++j) vl += ((A.keys[(size_t)r * B + j] & pmask) <= prefix) ? 1 : 0;
+        for (int j = 0; j < B; ++j) {
+          const uint64_t k = in_lds ? lkeys[j * R + r] : A.keys[(size_t)r * B + j];
+          vl += ((k & pmask) <= prefix) ? 1 : 0;
+        }
       A.verify_len[r] = vl;
     }
     int total;
