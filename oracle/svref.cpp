@@ -455,6 +455,68 @@ int32_t svref_plan_windows(const float* confidence, int64_t ld_conf, int32_t num
   return 0;
 }
 
+int32_t svref_budget_from_costs(const float* confidence, int64_t ld_conf, int32_t num_requests,
+                                int32_t block, const float* cost, int32_t ncost,
+                                int32_t* budget, double* theta) {
+  if (!budget || (num_requests > 0 && block > 0 && !confidence)) return -1;
+  if (num_requests < 0 || block < 0 || (num_requests > 0 && ld_conf < block)) return -2;
+  const int32_t R = num_requests, B = block;
+  const int64_t n = (int64_t)R * B;
+
+  /* The survivals and their rank order, as the planner computes them. */
+  std::vector<float> S((size_t)n);
+  std::vector<int32_t> vl((size_t)R), qo((size_t)R + 1);
+  if (n > 0 && svref_plan_windows(confidence, ld_conf, R, B, 0, vl.data(), qo.data(), S.data()))
+    return -2;
+  std::vector<std::pair<int32_t, int32_t>> order;  /* (j, r) of each survival */
+  order.reserve((size_t)n);
+  for (int32_t r = 0; r < R; ++r)
+    for (int32_t j = 0; j < B; ++j) order.push_back({j, r});
+  std::sort(order.begin(), order.end(), [&](const std::pair<int32_t, int32_t>& x,
+                                            const std::pair<int32_t, int32_t>& y) {
+    const float sx = S[(size_t)x.second * B + x.first], sy = S[(size_t)y.second * B + y.first];
+    if (sx != sy) return sx > sy;
+    if (x.first != y.first) return x.first < y.first;
+    return x.second < y.second;
+  });
+
+  /* No table, or a flat one: no trim. */
+  bool flat = true;
+  if (cost && ncost > 0) {
+    if ((int64_t)ncost < n + R + 1) return -3;
+    for (int64_t t = R; t <= n + R; ++t) {
+      if (!(cost[t] > 0.0f) || !std::isfinite(cost[t])) return -3;
+      if (cost[t] != cost[R]) flat = false;
+    }
+  }
+  if (flat) {
+    *budget = (int32_t)n;
+    if (theta) {
+      double tau = (double)R;
+      for (const auto& o : order) tau += (double)S[(size_t)o.second * B + o.first];
+      *theta = (cost && ncost > 0) ? tau / (double)cost[n + R] : 0.0;
+    }
+    return 0;
+  }
+
+  /* Global argmax of Theta over every budget; ties to the smaller budget. */
+  double tau = (double)R;
+  int64_t best_b = 0;
+  double best = tau / (double)cost[R];
+  for (int64_t b = 1; b <= n; ++b) {
+    const auto& o = order[(size_t)(b - 1)];
+    tau += (double)S[(size_t)o.second * B + o.first];
+    const double th = tau / (double)cost[b + R];
+    if (th > best) {
+      best = th;
+      best_b = b;
+    }
+  }
+  *budget = (int32_t)best_b;
+  if (theta) *theta = best;
+  return 0;
+}
+
 int32_t svref_accept_prefix(const uint8_t* accepted, const int32_t* qo_indptr,
                             int32_t num_requests, const int32_t* verify_cap, int32_t* accept_len) {
   if (!accepted || !qo_indptr || !accept_len || num_requests < 0) return -1;

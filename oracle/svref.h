@@ -109,6 +109,23 @@ int32_t svref_plan_windows(const float* confidence, int64_t ld_conf, int32_t num
 int32_t svref_accept_prefix(const uint8_t* accepted, const int32_t* qo_indptr,
                             int32_t num_requests, const int32_t* verify_cap, int32_t* accept_len);
 
+/* Verify budget from a step-cost table (TensorRT-LLM PR #17056, description:
+ * the planner's budget is a global argmax of tau/cost over a profiled
+ * step-cost table, not a first descent, since the table is a staircase).
+ * Survivals S and their rank order are those of svref_plan_windows.  For a
+ * budget b in [0, R*B], tau(b) = R + (sum of the b first survivals in rank
+ * order, fp64, in that order) is the expected count of tokens the step emits
+ * (accepted drafts plus one bonus or correction token per request), and the
+ * step packs b + R verify rows, so Theta(b) = tau(b) / cost[b + R].  The
+ * smallest b with the largest Theta wins.  With no table (cost NULL or
+ * ncost 0), or a table equal at every count in [R, R*B + R], the budget is
+ * R*B: nothing is trimmed.  theta (may be NULL) receives Theta(budget).
+ * Returns -3 when the table is shorter than R*B + R + 1 entries or holds a
+ * non-finite or non-positive cost in that range. */
+int32_t svref_budget_from_costs(const float* confidence, int64_t ld_conf, int32_t num_requests,
+                                int32_t block, const float* cost, int32_t ncost,
+                                int32_t* budget, double* theta);
+
 /* Acceptance and trim statistics of one verify step (TensorRT-LLM PR #17056,
  * commit note on the trim-regret metric: a trimmed request that accepted its
  * whole window lost acceptance to the cut; the consolidation study, section 1:

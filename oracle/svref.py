@@ -78,6 +78,8 @@ def lib():
         L.svref_accept_prefix.restype = i32
         L.svref_acceptance_stats.argtypes = [P, P, i32, i32, P]
         L.svref_acceptance_stats.restype = i32
+        L.svref_budget_from_costs.argtypes = [P, i64, i32, i32, P, i32, P, P]
+        L.svref_budget_from_costs.restype = i32
         L.svref_est_init.argtypes = [P, i32]
         L.svref_est_init.restype = i32
         L.svref_est_feature.argtypes = [P, P, P, i32, P]
@@ -203,6 +205,22 @@ def plan_windows(conf, budget):
     if rc != 0:
         raise ValueError(f"svref_plan_windows returned {rc}")
     return vl, qo, surv
+
+
+def budget_from_costs(conf, cost):
+    """Verify budget maximising tau/cost over a step-cost table
+    (svref_budget_from_costs): (budget, theta).  cost None: no table."""
+    c = _c(conf, np.float32)
+    R, B = (c.shape if c.ndim == 2 else (0, 0))
+    tb = None if cost is None else _c(cost, np.float32)
+    b = np.zeros(1, np.int32)
+    th = np.zeros(1, np.float64)
+    rc = lib().svref_budget_from_costs(_p(c), int(B), int(R), int(B),
+                                       None if tb is None else _p(tb),
+                                       0 if tb is None else int(tb.size), _p(b), _p(th))
+    if rc != 0:
+        raise ValueError(f"svref_budget_from_costs returned {rc}")
+    return int(b[0]), float(th[0])
 
 
 def acceptance_stats(accept_len, verify_len, block):

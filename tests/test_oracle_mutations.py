@@ -63,6 +63,13 @@ CASES = [
     ("estimator drops a slope step instead of halving it",
      "while (e->slope + step < 0.0 && halvings < 8) {", "while (false) {",
      ["test_oracle_estimator.py::test_halving_keeps_the_slope_non_negative"]),
+    ("budget prices the rows without the bonus rows", "const double th = tau / (double)cost[b + R];",
+     "const double th = tau / (double)cost[b];",
+     ["test_oracle_budget.py::test_linear_cost_closed_form"]),
+    ("budget stops at the first descent", "if (th > best) {", "if (th > best && b == best_b + 1) {",
+     ["test_oracle_budget.py::test_global_argmax_not_first_descent"]),
+    ("budget ties go to the larger budget", "if (th > best) {", "if (th >= best) {",
+     ["test_oracle_budget.py::test_ties_take_the_smaller_budget"]),
 ]
 
 
