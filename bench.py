@@ -143,6 +143,18 @@ def make_inputs(torch, B, nsets: int, workload: str = "c3"):
             vl, qo, _ = B.plan_windows(conf, budget, want_survival=False)
         torch.cuda.synchronize()
         extra["planner_us"] = round((time.perf_counter() - t0) / 20 * 1e6, 2)
+        # the budget a synthetic staircase step-cost table would pick (graph
+        # tiers of 512 packed rows, +25 % per tier); the step keeps its budget
+        tiers = torch.arange(R * (nb - 1) + R + 1, device=dev, dtype=torch.float32) // 512
+        cost = (1.0 + 0.25 * tiers).contiguous()
+        B.plan_budget(conf, cost)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(20):
+            bsel, _ = B.plan_budget(conf, cost)
+        torch.cuda.synchronize()
+        extra["plan_budget_us"] = round((time.perf_counter() - t0) / 20 * 1e6, 2)
+        extra["cost_table_budget"] = int(bsel.item())
         extra["_verify_len"] = vl  # the windows, for the step's acceptance statistics
         rows = min(budget, R * (nb - 1)) + R
     else:

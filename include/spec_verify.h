@@ -162,6 +162,28 @@ int32_t spec_verify_plan_windows(const float* confidence, int64_t ld_conf, int32
                                  int32_t* qo_indptr, float* survival, void* workspace,
                                  size_t workspace_bytes, sv_stream_t stream);
 
+/* Verify budget from a step-cost table (TensorRT-LLM PR #17056, description:
+ * the planner's budget is a global argmax of tau/cost over a profiled
+ * step-cost table, not a first descent, because the table is a staircase;
+ * without a profiled table it does not trim).  Survivals and their rank order
+ * are spec_verify_plan_windows's.  For b in [0, R*B]: tau(b) = R + the b best
+ * survivals (fp64), the step packs b + R verify rows (bonus rows included), and
+ * Theta(b) = tau(b) / cost[b + R]; the smallest b with the largest Theta wins.
+ *   confidence [R, ld_conf] fp32, device (as spec_verify_plan_windows)
+ *   cost       [ncost] fp32, device: step cost by packed verify row count; NULL
+ *              or ncost 0: no table.  ncost must reach R*B + R + 1.
+ *   budget     [1] int32, device, written: the budget; R*B when there is no
+ *              table or it is equal over [R, R*B + R]; -1 when a cost in that
+ *              range is non-positive or non-finite
+ *   theta      [1] fp64, device, written (NULL: skipped): Theta(budget), 0 with
+ *              no table, NaN with an invalid one
+ * R*B must be at most 4096.  One workgroup, no host synchronisation: the
+ * budget stays on the device.  Errors (host-side checks, returned before any
+ * launch): SV_ERR_SHAPE, SV_ERR_NULL. */
+int32_t spec_verify_plan_budget(const float* confidence, int64_t ld_conf, int32_t num_requests,
+                                int32_t block, const float* cost, int32_t ncost, int32_t* budget,
+                                double* theta, sv_stream_t stream);
+
 /* Accepted prefix from per-row accept bytes (greedy accept with precomputed
  * argmax ids, DFLASH-through-DSpark commit note): accept_len[r] = first j <
  * min(gamma_r, verify_cap[r]) with accepted[s_r + j] == 0, else that bound. */

@@ -32,7 +32,7 @@ EXPORTS = [
     "spec_verify_status_string", "spec_verify_last_error", "spec_verify_profile_enable",
     "spec_verify_profile_read", "spec_verify_profile_reset", "spec_verify_acceptance_stats",
     "spec_verify_estimator_state_doubles", "spec_verify_estimator_init",
-    "spec_verify_estimator_predict", "spec_verify_estimator_observe",
+    "spec_verify_estimator_predict", "spec_verify_estimator_observe", "spec_verify_plan_budget",
 ]
 
 
@@ -67,6 +67,8 @@ def load(path: str = LIB_PATH):
     L.spec_verify_rejection_sample.restype = i32
     L.spec_verify_plan_windows.argtypes = [P, i64, i32, i32, i32, P, P, P, P, sz, P]
     L.spec_verify_plan_windows.restype = i32
+    L.spec_verify_plan_budget.argtypes = [P, i64, i32, i32, P, i32, P, P, P]
+    L.spec_verify_plan_budget.restype = i32
     L.spec_verify_accept_prefix.argtypes = [P, P, i32, P, P, P]
     L.spec_verify_accept_prefix.restype = i32
     L.spec_verify_acceptance_stats.argtypes = [P, P, i32, i32, P, P]
@@ -320,6 +322,22 @@ def plan_windows(confidence: torch.Tensor, budget: int, want_survival: bool = Tr
                                          _ptr(surv), _ptr(ws), ws.numel(), _stream())
     _check(rc)
     return vl, qo, surv
+
+
+def plan_budget(confidence: torch.Tensor, cost: Optional[torch.Tensor]):
+    """Verify budget maximising tau/cost over a step-cost table
+    (spec_verify_plan_budget): (budget int32 [1], theta fp64 [1]), both on the
+    device.  cost None: no table (no trim)."""
+    conf = _dev(confidence, torch.float32, "confidence")
+    R, B = conf.shape
+    tb = _dev(cost, torch.float32, "cost")
+    budget = torch.empty(1, dtype=torch.int32, device=conf.device)
+    theta = torch.empty(1, dtype=torch.float64, device=conf.device)
+    rc = load().spec_verify_plan_budget(_ptr(conf), B, R, B, _ptr(tb),
+                                        0 if tb is None else tb.numel(), _ptr(budget),
+                                        _ptr(theta), _stream())
+    _check(rc)
+    return budget, theta
 
 
 def accept_prefix(accepted: torch.Tensor, qo_indptr: torch.Tensor,

@@ -317,6 +317,23 @@ int32_t spec_verify_plan_windows(const float* confidence, int64_t ld_conf, int32
   return check_launch("planner");
 }
 
+int32_t spec_verify_plan_budget(const float* confidence, int64_t ld_conf, int32_t num_requests,
+                                int32_t block, const float* cost, int32_t ncost, int32_t* budget,
+                                double* theta, sv_stream_t stream) {
+  if (num_requests < 0 || block < 0 || ncost < 0) return fail(SV_ERR_SHAPE, "negative size");
+  const int64_t n = (int64_t)num_requests * block;
+  if (n > sv::kBudgetMaxKeys) return fail(SV_ERR_SHAPE, "num_requests * block must be <= 4096");
+  if (!budget) return fail(SV_ERR_NULL, "budget is NULL");
+  if (n > 0 && !confidence) return fail(SV_ERR_NULL, "confidence is NULL");
+  if (num_requests > 0 && ld_conf < block) return fail(SV_ERR_SHAPE, "ld_conf < block");
+  if (ncost > 0 && !cost) return fail(SV_ERR_NULL, "cost is NULL with ncost > 0");
+  if (cost && ncost > 0 && (int64_t)ncost < n + num_requests + 1)
+    return fail(SV_ERR_SHAPE, "cost table shorter than num_requests * block + num_requests + 1");
+  launch(3, sv::budget_kernel, dim3(1), dim3(sv::kPlanBlock), (hipStream_t)stream, confidence,
+         ld_conf, num_requests, block, ncost > 0 ? cost : nullptr, budget, theta);
+  return check_launch("cost-table budget");
+}
+
 int32_t spec_verify_accept_prefix(const uint8_t* accepted, const int32_t* qo_indptr,
                                   int32_t num_requests, const int32_t* verify_cap,
                                   int32_t* accept_len, sv_stream_t stream) {

@@ -84,6 +84,8 @@ __global__ void race_segment_kernel(VerifyArgs A);
 __global__ void race_finish_kernel(VerifyArgs A);
 __global__ void build_out_kernel(VerifyArgs A, BuildOutArgs B);
 __global__ void plan_kernel(PlanArgs A);
+__global__ void budget_kernel(const float* conf, int64_t ld_conf, int32_t R, int32_t B,
+                              const float* cost, int32_t* budget, double* theta);
 __global__ void accept_prefix_kernel(const uint8_t* accepted, const int32_t* qo, int32_t R,
                                      const int32_t* verify_cap, int32_t* accept_len);
 __global__ void acceptance_stats_kernel(const int32_t* accept_len, const int32_t* verify_len,
@@ -99,6 +101,7 @@ __global__ void est_observe_kernel(const double* feature, const int32_t* accept_
 constexpr int kRowBlock = SV_BLOCK;
 constexpr int kRowPassPerCU = 4;     // row-pass workgroups resident per CU (LDS and VGPR bound)
 constexpr int kPlanBlock = 1024;
+constexpr int kBudgetMaxKeys = 4096; // drafted positions a cost-table budget search sorts in LDS
 constexpr size_t kRowRecBytes = 64;
 constexpr int kEstMaxBlock = 64;     // estimator positions per request
 constexpr int kEstRefit = 100;       // estimator observe calls per refit

@@ -171,6 +171,116 @@ __global__ __launch_bounds__(kPB) void plan_kernel(PlanArgs A) {
   if (tid == 0) A.qo_indptr[R] = carry;
 }
 
+// Verify budget from a step-cost table (TensorRT-LLM PR #17056, description:
+// the budget is a global argmax of tau/cost over a profiled step-cost table,
+// since the table is a staircase; no profiled table, no trim).  tau(b) = R +
+// the b best survivals in the planner's rank order; budget b packs b + R
+// verify rows, so Theta(b) = tau(b) / cost[b + R]; the smallest b with the
+// largest Theta wins.  One workgroup: the planner's survival keys sorted in
+// LDS (bitonic), the survivals in rank order summed by a block scan (fp64),
+// and a block argmax.  A table equal over [R, R*B + R], or none, gives R*B;
+// a non-positive or non-finite cost in that range gives budget -1.
+__global__ __launch_bounds__(kPB) void budget_kernel(const float* conf, int64_t ld_conf, int32_t R,
+                                                     int32_t B, const float* cost, int32_t* budget,
+                                                     double* theta) {
+  __shared__ uint64_t keys[kBudgetMaxKeys];
+  __shared__ double wtot[kPW];
+  __shared__ double wth[kPW];
+  __shared__ int wb[kPW];
+  __shared__ int bad_s, flat_s;
+  const int tid = threadIdx.x, w = wave_id(), l = lane_id();
+  const int n = R * B;
+  int np = 1;
+  while (np < n) np <<= 1;
+
+  for (int r = tid; r < R; r += kPB) {
+    float acc = 1.0f;
+    for (int j = 0; j < B; ++j) {
+      float cf = conf[(size_t)r * ld_conf + j];
+      cf = (cf > 0.0f) ? (cf < 1.0f ? cf : 1.0f) : 0.0f;
+      acc = (j == 0) ? cf : __fmul_rn(acc, cf);
+      const uint32_t sb = __float_as_uint(acc);
+      keys[j * R + r] = ((uint64_t)(~sb) << 32) | (uint64_t)(uint32_t)(j * R + r);
+    }
+  }
+  for (int t = n + tid; t < np; t += kPB) keys[t] = ~0ull;  // padding sorts last
+  if (tid == 0) { bad_s = 0; flat_s = 1; }
+  __syncthreads();
+  if (cost) {
+    const float c0 = cost[R];
+    for (int t = R + tid; t <= n + R; t += kPB) {
+      const float c = cost[t];
+      if (!(c > 0.0f) || !isfinite(c)) atomicOr(&bad_s, 1);
+      if (c != c0) atomicAnd(&flat_s, 0);
+    }
+  }
+  // ascending keys = (S desc, j asc, r asc)
+  for (int k = 2; k <= np; k <<= 1) {
+    for (int jj = k >> 1; jj > 0; jj >>= 1) {
+      for (int i = tid; i < np; i += kPB) {
+        const int o = i ^ jj;
+        if (o > i) {
+          const uint64_t a = keys[i], b = keys[o];
+          if ((a > b) == ((i & k) == 0)) { keys[i] = b; keys[o] = a; }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  __syncthreads();
+  // thread t holds ranks [t * C, t * C + C): their survivals' sum, then a block scan
+  const int C = (n + kPB - 1) / kPB;
+  double loc = 0.0;
+  for (int c = 0; c < C; ++c) {
+    const int i = tid * C + c;
+    if (i < n) loc += (double)__uint_as_float(~(uint32_t)(keys[i] >> 32));
+  }
+  const double incl = wave_scan_dpp(loc);
+  if (l == 63) wtot[w] = incl;
+  __syncthreads();
+  double base = 0.0;
+  for (int q = 0; q < w; ++q) base += wtot[q];
+  double pre = (double)R + base + (incl - loc);  // tau of the budget before this thread's ranks
+  double best_th = -1.0;
+  int best_b = 0x7FFFFFFF;
+  if (cost) {
+    if (tid == 0) { best_th = (double)R / (double)cost[R]; best_b = 0; }
+    for (int c = 0; c < C; ++c) {
+      const int i = tid * C + c;
+      if (i >= n) break;
+      pre += (double)__uint_as_float(~(uint32_t)(keys[i] >> 32));
+      const double th = pre / (double)cost[i + 1 + R];
+      if (th > best_th) { best_th = th; best_b = i + 1; }
+    }
+  }
+  // block argmax: larger Theta, then smaller budget
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    const double ot = __shfl_xor(best_th, d, 64);
+    const int ob = __shfl_xor(best_b, d, 64);
+    if (ot > best_th || (ot == best_th && ob < best_b)) { best_th = ot; best_b = ob; }
+  }
+  if (l == 0) { wth[w] = best_th; wb[w] = best_b; }
+  __syncthreads();
+  if (tid == 0) {
+    double bt = wth[0];
+    int bb = wb[0];
+    for (int q = 1; q < kPW; ++q)
+      if (wth[q] > bt || (wth[q] == bt && wb[q] < bb)) { bt = wth[q]; bb = wb[q]; }
+    if (cost && bad_s) {
+      bb = -1;
+      bt = __builtin_nan("");
+    } else if (!cost || flat_s) {
+      bb = n;
+      double tau = (double)R;
+      for (int q = 0; q < kPW; ++q) tau += wtot[q];
+      bt = cost ? tau / (double)cost[n + R] : 0.0;
+    }
+    *budget = bb;
+    if (theta) *theta = bt;
+  }
+}
+
 // One wave per request: accept_len = first j < min(gamma, cap) with a zero byte.
 __global__ __launch_bounds__(256) void accept_prefix_kernel(const uint8_t* accepted,
                                                             const int32_t* qo, int32_t R,

@@ -1,0 +1,76 @@
+"""GPU parity of spec_verify_plan_budget against the oracle's cost-table budget."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import svref
+from tests.gpu_common import progress
+
+pytestmark = pytest.mark.gpu
+
+
+def staircase(rng, n_rows, steps):
+    edges = np.sort(rng.choice(np.arange(1, n_rows + 1), size=min(steps, n_rows), replace=False))
+    cost = np.full(n_rows + 1, 1.0)
+    for e in edges:
+        cost[e:] += rng.uniform(0.05, 0.6)
+    return cost.astype(np.float32)
+
+
+def oracle_thetas(conf, cost):
+    """Theta of every budget from the oracle's planner (for near-tie checks)."""
+    R, B = conf.shape
+    _, _, surv = svref.plan_windows(conf, 0)
+    keys = sorted(((-float(surv[r, j]), j, r) for r in range(R) for j in range(B)))
+    tau = float(R)
+    th = [tau / float(cost[R])]
+    for b, (ns, _, _) in enumerate(keys, start=1):
+        tau += -ns
+        th.append(tau / float(cost[b + R]))
+    return np.array(th)
+
+
+@pytest.mark.parametrize("R,B,seed", [(1, 1, 0), (3, 5, 1), (40, 7, 2), (256, 16, 3),
+                                      (1000, 4, 4), (64, 64, 5), (4096, 1, 6)])
+def test_plan_budget_matches_oracle(R, B, seed):
+    from rejection_sampling_amd import binding as Bd
+    rng = np.random.default_rng(seed)
+    conf = (1 / (1 + np.exp(-rng.normal(1, 1.5, (R, B)))) * 0.95 ** np.arange(B)).astype(np.float32)
+    conf[rng.random((R, B)) < 0.02] = np.nan
+    cost = staircase(rng, R * B + R, int(rng.integers(1, 40)))
+    progress(f"plan budget R={R} B={B}")
+    b_g, th_g = Bd.plan_budget(torch.from_numpy(conf).cuda(), torch.from_numpy(cost).cuda())
+    b_g, th_g = int(b_g.item()), float(th_g.item())
+    b_o, th_o = svref.budget_from_costs(conf, cost)
+    ths = oracle_thetas(conf, cost)
+    top = np.sort(ths)[-2:]
+    if len(top) < 2 or top[1] - top[0] > 1e-9 * top[1]:
+        assert b_g == b_o
+    else:  # near tie: any budget within rounding of the maximum is correct
+        assert ths[b_g] >= ths.max() * (1 - 1e-12)
+    assert th_g == pytest.approx(ths[b_g], rel=1e-12)
+
+
+def test_plan_budget_special_tables():
+    from rejection_sampling_amd import binding as Bd
+    conf = np.full((1, 8), 0.9, np.float32)
+    cost = np.array([1.0, 1.0, 1.0, 1.6, 1.6, 1.6, 1.6, 1.65, 1.65, 1.65], np.float32)
+    b, _ = Bd.plan_budget(torch.from_numpy(conf).cuda(), torch.from_numpy(cost).cuda())
+    assert int(b.item()) == 8 == svref.budget_from_costs(conf, cost)[0]
+    conf2 = np.array([[0.5, 0.0, 0.0, 0.0]], np.float32)
+    cost2 = np.array([1.0, 1.0, 1.0, 1.0, 1.0, 2.0], np.float32)
+    b, th = Bd.plan_budget(torch.from_numpy(conf2).cuda(), torch.from_numpy(cost2).cuda())
+    assert int(b.item()) == 1 and float(th.item()) == 1.5
+    conf3 = np.full((6, 4), 0.01, np.float32)
+    b, th = Bd.plan_budget(torch.from_numpy(conf3).cuda(), None)
+    assert int(b.item()) == 24 and float(th.item()) == 0.0
+    flat = np.full(31, 3.0, np.float32)
+    b, _ = Bd.plan_budget(torch.from_numpy(conf3).cuda(), torch.from_numpy(flat).cuda())
+    assert int(b.item()) == 24
+    bad = np.ones(31, np.float32)
+    bad[10] = 0.0
+    b, th = Bd.plan_budget(torch.from_numpy(conf3).cuda(), torch.from_numpy(bad).cuda())
+    assert int(b.item()) == -1 and np.isnan(float(th.item()))
+    with pytest.raises(RuntimeError):
+        Bd.plan_budget(torch.from_numpy(conf3).cuda(), torch.ones(20, device="cuda"))
+    torch.cuda.synchronize()
