@@ -105,6 +105,17 @@ def test_host_validation_without_gpu(lib):
     assert lib.spec_verify_estimator_init(fake, 65, None) == -2
     assert lib.spec_verify_estimator_init(None, 8, None) == -1
     assert lib.spec_verify_estimator_state_doubles(8) == 6 + 5 * 8
+    # cost-table budget: more than 4096 positions, a table too short, NULL budget,
+    # a NULL table with entries
+    c = ctypes.c_void_p
+    lib.spec_verify_plan_budget.argtypes = [c, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, c,
+                                            ctypes.c_int32, c, c, c]
+    assert lib.spec_verify_plan_budget(fake, 64, 65, 64, fake, 5000, fake, None, None) == -2
+    assert lib.spec_verify_plan_budget(fake, 4, 3, 4, fake, 15, fake, None, None) == -2
+    assert b"cost table" in lib.spec_verify_last_error()
+    assert lib.spec_verify_plan_budget(fake, 4, 3, 4, fake, 16, None, None, None) == -1
+    assert lib.spec_verify_plan_budget(fake, 4, 3, 4, None, 16, fake, None, None) == -1
+    assert lib.spec_verify_plan_budget(fake, 2, 3, 4, fake, 16, fake, None, None) == -2
 
 
 def test_workspace_query_grows_with_rows(lib):
