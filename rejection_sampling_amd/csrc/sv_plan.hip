@@ -176,14 +176,15 @@ __global__ __launch_bounds__(kPB) void plan_kernel(PlanArgs A) {
 // since the table is a staircase; no profiled table, no trim).  tau(b) = R +
 // the b best survivals in the planner's rank order; budget b packs b + R
 // verify rows, so Theta(b) = tau(b) / cost[b + R]; the smallest b with the
-// largest Theta wins.  One workgroup: the planner's survival keys sorted in
-// LDS (bitonic), the survivals in rank order summed by a block scan (fp64),
-// and a block argmax.  A table equal over [R, R*B + R], or none, gives R*B;
+// largest Theta wins.  One workgroup: the survivals sorted in LDS (bitonic,
+// 32-bit: tau depends on the values only, so the planner's index tie-break
+// among equal survivals needs no place in the key), summed in that order by a
+// block scan (fp64), and a block argmax.  A table equal over [R, R*B + R], or none, gives R*B;
 // a non-positive or non-finite cost in that range gives budget -1.
 __global__ __launch_bounds__(kPB) void budget_kernel(const float* conf, int64_t ld_conf, int32_t R,
                                                      int32_t B, const float* cost, int32_t* budget,
                                                      double* theta) {
-  __shared__ uint64_t keys[kBudgetMaxKeys];
+  __shared__ uint32_t keys[kBudgetMaxKeys];  // ~bits(S): ascending = S descending
   __shared__ double wtot[kPW];
   __shared__ double wth[kPW];
   __shared__ int wb[kPW];
@@ -199,11 +200,10 @@ __global__ __launch_bounds__(kPB) void budget_kernel(const float* conf, int64_t 
       float cf = conf[(size_t)r * ld_conf + j];
       cf = (cf > 0.0f) ? (cf < 1.0f ? cf : 1.0f) : 0.0f;
       acc = (j == 0) ? cf : __fmul_rn(acc, cf);
-      const uint32_t sb = __float_as_uint(acc);
-      keys[j * R + r] = ((uint64_t)(~sb) << 32) | (uint64_t)(uint32_t)(j * R + r);
+      keys[j * R + r] = ~__float_as_uint(acc);  // acc >= +0: bits order = value order
     }
   }
-  for (int t = n + tid; t < np; t += kPB) keys[t] = ~0ull;  // padding sorts last
+  for (int t = n + tid; t < np; t += kPB) keys[t] = 0xFFFFFFFFu;  // padding sorts last
   if (tid == 0) { bad_s = 0; flat_s = 1; }
   __syncthreads();
   if (cost) {
@@ -214,14 +214,23 @@ __global__ __launch_bounds__(kPB) void budget_kernel(const float* conf, int64_t 
       if (c != c0) atomicAnd(&flat_s, 0);
     }
   }
-  // ascending keys = (S desc, j asc, r asc)
+  // np <= 4 * kPB: every pair of a stage is disjoint from the others, so each
+  // thread loads its (up to four) pairs first and then writes them back
   for (int k = 2; k <= np; k <<= 1) {
     for (int jj = k >> 1; jj > 0; jj >>= 1) {
-      for (int i = tid; i < np; i += kPB) {
-        const int o = i ^ jj;
-        if (o > i) {
-          const uint64_t a = keys[i], b = keys[o];
-          if ((a > b) == ((i & k) == 0)) { keys[i] = b; keys[o] = a; }
+      uint32_t av[4], bv[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int i = tid + m * kPB, o = i ^ jj;
+        av[m] = bv[m] = 0u;
+        if (i < np && o > i) { av[m] = keys[i]; bv[m] = keys[o]; }
+      }
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int i = tid + m * kPB, o = i ^ jj;
+        if (i < np && o > i && (av[m] > bv[m]) == ((i & k) == 0)) {
+          keys[i] = bv[m];
+          keys[o] = av[m];
         }
       }
       __syncthreads();
@@ -233,7 +242,7 @@ __global__ __launch_bounds__(kPB) void budget_kernel(const float* conf, int64_t 
   double loc = 0.0;
   for (int c = 0; c < C; ++c) {
     const int i = tid * C + c;
-    if (i < n) loc += (double)__uint_as_float(~(uint32_t)(keys[i] >> 32));
+    if (i < n) loc += (double)__uint_as_float(~keys[i]);
   }
   const double incl = wave_scan_dpp(loc);
   if (l == 63) wtot[w] = incl;
@@ -248,7 +257,7 @@ __global__ __launch_bounds__(kPB) void budget_kernel(const float* conf, int64_t 
     for (int c = 0; c < C; ++c) {
       const int i = tid * C + c;
       if (i >= n) break;
-      pre += (double)__uint_as_float(~(uint32_t)(keys[i] >> 32));
+      pre += (double)__uint_as_float(~keys[i]);
       const double th = pre / (double)cost[i + 1 + R];
       if (th > best_th) { best_th = th; best_b = i + 1; }
     }
