@@ -214,28 +214,51 @@ __global__ __launch_bounds__(kPB) void budget_kernel(const float* conf, int64_t 
       if (c != c0) atomicAnd(&flat_s, 0);
     }
   }
-  // np <= 4 * kPB: every pair of a stage is disjoint from the others, so each
-  // thread loads its (up to four) pairs first and then writes them back
+  // Bitonic sort with the keys in registers: thread t owns i = t + m * kPB
+  // (np <= 4 * kPB) and computes each stage's new value of its own elements.
+  // The partner i ^ jj is in the same thread for jj >= kPB, in the same wave
+  // for jj < 64 (a shuffle), and otherwise read through LDS between barriers.
+  uint32_t kv[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int i = tid + m * kPB;
+    kv[m] = i < np ? keys[i] : 0xFFFFFFFFu;
+  }
   for (int k = 2; k <= np; k <<= 1) {
     for (int jj = k >> 1; jj > 0; jj >>= 1) {
-      uint32_t av[4], bv[4];
+      uint32_t pv[4];
+      if (jj >= kPB) {
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int i = tid + m * kPB, o = i ^ jj;
-        av[m] = bv[m] = 0u;
-        if (i < np && o > i) { av[m] = keys[i]; bv[m] = keys[o]; }
-      }
+        for (int m = 0; m < 4; ++m) pv[m] = kv[m ^ (jj / kPB)];
+      } else if (jj >= 64) {
+        __syncthreads();  // the previous readers of keys are done
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int i = tid + m * kPB, o = i ^ jj;
-        if (i < np && o > i && (av[m] > bv[m]) == ((i & k) == 0)) {
-          keys[i] = bv[m];
-          keys[o] = av[m];
+        for (int m = 0; m < 4; ++m)
+          if (tid + m * kPB < np) keys[tid + m * kPB] = kv[m];
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const int i = tid + m * kPB;
+          pv[m] = i < np ? keys[i ^ jj] : 0xFFFFFFFFu;
         }
+      } else {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) pv[m] = (uint32_t)__shfl_xor((int)kv[m], jj, 64);
       }
-      __syncthreads();
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int i = tid + m * kPB;
+        const bool keep_min = ((i & k) == 0) == ((i & jj) == 0);  // ascending run, lower index
+        const uint32_t lo = kv[m] < pv[m] ? kv[m] : pv[m];
+        const uint32_t hi = kv[m] < pv[m] ? pv[m] : kv[m];
+        if (i < np) kv[m] = keep_min ? lo : hi;
+      }
     }
   }
+  __syncthreads();
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+    if (tid + m * kPB < np) keys[tid + m * kPB] = kv[m];
   __syncthreads();
   // thread t holds ranks [t * C, t * C + C): their survivals' sum, then a block scan
   const int C = (n + kPB - 1) / kPB;
