@@ -109,10 +109,24 @@ struct RowDist {
   int32_t a = -1;        /* argmax, lowest index among ties          */
   double lse = 0;        /* log sum exp(x / T_eff)                   */
   std::vector<int32_t> kept;  /* N in order (value desc, index asc)  */
+  std::vector<int32_t> order; /* the row order pi (sampled rows)     */
   std::vector<double> p;      /* dense p_v over the vocabulary       */
   double zk = 0, zn = 0;      /* masses of K and N relative to max   */
+  int32_t n_lo = 0, n_hi = 0; /* kept counts over the near-tie band  */
   bool near_topp = false;
 };
+
+/* Kept count of the nucleus walk for a mass target: positions t < kc whose
+ * prefix mass before them is below the target (pi_0 is counted whenever the
+ * target is positive). */
+int32_t nucleus_count(const std::vector<double>& w, int32_t kc, double target) {
+  double c = 0.0;
+  int32_t n = 0;
+  for (int32_t t = 0; t < kc; ++t) {
+    if (c < target) { ++n; c += w[t]; } else { break; }
+  }
+  return n;
+}
 
 void build_row(const void* logits, int32_t dtype, int64_t ld, int64_t row, int32_t V,
                const Params& prm, RowDist& out) {
@@ -141,8 +155,10 @@ void build_row(const void* logits, int32_t dtype, int64_t ld, int64_t row, int32
   if (prm.greedy) {
     /* O2: one-hot at the argmax. */
     out.kept.push_back(a);
+    out.order.assign(1, a);
     out.p[a] = 1.0;
     out.zk = out.zn = 1.0;
+    out.n_lo = out.n_hi = 1;
     return;
   }
 
@@ -170,22 +186,19 @@ void build_row(const void* logits, int32_t dtype, int64_t ld, int64_t row, int32
   int32_t n = kc;
   if (!(prm.P < 1.0f)) {
     n = kc;                        /* off (P >= 1 or NaN) */
+    out.n_lo = out.n_hi = n;
   } else if (!(prm.P > 0.0f)) {
     n = 1;                         /* P <= 0 keeps the top token */
+    out.n_lo = out.n_hi = n;
   } else {
-    double target = (double)prm.P * zk;
-    double c = 0.0;
-    n = 0;
-    for (int32_t t = 0; t < kc; ++t) {
-      if (c < target) { ++n; c += w[t]; } else { break; }
-    }
-    /* Near-tie margins at the last kept and the first dropped position. */
-    double c_before_last = 0.0;
-    for (int32_t t = 0; t + 1 < n; ++t) c_before_last += w[t];
-    double c_after_last = c_before_last + w[n - 1];
-    double margin = target - c_before_last;
-    if (n < kc) margin = std::min(margin, c_after_last - target);
-    if (margin < 1e-6 * zk) out.near_topp = true;
+    const double target = (double)prm.P * zk;
+    n = nucleus_count(w, kc, target);
+    /* Near-tie band: the kept counts a target anywhere within 1e-6 * Z_K of
+     * P * Z_K would give.  The row is a top-p near tie when they differ. */
+    const double band = 1e-6 * zk;
+    out.n_lo = std::max(1, nucleus_count(w, kc, target - band));
+    out.n_hi = nucleus_count(w, kc, target + band);
+    out.near_topp = out.n_lo != out.n_hi;
   }
 
   /* O7: probabilities on N. */
@@ -193,7 +206,8 @@ void build_row(const void* logits, int32_t dtype, int64_t ld, int64_t row, int32
   for (int32_t t = 0; t < n; ++t) zn += w[t];
   out.zn = zn;
   out.kept.assign(pi.begin(), pi.begin() + n);
-  for (int32_t t = 0; t < n; ++t) out.p[pi[t]] = w[t] / zn;
+  out.order.swap(pi);
+  for (int32_t t = 0; t < n; ++t) out.p[out.order[t]] = w[t] / zn;
 }
 
 Params request_params(const svref_sampling* sp, int32_t r) {
@@ -267,7 +281,9 @@ int32_t svref_build_target_probs(const void* logits, int32_t dtype, int64_t ld_l
                                  int32_t num_requests, const svref_sampling* sp, double* probs,
                                  int64_t ld_probs, double* row_max, int32_t* row_argmax,
                                  double* row_lse, int32_t* kept_count, int32_t* kept_idx,
-                                 int32_t kmax, double* row_zn, uint8_t* row_flags) {
+                                 int32_t kmax, double* row_zn, uint8_t* row_flags,
+                                 double* row_zk, int32_t* kept_lo, int32_t* kept_hi,
+                                 int32_t* order_idx) {
   if (!logits || !sp || vocab <= 0 || ld_logits < vocab) return -1;
   if (dtype != SVREF_F32 && dtype != SVREF_BF16) return -3;
   if (!check_layout(qo_indptr, num_requests, num_rows)) return -2;
@@ -281,11 +297,18 @@ int32_t svref_build_target_probs(const void* logits, int32_t dtype, int64_t ld_l
       if (row_argmax) row_argmax[i] = d.a;
       if (row_lse) row_lse[i] = d.lse;
       if (row_zn) row_zn[i] = d.zn;
+      if (row_zk) row_zk[i] = d.zk;
       if (row_flags) row_flags[i] = d.near_topp ? SVREF_ROW_NEAR_TOPP : 0;
       if (kept_count) kept_count[i] = (int32_t)d.kept.size();
+      if (kept_lo) kept_lo[i] = d.n_lo;
+      if (kept_hi) kept_hi[i] = d.n_hi;
       if (kept_idx) {
         for (int32_t t = 0; t < kmax; ++t)
           kept_idx[(int64_t)i * kmax + t] = t < (int32_t)d.kept.size() ? d.kept[t] : -1;
+      }
+      if (order_idx) {
+        for (int32_t t = 0; t < kmax; ++t)
+          order_idx[(int64_t)i * kmax + t] = t < (int32_t)d.order.size() ? d.order[t] : -1;
       }
       if (probs) {
         for (int32_t v = 0; v < vocab; ++v) probs[(int64_t)i * ld_probs + v] = d.p[v];
@@ -301,7 +324,7 @@ int32_t svref_rejection_sample(const void* logits, int32_t dtype, int64_t ld_log
                                const float* draft_probs, int64_t ld_q, const int32_t* verify_cap,
                                const svref_sampling* sp, int32_t* accept_len, int32_t* out_tokens,
                                int32_t* next_token, uint8_t* row_flags, double* row_ratio,
-                               double* row_u) {
+                               double* row_u, double* row_zk, double* row_zn) {
   if (!logits || !sp || !draft_tokens || !accept_len || !out_tokens || !next_token) return -1;
   if (vocab <= 0 || ld_logits < vocab) return -2;
   if (dtype != SVREF_F32 && dtype != SVREF_BF16) return -3;
@@ -319,6 +342,8 @@ int32_t svref_rejection_sample(const void* logits, int32_t dtype, int64_t ld_log
     if (row_flags) row_flags[i] = 0;
     if (row_ratio) row_ratio[i] = nan;
     if (row_u) row_u[i] = nan;
+    if (row_zk) row_zk[i] = nan;
+    if (row_zn) row_zn[i] = nan;
   }
 
   RowDist d;
@@ -354,6 +379,8 @@ int32_t svref_rejection_sample(const void* logits, int32_t dtype, int64_t ld_log
         acc = (dtok == d.a);
       } else {
         build_row(logits, dtype, ld_logits, i, vocab, prm, d);
+        if (row_zk) row_zk[i] = d.zk;
+        if (row_zn) row_zn[i] = d.zn;
         if (d.near_topp) fl |= SVREF_ROW_NEAR_TOPP;
         double pd = d.p[dtok];
         double q = (double)draft_probs[(int64_t)i * ld_q + dtok];
@@ -377,6 +404,10 @@ int32_t svref_rejection_sample(const void* logits, int32_t dtype, int64_t ld_log
      * rejection, the target distribution after a full (or capped) accept. */
     const int32_t is = s + L;
     build_row(logits, dtype, ld_logits, is, vocab, prm, d);
+    if (!prm.greedy) {
+      if (row_zk) row_zk[is] = d.zk;
+      if (row_zn) row_zn[is] = d.zn;
+    }
     int32_t sample;
     uint8_t sfl = SVREF_ROW_SAMPLED;
     if (prm.greedy) {

@@ -80,24 +80,35 @@ double svref_uniform_race(uint64_t seed, uint32_t request_id, uint32_t position,
  *   row_max, row_argmax, row_lse (lse at T_eff = T, or 1 on greedy rows)
  *   kept_count [rows], kept_idx [rows, kmax] in order (value desc, index asc),
  *   row_zn    [rows] mass of the kept set relative to the row max (Z_N)
- *   row_flags [rows] SVREF_ROW_NEAR_TOPP where the top-p boundary is a near tie */
+ *   row_flags [rows] SVREF_ROW_NEAR_TOPP where the top-p boundary is a near tie
+ *   row_zk    [rows] mass of the top-k set relative to the row max (Z_K)
+ *   kept_lo, kept_hi [rows] the near-tie band of the kept count: the smallest
+ *             and largest counts a top-p target anywhere within 1e-6 * Z_K of
+ *             P * Z_K gives (equal to kept_count off the band); the row is
+ *             flagged SVREF_ROW_NEAR_TOPP exactly when they differ
+ *   order_idx [rows, kmax] the first kmax ids of the row order (value desc,
+ *             index asc); greedy rows hold the argmax only */
 int32_t svref_build_target_probs(const void* logits, int32_t dtype, int64_t ld_logits,
                                  int32_t num_rows, int32_t vocab, const int32_t* qo_indptr,
                                  int32_t num_requests, const svref_sampling* sp, double* probs,
                                  int64_t ld_probs, double* row_max, int32_t* row_argmax,
                                  double* row_lse, int32_t* kept_count, int32_t* kept_idx,
-                                 int32_t kmax, double* row_zn, uint8_t* row_flags);
+                                 int32_t kmax, double* row_zn, uint8_t* row_flags,
+                                 double* row_zk, int32_t* kept_lo, int32_t* kept_hi,
+                                 int32_t* order_idx);
 
 /* The verify step.  draft_probs may be NULL only when every request is greedy.
  * verify_cap may be NULL.  row_ratio / row_u (diagnostics, may be NULL) get the
- * ratio and the uniform of each tested draft row (NaN elsewhere). */
+ * ratio and the uniform of each tested draft row (NaN elsewhere); row_zk /
+ * row_zn (may be NULL) the masses Z_K and Z_N of every sampled row the step
+ * builds (NaN elsewhere). */
 int32_t svref_rejection_sample(const void* logits, int32_t dtype, int64_t ld_logits,
                                int32_t vocab, const int32_t* qo_indptr, int32_t num_requests,
                                int32_t num_rows, const int32_t* draft_tokens,
                                const float* draft_probs, int64_t ld_q, const int32_t* verify_cap,
                                const svref_sampling* sp, int32_t* accept_len, int32_t* out_tokens,
                                int32_t* next_token, uint8_t* row_flags, double* row_ratio,
-                               double* row_u);
+                               double* row_u, double* row_zk, double* row_zn);
 
 /* Confidence planner: survival cumprod (fp32), rank (S desc, j asc, r asc),
  * budget -> verify_len [R], qo_indptr [R+1], survival [R, block] (may be NULL). */

@@ -67,10 +67,10 @@ def lib():
         L.svref_uniform_race.argtypes = [u64, u32, u32, u32, u32]
         L.svref_uniform_race.restype = ctypes.c_double
         L.svref_build_target_probs.argtypes = [P, i32, i64, i32, i32, P, i32, P, P, i64, P, P, P,
-                                               P, P, i32, P, P]
+                                               P, P, i32, P, P, P, P, P, P]
         L.svref_build_target_probs.restype = i32
         L.svref_rejection_sample.argtypes = [P, i32, i64, i32, P, i32, i32, P, P, i64, P, P, P, P,
-                                             P, P, P, P]
+                                             P, P, P, P, P, P]
         L.svref_rejection_sample.restype = i32
         L.svref_plan_windows.argtypes = [P, i64, i32, i32, i32, P, P, P]
         L.svref_plan_windows.restype = i32
@@ -153,16 +153,22 @@ def build_target_probs(logits, qo, T, k=None, P=None, rid=None, pos0=None, seed=
         "kept_count": np.zeros(rows, np.int32),
         "row_zn": np.zeros(rows, np.float64),
         "row_flags": np.zeros(rows, np.uint8),
+        "row_zk": np.zeros(rows, np.float64),
+        "kept_lo": np.zeros(rows, np.int32),
+        "kept_hi": np.zeros(rows, np.int32),
     }
     kept_idx = np.zeros((rows, kmax), np.int32) if kmax > 0 else None
+    order_idx = np.zeros((rows, kmax), np.int32) if kmax > 0 else None
     probs = np.zeros((rows, V), np.float64) if want_probs else None
     rc = lib().svref_build_target_probs(
         _p(logits), _dt(logits), V, rows, V, _p(qo), R, ctypes.byref(prm.s), _p(probs), V,
         _p(out["row_max"]), _p(out["row_argmax"]), _p(out["row_lse"]), _p(out["kept_count"]),
-        _p(kept_idx), kmax, _p(out["row_zn"]), _p(out["row_flags"]))
+        _p(kept_idx), kmax, _p(out["row_zn"]), _p(out["row_flags"]), _p(out["row_zk"]),
+        _p(out["kept_lo"]), _p(out["kept_hi"]), _p(order_idx))
     if rc != 0:
         raise ValueError(f"svref_build_target_probs returned {rc}")
     out["kept_idx"] = kept_idx
+    out["order_idx"] = order_idx
     out["probs"] = probs
     return out
 
@@ -184,12 +190,15 @@ def rejection_sample(logits, qo, drafts, q, T, k=None, P=None, rid=None, pos0=No
         "row_flags": np.zeros(rows, np.uint8),
         "row_ratio": np.zeros(rows, np.float64),
         "row_u": np.zeros(rows, np.float64),
+        "row_zk": np.zeros(rows, np.float64),
+        "row_zn": np.zeros(rows, np.float64),
     }
     ldq = q.shape[1] if q is not None else V
     rc = lib().svref_rejection_sample(
         _p(logits), _dt(logits), V, V, _p(qo), R, rows, _p(drafts), _p(q), ldq, _p(cap),
         ctypes.byref(prm.s), _p(out["accept_len"]), _p(out["out_tokens"]),
-        _p(out["next_token"]), _p(out["row_flags"]), _p(out["row_ratio"]), _p(out["row_u"]))
+        _p(out["next_token"]), _p(out["row_flags"]), _p(out["row_ratio"]), _p(out["row_u"]),
+        _p(out["row_zk"]), _p(out["row_zn"]))
     if rc != 0:
         raise ValueError(f"svref_rejection_sample returned {rc}")
     return out
@@ -395,6 +404,8 @@ def parallel_rejection_sample(logits, qo, drafts, q, T, k, P, rid, pos0, seed, v
         "row_flags": np.zeros(rows, np.uint8),
         "row_ratio": np.full(rows, np.nan),
         "row_u": np.full(rows, np.nan),
+        "row_zk": np.full(rows, np.nan),
+        "row_zn": np.full(rows, np.nan),
     }
     spans = _shards(qo, threads * 4) if requests is None else [(int(r), int(r) + 1)
                                                                 for r in requests]
@@ -408,7 +419,7 @@ def parallel_rejection_sample(logits, qo, drafts, q, T, k, P, rid, pos0, seed, v
                                _sub(pos0, r0, r1), seed, _sub(verify_cap, r0, r1))
         res["accept_len"][r0:r1] = out["accept_len"]
         res["next_token"][r0:r1] = out["next_token"]
-        for key in ("out_tokens", "row_flags", "row_ratio", "row_u"):
+        for key in ("out_tokens", "row_flags", "row_ratio", "row_u", "row_zk", "row_zn"):
             res[key][s0:s1] = out[key]
 
     with ThreadPoolExecutor(threads) as ex:

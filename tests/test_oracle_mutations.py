@@ -70,6 +70,22 @@ CASES = [
      ["test_oracle_budget.py::test_global_argmax_not_first_descent"]),
     ("budget ties go to the larger budget", "if (th > best) {", "if (th >= best) {",
      ["test_oracle_budget.py::test_ties_take_the_smaller_budget"]),
+    ("ratio near-tie band ten times too narrow", "std::fabs(u - ratio) < 1e-5",
+     "std::fabs(u - ratio) < 1e-6", ["test_oracle_near_ties.py::test_ratio_band"]),
+    ("ratio near-tie flag on one side only", "std::fabs(u - ratio) < 1e-5", "(u - ratio) < 1e-5",
+     ["test_oracle_near_ties.py::test_ratio_band"]),
+    ("top-p band ten times too wide", "const double band = 1e-6 * zk;",
+     "const double band = 1e-5 * zk;", ["test_oracle_near_ties.py::test_topp_band"]),
+    ("top-p band absolute instead of relative to Z_K", "const double band = 1e-6 * zk;",
+     "const double band = 1e-6;", ["test_oracle_near_ties.py::test_topp_band_is_relative_to_zk"]),
+    ("top-p band looks below the target only", "out.n_hi = nucleus_count(w, kc, target + band);",
+     "out.n_hi = n;", ["test_oracle_near_ties.py::test_topp_band"]),
+    ("top-p flag always set", "out.near_topp = out.n_lo != out.n_hi;", "out.near_topp = true;",
+     ["test_oracle_near_ties.py::test_topp_band"]),
+    ("race near-tie band ten times too wide", "(best - second) / best < 1e-6",
+     "(best - second) / best < 1e-5", ["test_oracle_near_ties.py::test_race_band"]),
+    ("race forgets the replaced best", "      second = best;\n      best = key;",
+     "      best = key;", ["test_oracle_near_ties.py::test_race_band_sees_a_replaced_best"]),
 ]
 
 
