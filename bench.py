@@ -13,8 +13,11 @@ serve a repeat.
 
 Prints one JSON line: whole-job rows/s; the roofline of the dominant kernel
 (the row pass: algorithmic bytes = rows x V x 2 per launch, over its mean
-launch time from HIP events recorded on the call's stream); and the CPU
-oracle timed on a bounded sample of the same workload on one host core.
+launch time from HIP events recorded on the call's stream), with the same
+bytes over the whole step beside it; the CPU oracle timed on one host core on
+a bounded sample of the GPU's own timed inputs (copied back from the device);
+and, at the headline configuration, the dense-output target-probs build as a
+context figure.
 """
 from __future__ import annotations
 
@@ -186,9 +189,13 @@ def make_inputs(torch, B, nsets: int, workload: str = "c3"):
         Tt = torch.full((R,), 0.8, device=dev)
         kt = torch.zeros(R, device=dev, dtype=torch.int32)
         pt = torch.full((R,), 0.95, device=dev)
-    params = B.Params(Tt.float().contiguous(), kt.contiguous(), pt.float().contiguous(), rid,
-                      pos0, SEED if workload == "c3" else SEED + int(workload[1:]),
-                      all_greedy=(workload == "c1"))
+    # the caller knows its requests' sampling values on the host: the hints
+    # (all greedy, kept sets bounded by top-k) come from them, read once here
+    params = B.Params.from_host(Tt.float().cpu().numpy(), kt.cpu().numpy(),
+                                pt.float().cpu().numpy(), rid.cpu().numpy().astype("uint32"),
+                                pos0.cpu().numpy().astype("uint32"),
+                                SEED if workload == "c3" else SEED + int(workload[1:]))
+    extra["_qo_host"] = qo.cpu().numpy()
     scale = {"c1": 2.0, "c2": 3.0, "c3": 4.0, "c4": 3.0, "c5": 4.0}[workload]
     sets = []
     for s in range(nsets):
@@ -218,26 +225,35 @@ def make_inputs(torch, B, nsets: int, workload: str = "c3"):
     return sets, qo, params, rows, V, extra
 
 
-def cpu_baseline(n_requests: int):
-    """The CPU oracle as it stands, single-threaded on one host core, on a
-    bounded sample of the same workload (n_requests x 8 rows, V 248320)."""
+def cpu_baseline(torch, logits, q, drafts, qo_host, params, gpu_out, n_requests: int):
+    """The CPU oracle as it stands, single-threaded on one host core, on the
+    first n_requests requests of the GPU's own timed input set (the same bytes:
+    bf16 logits, fp32 draft distributions and drafted tokens copied back from
+    the device).  The oracle's outputs on that sample are also compared with
+    the GPU's, as a check that the timed kernels computed the same step."""
     import numpy as np
     from oracle import svref
-    from rejection_sampling_amd import workloads as W
-    w = W.workload3(num_requests=n_requests)
-    qo = w.qo_indptr()
-    # inputs (untimed): draft distributions and drafted tokens by the oracle
-    q = svref.parallel_draft_probs(w.draft_logits, qo, w.temperature, w.top_k, w.top_p,
-                                   w.request_id, w.position0, w.seed)
-    d = svref.sample_probs(q, qo, w.request_id, w.position0, w.seed, tag=2)
+    n = min(n_requests, len(qo_host) - 1)
+    r1 = int(qo_host[n])
+    lg = logits[:r1].contiguous()
+    lg_host = (lg.view(torch.int16).cpu().numpy().view(np.uint16) if lg.dtype == torch.bfloat16
+               else lg.cpu().numpy())
+    q_host = q[:r1].cpu().numpy() if q is not None else None
+    d_host = drafts[:r1].cpu().numpy()
+    T, k, P = (a[:n] for a in params.host)
+    rid = params.rid[:n].cpu().numpy().view(np.uint32)
+    pos0 = params.pos0[:n].cpu().numpy().view(np.uint32)
+    qo = qo_host[:n + 1].astype(np.int32)
+    seed = params.s.seed
     try:  # the timed call runs pinned to one core
         os.sched_setaffinity(0, {sorted(os.sched_getaffinity(0))[0]})
     except (AttributeError, OSError):
         pass
     t0 = time.perf_counter()
-    svref.rejection_sample(w.logits, qo, d, q, w.temperature, w.top_k, w.top_p, w.request_id,
-                           w.position0, w.seed)
+    ref = svref.rejection_sample(lg_host, qo, d_host, q_host, T, k, P, rid, pos0, seed)
     dt = time.perf_counter() - t0
+    same = sum(int(ref["accept_len"][r] == gpu_out["accept_len"][r] and
+                   ref["next_token"][r] == gpu_out["next_token"][r]) for r in range(n))
     cpu = "unknown"
     try:
         with open("/proc/cpuinfo") as f:
@@ -247,10 +263,30 @@ def cpu_baseline(n_requests: int):
                     break
     except OSError:
         pass
-    return {"value": round(w.num_rows / dt, 3), "unit": "rows/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n_requests} requests x {BLOCK} rows of the {ROWS} x {VOCAB} bf16 "
-                      f"workload (same recipe, generated on the host), one call, "
-                      f"{dt:.2f} s on 1 core of {os.cpu_count()} ({cpu})"}
+    return {"value": round(r1 / dt, 3), "unit": "rows/s", "cores": 1, "kind": "oracle",
+            "sample": f"the first {n} requests ({r1} rows) of the GPU's first timed input set, "
+                      f"copied back from the device, one call, {dt:.2f} s on 1 core of "
+                      f"{os.cpu_count()} ({cpu}); oracle and GPU agree on accept_len and "
+                      f"next_token for {same} of {n} requests"}
+
+
+def build_dense_figure(torch, B, logits, qo, params, V, steps=10):
+    """spec_verify_build_target_probs with the dense fp32 probability output
+    (read the bf16 logits, write fp32 [rows, V]): the like-for-like context of
+    the pages' target-probs build time."""
+    rows = logits.shape[0]
+    for _ in range(2):
+        B.build_target_probs(logits, qo, params, want_probs=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        B.build_target_probs(logits, qo, params, want_probs=True)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    nbytes = rows * V * (2 + 4)
+    return {"call": "spec_verify_build_target_probs with dense fp32 probs", "ms": round(ms, 4),
+            "bytes": nbytes, "GB_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
 
 
 def main():
@@ -264,6 +300,8 @@ def main():
                          "same line for the other four configurations")
     ap.add_argument("--cpu-requests", type=int, default=80,
                     help="requests in the CPU-baseline sample (0 skips it)")
+    ap.add_argument("--no-dense", action="store_true",
+                    help="skip the dense target-probs build figure")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 512 MiB device copy (counter calibration)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -292,6 +330,7 @@ def main():
     print(f"[bench] building {wl} inputs ({args.sets} logits sets)", file=sys.stderr, flush=True)
     sets, qo, params, rows, V, extra = make_inputs(torch, B, args.sets, wl)
     windows = extra.pop("_verify_len", None)
+    qo_host = extra.pop("_qo_host")
     out = {
         "accept_len": torch.empty(R, dtype=torch.int32, device="cuda"),
         "out_tokens": torch.empty(rows, dtype=torch.int32, device="cuda"),
@@ -299,7 +338,9 @@ def main():
         "row_flags": torch.empty(rows, dtype=torch.uint8, device="cuda"),
     }
 
-    calls = [B.PreparedRejectionSample(logits, qo, drafts, q, params, out=out)
+    # rows that may take the multi-pass exact path go first (host-side schedule)
+    order = B.heavy_first_order(qo_host, params, V)
+    calls = [B.PreparedRejectionSample(logits, qo, drafts, q, params, out=out, row_order=order)
              for logits, q, drafts in sets]
 
     def step(i):
@@ -375,7 +416,15 @@ def main():
         torch.cuda.synchronize()
         extra["estimator_us"] = round((time.perf_counter() - t0) / 20 * 1e6, 2)
 
-    cpu = cpu_baseline(args.cpu_requests) if (args.cpu_requests > 0 and wl == "c3") else None
+    cpu = None
+    if args.cpu_requests > 0 and wl == "c3":
+        calls[0]()
+        torch.cuda.synchronize()
+        gout = {k: v.cpu().numpy() for k, v in out.items()}
+        logits0, q0, d0 = sets[0]
+        cpu = cpu_baseline(torch, logits0, q0, d0, qo_host, params, gout, args.cpu_requests)
+    if wl == "c3" and not args.no_dense:
+        extra["build_dense"] = build_dense_figure(torch, B, sets[0][0], qo, params, V)
     config = {"workload": f"{wl}: {R} requests, {rows} rows x {V} vocab; {desc}",
               "rows": rows, "requests": R, "vocab": V,
               "draft_probs": "dense fp32, gathered" if wl != "c1" else "none (all greedy)",
@@ -400,6 +449,9 @@ def main():
                      "traffic": measured_traffic() if wl == "c3" else None,
                      "kernel": "row_pass_kernel", "kernel_ms": round(kern_ms, 5),
                      "algorithmic_bytes": alg_bytes,
+                     # the same bytes over the whole step (every launch of the call)
+                     "step_achieved": round(alg_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+                     "step_frac": round(alg_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                      "finalize_ms": round(ms_fz / max(n_fz, 1), 5),
                      "race_ms": round((ms_rs + ms_rf) / max(n_fz, 1), 5)},
         "cpu_baseline": cpu,

@@ -26,8 +26,11 @@
  * host can see (null pointer, bad size, bad dtype, workspace too small, HIP
  * launch error).  spec_verify_status_string() names a code and
  * spec_verify_last_error() gives a thread-local message for the last failure.
- * Contract violations inside device data (a non-monotone qo_indptr, a
- * qo_indptr[R] different from num_rows) are undefined.
+ * Contract violations inside device data (a qo_indptr that does not start at
+ * 0, decreases, or does not end at num_rows) are undefined on the fast path;
+ * with SV_CHECK the call checks the layout on the device first and refuses a
+ * violation instead of reading through it (TensorRT-LLM PR #17056, commit
+ * notes on the layout assertions: refuse rather than degrade silently).
  */
 #ifndef SPEC_VERIFY_H
 #define SPEC_VERIFY_H
@@ -52,17 +55,34 @@ enum {
   SV_ERR_HIP = -5        /* a HIP call failed (message in spec_verify_last_error) */
 };
 
-/* Hints in sv_sampling.flags. */
+/* Flags in sv_sampling.flags. */
 enum {
   SV_ALL_GREEDY = 1u, /* every request is greedy: draft_probs may be NULL. The
                          host-side all-greedy skip of the consolidation study,
                          section 6 (sampling prep is inert at temperature 0). */
-  SV_LIST_BOUNDED = 2u /* every sampled request has 0 < top_k <= 4096, so no
+  SV_CHECK = 2u,      /* check qo_indptr on the device before the call's
+                         kernels (one extra single-workgroup launch): qo[0] =
+                         0, non-decreasing, qo[R] = num_rows.  The int32 at
+                         byte 0 of the workspace receives 0 or the violated
+                         SV_LAYOUT_* bits.  A violated layout is refused, not
+                         read: spec_verify_rejection_sample then writes
+                         accept_len 0, next_token -1 and out_tokens -1 /
+                         row_flags 0 on every row, spec_verify_build_target_probs
+                         writes row_max / row_lse NaN, row_argmax -1,
+                         kept_count -1, kept_idx -1 and leaves probs untouched. */
+  SV_LIST_BOUNDED = 4u /* every sampled request has 0 < top_k <= 4096, so no
                          correction or bonus token is sampled over the whole
                          vocabulary: the call skips the two launches that split
                          such samples over workgroups.  A performance hint only:
                          a request that breaks it is still sampled exactly (by
                          one workgroup). */
+};
+
+/* Bits of the layout check word (SV_CHECK, spec_verify_check_layout). */
+enum {
+  SV_LAYOUT_START = 1, /* qo_indptr[0] != 0            */
+  SV_LAYOUT_ORDER = 2, /* qo_indptr decreases somewhere */
+  SV_LAYOUT_END = 4    /* qo_indptr[R] != num_rows      */
 };
 
 /* Row flag bits written by spec_verify_rejection_sample (row_flags). */
@@ -79,7 +99,7 @@ typedef struct {
   const uint32_t* request_id;/* [R] device or NULL (r): Philox counter word         */
   const uint32_t* position0; /* [R] device or NULL (0): absolute position of row 0  */
   uint64_t seed;             /* Philox4x32-10 key                                   */
-  uint32_t flags;            /* SV_ALL_GREEDY | SV_LIST_BOUNDED                     */
+  uint32_t flags;            /* SV_ALL_GREEDY | SV_CHECK | SV_LIST_BOUNDED          */
   const int32_t* row_order;  /* [num_rows] device or NULL (natural order): the order
                                 in which rows are scheduled, a permutation of
                                 0..num_rows-1 (anything else leaves the results
@@ -91,8 +111,10 @@ typedef struct {
 
 /* Bytes of device workspace the calls below need for these sizes (block: the
  * planner's positions per request, 0 when the planner is not used).  The
- * workspace is scratch: its contents need no initialisation and are
- * meaningless after the call. */
+ * workspace is scratch: its contents need no initialisation.  After a call,
+ * the int32 at byte 0 holds the SV_CHECK layout word (when the call had
+ * SV_CHECK) and spec_verify_row_diagnostics can read the per-row records;
+ * the rest is meaningless.  It must be 256-byte aligned. */
 size_t spec_verify_workspace_bytes(int32_t num_rows, int32_t vocab, int32_t num_requests,
                                    int32_t block);
 
@@ -191,6 +213,27 @@ int32_t spec_verify_accept_prefix(const uint8_t* accepted, const int32_t* qo_ind
                                   int32_t num_requests, const int32_t* verify_cap,
                                   int32_t* accept_len, sv_stream_t stream);
 
+/* Layout check of a packed qo_indptr (the check SV_CHECK runs inside a call),
+ * for callers that build qo_indptr on the device (e.g. with
+ * spec_verify_plan_windows) and want the verdict before any verify call:
+ * writes 0 or the violated SV_LAYOUT_* bits to error_word (one int32, device).
+ * Reads qo_indptr[0..R] only.  One workgroup, no synchronisation. */
+int32_t spec_verify_check_layout(const int32_t* qo_indptr, int32_t num_requests,
+                                 int32_t num_rows, int32_t* error_word, sv_stream_t stream);
+
+/* Diagnostics of the decision quantities: after spec_verify_rejection_sample or
+ * spec_verify_build_target_probs on this workspace (and before another call
+ * reuses it), copy per row the top-k mass Z_K (over the whole row when top-k is
+ * off), the kept mass Z_N (both relative to exp(m / T)), p(d) of a tested draft
+ * as the ratio test used it, and the row mode (0 unused, 1 greedy, 2 kept list,
+ * 3 whole row, 4 kept range, 5 exact path).  Every output [num_rows] device
+ * array may be NULL.  These are the values a caller compares against a
+ * reference to check that the device decided with enough precision; they are
+ * not needed for verification itself. */
+int32_t spec_verify_row_diagnostics(const void* workspace, size_t workspace_bytes,
+                                    int32_t num_rows, double* row_zk, double* row_zn,
+                                    double* row_pd, int32_t* row_mode, sv_stream_t stream);
+
 /* Acceptance and trim statistics of one verify step (TensorRT-LLM PR #17056,
  * commit note on the trim-regret metric: a trimmed request that accepted its
  * entire window was still alive at the cut, so the cut cost acceptance;
@@ -258,7 +301,8 @@ const char* spec_verify_last_error(void);
  * read() waits for them and returns, per kernel id, the launch count and the
  * summed milliseconds since the last reset.  Kernel ids: 0 row pass, 1 request
  * finalize, 2 target-probs writer, 3 planner, 4 accept prefix, 5 race
- * segments, 6 race finish, 7 acceptance statistics and estimator. */
+ * segments, 6 race finish, 7 acceptance statistics and estimator, 8 layout
+ * check, 9 row diagnostics. */
 int32_t spec_verify_profile_enable(int32_t on);
 int32_t spec_verify_profile_read(int32_t kernel_id, int64_t* launches, double* total_ms);
 int32_t spec_verify_profile_reset(void);

@@ -425,3 +425,48 @@ def parallel_rejection_sample(logits, qo, drafts, q, T, k, P, rid, pos0, seed, v
     with ThreadPoolExecutor(threads) as ex:
         list(ex.map(job, spans))
     return res
+
+
+def parallel_build(logits, qo, T, k, P, rid=None, pos0=None, seed=0, kmax=0, prob_rows=None,
+                   threads=None):
+    """Oracle target-distribution build over every request, sharded by request
+    on a thread pool (each shard one plain call).  Per-row outputs for all
+    rows; dense probabilities only for the rows listed in ``prob_rows`` (a
+    dict row -> fp64 [V] array), which bounds the memory at large shapes."""
+    threads = threads or min(16, os.cpu_count() or 1)
+    qo = np.asarray(qo, np.int32)
+    rows, V = logits.shape
+    res = {
+        "row_max": np.zeros(rows, np.float64), "row_argmax": np.zeros(rows, np.int32),
+        "row_lse": np.zeros(rows, np.float64), "kept_count": np.zeros(rows, np.int32),
+        "row_zn": np.zeros(rows, np.float64), "row_flags": np.zeros(rows, np.uint8),
+        "row_zk": np.zeros(rows, np.float64), "kept_lo": np.zeros(rows, np.int32),
+        "kept_hi": np.zeros(rows, np.int32),
+        "kept_idx": np.zeros((rows, kmax), np.int32) if kmax else None,
+        "order_idx": np.zeros((rows, kmax), np.int32) if kmax else None,
+    }
+    want = set() if prob_rows is None else set(int(i) for i in prob_rows)
+    probs = {}
+
+    def job(span):
+        r0, r1 = span
+        for a in range(r0, r1):
+            sa, sb = int(qo[a]), int(qo[a + 1])
+            if sb <= sa:
+                continue
+            dense = any(i in want for i in range(sa, sb))
+            out = build_target_probs(logits[sa:sb], qo[a:a + 2] - qo[a], _sub(T, a, a + 1),
+                                     _sub(k, a, a + 1), _sub(P, a, a + 1), _sub(rid, a, a + 1),
+                                     _sub(pos0, a, a + 1), seed, want_probs=dense, kmax=kmax)
+            for key in res:
+                if res[key] is not None:
+                    res[key][sa:sb] = out[key]
+            if dense:
+                for i in range(sa, sb):
+                    if i in want:
+                        probs[i] = out["probs"][i - sa].copy()
+
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(job, _shards(qo, threads * 4)))
+    res["probs_rows"] = probs
+    return res

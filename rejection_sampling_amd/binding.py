@@ -19,12 +19,15 @@ LIB_PATH = os.path.join(HERE, "libspecverify.so")
 
 SV_F32, SV_BF16 = 0, 1
 SV_ALL_GREEDY = 1
-SV_LIST_BOUNDED = 2
+SV_CHECK = 2
+SV_LIST_BOUNDED = 4
+LAYOUT_START, LAYOUT_ORDER, LAYOUT_END = 1, 2, 4
 LIST_CAP = 4096  # kept-set entries a row can list (top-k bound of SV_LIST_BOUNDED)
 TOPK_SINGLE_PASS = 256  # largest top-k the streaming pass selects by itself
 ROW_ACCEPT, ROW_SAMPLED, ROW_RESID_EMPTY = 1, 2, 32
 KERNEL_IDS = {"row_pass": 0, "finalize": 1, "build_out": 2, "planner": 3, "accept_prefix": 4,
-              "race_segment": 5, "race_finish": 6, "acceptance_stats": 7}
+              "race_segment": 5, "race_finish": 6, "acceptance_stats": 7, "check_layout": 8,
+              "diagnostics": 9}
 
 EXPORTS = [
     "spec_verify_workspace_bytes", "spec_verify_build_target_probs",
@@ -33,6 +36,7 @@ EXPORTS = [
     "spec_verify_profile_read", "spec_verify_profile_reset", "spec_verify_acceptance_stats",
     "spec_verify_estimator_state_doubles", "spec_verify_estimator_init",
     "spec_verify_estimator_predict", "spec_verify_estimator_observe", "spec_verify_plan_budget",
+    "spec_verify_check_layout", "spec_verify_row_diagnostics",
 ]
 
 
@@ -69,6 +73,10 @@ def load(path: str = LIB_PATH):
     L.spec_verify_plan_windows.restype = i32
     L.spec_verify_plan_budget.argtypes = [P, i64, i32, i32, P, i32, P, P, P]
     L.spec_verify_plan_budget.restype = i32
+    L.spec_verify_check_layout.argtypes = [P, i32, i32, P, P]
+    L.spec_verify_check_layout.restype = i32
+    L.spec_verify_row_diagnostics.argtypes = [P, sz, i32, P, P, P, P, P]
+    L.spec_verify_row_diagnostics.restype = i32
     L.spec_verify_accept_prefix.argtypes = [P, P, i32, P, P, P]
     L.spec_verify_accept_prefix.restype = i32
     L.spec_verify_acceptance_stats.argtypes = [P, P, i32, i32, P, P]
@@ -139,11 +147,19 @@ def _stream():
 _ws_cache = {}
 
 
+def _device(device=None) -> torch.device:
+    """A device with its index filled in (the workspace cache key)."""
+    dev = torch.device(device or "cuda")
+    if dev.index is None:
+        dev = torch.device(dev.type, torch.cuda.current_device())
+    return dev
+
+
 def workspace(num_rows: int, vocab: int, num_requests: int, block: int = 0,
               device=None) -> torch.Tensor:
     """A cached device workspace of at least the queried size."""
     n = int(load().spec_verify_workspace_bytes(num_rows, vocab, num_requests, block))
-    dev = torch.device(device or "cuda")
+    dev = _device(device)
     cur = _ws_cache.get(dev)
     if cur is None or cur.numel() < n:
         cur = torch.empty(max(n, 1 << 20), dtype=torch.uint8, device=dev)
@@ -152,10 +168,16 @@ def workspace(num_rows: int, vocab: int, num_requests: int, block: int = 0,
 
 
 class Params:
-    """Per-request sampling values as device tensors (kept alive with the call)."""
+    """Per-request sampling values as device tensors (kept alive with the
+    call).  Nothing here reads device memory: the flags are the caller's
+    (all_greedy, list_bounded: hints the caller knows from its own host-side
+    request parameters; check: the device-side layout check of SV_CHECK).
+    Params.from_host() takes host arrays instead, derives the hints from them
+    and uploads the values once."""
 
     def __init__(self, temperature, top_k=None, top_p=None, request_id=None, position0=None,
-                 seed: int = 0, all_greedy: bool = False, list_bounded=None):
+                 seed: int = 0, all_greedy: bool = False, list_bounded: bool = False,
+                 check: bool = False):
         self.T = _dev(temperature, torch.float32, "temperature")
         self.k = _dev(top_k, torch.int32, "top_k")
         self.P = _dev(top_p, torch.float32, "top_p")
@@ -163,50 +185,68 @@ class Params:
         # the same bits
         self.rid = _dev(request_id, torch.int32, "request_id")
         self.pos0 = _dev(position0, torch.int32, "position0")
-        # one host copy of the values (here, never per call) for the hints
-        self._host = None
-        if self.T is not None:
-            R = self.T.numel()
-            Th = self.T.cpu()
-            kh = self.k.cpu() if self.k is not None else torch.zeros(R, dtype=torch.int32)
-            Ph = self.P.cpu() if self.P is not None else torch.ones(R)
-            self._host = (Th, kh, Ph)
-        if list_bounded is None:
-            # every sampled request keeps at most LIST_CAP tokens by top-k
-            if self._host is None:
-                list_bounded = True  # every request greedy
-            elif self.k is None:
-                list_bounded = False
-            else:
-                Th, kh, _ = self._host
-                sampled = Th > 0
-                list_bounded = bool(((kh[sampled] > 0) & (kh[sampled] <= LIST_CAP)).all())
-        flags = (SV_ALL_GREEDY if all_greedy else 0) | (SV_LIST_BOUNDED if list_bounded else 0)
+        self.host = None   # (T, k, P) host arrays when built by from_host
+        flags = ((SV_ALL_GREEDY if all_greedy else 0) | (SV_LIST_BOUNDED if list_bounded else 0) |
+                 (SV_CHECK if check else 0))
         self.s = Sampling(_ptr(self.T), _ptr(self.k), _ptr(self.P), _ptr(self.rid),
                           _ptr(self.pos0), int(seed) & ((1 << 64) - 1), flags, None)
 
-    def heavy_requests(self, vocab: int):
-        """Requests whose rows may take the multi-pass exact path: sampled,
-        top-k off with top-p on, or top-k above the single-pass limit."""
-        if self._host is None:
-            return None
-        Th, kh, Ph = self._host
-        k_off = (kh <= 0) | (kh >= vocab)
-        return (Th > 0) & ((k_off & (Ph < 1) & (Ph > 0)) | ((kh > TOPK_SINGLE_PASS) & ~k_off))
+    @classmethod
+    def from_host(cls, temperature, top_k=None, top_p=None, request_id=None, position0=None,
+                  seed: int = 0, device="cuda", check: bool = False):
+        """Build from host (numpy or CPU) arrays: every request greedy sets
+        SV_ALL_GREEDY, every sampled request with 0 < top_k <= 4096 sets
+        SV_LIST_BOUNDED.  The arrays are uploaded once, here."""
+        import numpy as np
+        T = np.ascontiguousarray(np.asarray(temperature, np.float32))
+        R = T.size
+        k = None if top_k is None else np.ascontiguousarray(np.asarray(top_k, np.int32))
+        P = None if top_p is None else np.ascontiguousarray(np.asarray(top_p, np.float32))
+        kk = np.zeros(R, np.int32) if k is None else k
+        all_greedy, list_bounded = sampling_hints(T, kk)
+        def up(a, dt):
+            return None if a is None else torch.from_numpy(np.ascontiguousarray(a, dt)).to(device)
+
+        def u32(a):  # uint32 values travel as int32 tensors with the same bits
+            return None if a is None else torch.from_numpy(
+                np.ascontiguousarray(a, np.uint32).view(np.int32)).to(device)
+        prm = cls(up(T, np.float32), up(k, np.int32), up(P, np.float32), u32(request_id),
+                  u32(position0), seed, all_greedy, list_bounded, check)
+        prm.host = (T, kk, np.ones(R, np.float32) if P is None else P)
+        return prm
 
 
-def row_order(qo_indptr: torch.Tensor, params: Params, vocab: int):
-    """Row schedule with the rows of heavy requests first (a device int32
-    permutation), or None when no reordering helps (none or all heavy)."""
-    heavy = params.heavy_requests(vocab)
-    if heavy is None or not bool(heavy.any()) or bool(heavy.all()):
+def sampling_hints(temperature, top_k):
+    """(all_greedy, list_bounded) from host values: no request samples (T > 0),
+    and every sampled request has 0 < top_k <= LIST_CAP."""
+    import numpy as np
+    T = np.asarray(temperature, np.float32)
+    k = np.asarray(top_k, np.int32)
+    sampled = T > 0
+    return (not bool(sampled.any()),
+            bool(((k[sampled] > 0) & (k[sampled] <= LIST_CAP)).all()))
+
+
+def heavy_first_order(qo_indptr, params: Params, vocab: int, device="cuda"):
+    """Row schedule (a device int32 permutation) with the rows of requests that
+    may take the multi-pass exact path first: sampled, top-k off with top-p
+    on, or top-k above the single-pass limit.  Computed on the host from the
+    host qo_indptr and the host values Params.from_host kept; None when no
+    reordering helps (no heavy request, or only heavy ones)."""
+    import numpy as np
+    if params.host is None:
+        raise ValueError("heavy_first_order needs Params.from_host (host sampling values)")
+    Th, kh, Ph = params.host
+    k_off = (kh <= 0) | (kh >= vocab)
+    heavy = (Th > 0) & ((k_off & (Ph < 1) & (Ph > 0)) | ((kh > TOPK_SINGLE_PASS) & ~k_off))
+    if not heavy.any() or heavy.all():
         return None
-    qo = qo_indptr.cpu().to(torch.int64)
-    rows = torch.arange(int(qo[-1]), dtype=torch.int64)
-    req = torch.searchsorted(qo[1:], rows, right=True)
+    qo = np.asarray(qo_indptr, np.int64)
+    rows = np.arange(int(qo[-1]), dtype=np.int64)
+    req = np.searchsorted(qo[1:], rows, side="right")
     first = heavy[req]
-    order = torch.cat([rows[first], rows[~first]]).to(torch.int32)
-    return order.to(qo_indptr.device)
+    order = np.concatenate([rows[first], rows[~first]]).astype(np.int32)
+    return torch.from_numpy(order).to(device)
 
 
 def build_target_probs(logits: torch.Tensor, qo_indptr: torch.Tensor, params: Params,
@@ -268,10 +308,11 @@ def rejection_sample(logits: torch.Tensor, qo_indptr: torch.Tensor, draft_tokens
 class PreparedRejectionSample:
     """rejection_sample with its arguments checked and marshalled once: each
     call is one foreign call on the stream current at construction.  The
-    tensors must stay alive and keep their shapes and storage."""
+    tensors must stay alive and keep their shapes and storage.  row_order
+    (device int32 [rows], e.g. from heavy_first_order) schedules the rows."""
 
     def __init__(self, logits, qo_indptr, draft_tokens, draft_probs, params: Params,
-                 verify_cap=None, out=None, reorder: bool = True):
+                 verify_cap=None, out=None, row_order: Optional[torch.Tensor] = None):
         dt = _logits(logits)
         rows, V = logits.shape
         qo = _dev(qo_indptr, torch.int32, "qo_indptr")
@@ -291,8 +332,10 @@ class PreparedRejectionSample:
             }
         ws = workspace(rows, V, R, 0, dev)
         ldq = draft_probs.stride(0) if draft_probs is not None else V
-        # this call's copy of the sampling block, with the heavy rows first
-        order = row_order(qo, params, V) if reorder else None
+        # this call's copy of the sampling block, with the caller's row order
+        order = _dev(row_order, torch.int32, "row_order")
+        if order is not None and order.numel() != rows:
+            raise ValueError("row_order must hold one entry per row")
         self._s = Sampling(*[getattr(params.s, f) for f, _ in Sampling._fields_])
         self._s.row_order = _ptr(order)
         self.out = out
@@ -338,6 +381,41 @@ def plan_budget(confidence: torch.Tensor, cost: Optional[torch.Tensor]):
                                         _ptr(theta), _stream())
     _check(rc)
     return budget, theta
+
+
+def check_layout(qo_indptr: torch.Tensor, num_rows: int) -> torch.Tensor:
+    """Device int32 [1]: 0, or the LAYOUT_* bits qo_indptr violates
+    (spec_verify_check_layout)."""
+    qo = _dev(qo_indptr, torch.int32, "qo_indptr")
+    word = torch.empty(1, dtype=torch.int32, device=qo.device)
+    _check(load().spec_verify_check_layout(_ptr(qo), qo.numel() - 1, int(num_rows), _ptr(word),
+                                           _stream()))
+    return word
+
+
+def row_diagnostics(num_rows: int, ws: Optional[torch.Tensor] = None, device=None):
+    """Per-row Z_K, Z_N, p(d) and mode recorded by the last call on the
+    workspace `ws` (default: this module's cached workspace of the device)."""
+    dev = _device(device)
+    ws = _ws_cache.get(dev) if ws is None else ws
+    if ws is None:
+        raise ValueError("no workspace: run a verify or build call first")
+    out = {"zk": torch.empty(num_rows, dtype=torch.float64, device=dev),
+           "zn": torch.empty(num_rows, dtype=torch.float64, device=dev),
+           "pd": torch.empty(num_rows, dtype=torch.float64, device=dev),
+           "mode": torch.empty(num_rows, dtype=torch.int32, device=dev)}
+    _check(load().spec_verify_row_diagnostics(_ptr(ws), ws.numel(), int(num_rows),
+                                              _ptr(out["zk"]), _ptr(out["zn"]), _ptr(out["pd"]),
+                                              _ptr(out["mode"]), _stream()))
+    return out
+
+
+def workspace_check_word(ws: Optional[torch.Tensor] = None, device=None) -> torch.Tensor:
+    """The SV_CHECK layout word of the last call on `ws` (a device view)."""
+    ws = _ws_cache.get(_device(device)) if ws is None else ws
+    if ws is None:
+        raise ValueError("no workspace: run a verify or build call first")
+    return ws[:4].view(torch.int32)
 
 
 def accept_prefix(accepted: torch.Tensor, qo_indptr: torch.Tensor,

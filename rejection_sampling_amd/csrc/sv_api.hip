@@ -31,8 +31,8 @@ struct Layout {
 
 Layout layout(int64_t rows, int64_t R, int64_t block) {
   Layout L;
-  L.rec = 0;
-  L.list = align256((size_t)rows * sizeof(sv::RowRec));
+  L.rec = sv::kWsHeader;  // bytes [0, 4): the layout check word of SV_CHECK
+  L.list = L.rec + align256((size_t)rows * sizeof(sv::RowRec));
   L.race_job = L.list + align256((size_t)rows * sv::kListCap * sizeof(sv::ListEntry));
   L.race_part = L.race_job + align256((size_t)R * sizeof(int32_t));
   L.keys = L.race_part + align256((size_t)R * sv::kMaxRaceSegs * sizeof(sv::RacePart));
@@ -57,8 +57,8 @@ struct Prof {
   struct Rec { int id; hipEvent_t a, b; };
   std::vector<Rec> pending;
   std::vector<hipEvent_t> pool;  // reused events (created once)
-  int64_t launches[8] = {};
-  double ms[8] = {};
+  int64_t launches[10] = {};
+  double ms[10] = {};
 };
 Prof& prof() {
   static Prof p;
@@ -192,7 +192,15 @@ static sv::VerifyArgs base_args(const void* logits, sv_dtype dt, int64_t ld, int
   A.list = (sv::ListEntry*)((char*)ws + L.list);
   A.race_job = (int32_t*)((char*)ws + L.race_job);
   A.race_part = (sv::RacePart*)((char*)ws + L.race_part);
+  A.check = (sp->flags & SV_CHECK) ? (const int32_t*)ws : nullptr;
   return A;
+}
+
+// SV_CHECK: the layout check writes the workspace's check word before the
+// call's kernels, which read it and refuse a failed layout.
+static int32_t launch_check(const int32_t* qo, int32_t R, int32_t rows, void* ws, hipStream_t s) {
+  launch(8, sv::check_layout_kernel, dim3(1), dim3(1024), s, qo, R, rows, (int32_t*)ws);
+  return check_launch("layout check");
 }
 
 int32_t spec_verify_build_target_probs(const void* logits, sv_dtype dt, int64_t ld_logits,
@@ -217,6 +225,7 @@ int32_t spec_verify_build_target_probs(const void* logits, sv_dtype dt, int64_t 
   sv::VerifyArgs A = base_args(logits, dt, ld_logits, vocab, qo_indptr, num_requests, num_rows,
                                sp, workspace);
   A.build = 1;
+  if (A.check && (rc = launch_check(qo_indptr, num_requests, num_rows, workspace, s))) return rc;
   launch(0, sv::row_pass_kernel, dim3(num_rows), dim3(sv::kRowBlock), s, A);
   if ((rc = check_launch("row pass"))) return rc;
   sv::BuildOutArgs B;
@@ -272,6 +281,7 @@ int32_t spec_verify_rejection_sample(const void* target_logits, sv_dtype dt, int
   if (!draft_probs) A.temperature = nullptr;  // SV_ALL_GREEDY: every request greedy
   A.race_segs = draft_probs ? race_segments(vocab, sp->flags) : 0;
   A.level = num_rows <= resident_row_workgroups() ? 1 : 0;
+  if (A.check && (rc = launch_check(qo_indptr, num_requests, num_rows, workspace, s))) return rc;
   if (num_rows > 0) launch(0, sv::row_pass_kernel, dim3(num_rows), dim3(sv::kRowBlock), s, A);
   if ((rc = check_launch("row pass"))) return rc;
   launch(1, sv::finalize_kernel, dim3(num_requests), dim3(sv::kRowBlock), s, A);
@@ -344,6 +354,30 @@ int32_t spec_verify_accept_prefix(const uint8_t* accepted, const int32_t* qo_ind
   launch(4, sv::accept_prefix_kernel, dim3((num_requests + 3) / 4), dim3(256), s, accepted,
          qo_indptr, num_requests, verify_cap, accept_len);
   return check_launch("accept prefix");
+}
+
+int32_t spec_verify_check_layout(const int32_t* qo_indptr, int32_t num_requests,
+                                 int32_t num_rows, int32_t* error_word, sv_stream_t stream) {
+  if (num_requests < 0 || num_rows < 0) return fail(SV_ERR_SHAPE, "negative size");
+  if (!qo_indptr || !error_word) return fail(SV_ERR_NULL, "qo_indptr / error_word are NULL");
+  launch(8, sv::check_layout_kernel, dim3(1), dim3(1024), (hipStream_t)stream, qo_indptr,
+         num_requests, num_rows, error_word);
+  return check_launch("layout check");
+}
+
+int32_t spec_verify_row_diagnostics(const void* workspace, size_t workspace_bytes,
+                                    int32_t num_rows, double* row_zk, double* row_zn,
+                                    double* row_pd, int32_t* row_mode, sv_stream_t stream) {
+  if (num_rows < 0) return fail(SV_ERR_SHAPE, "negative row count");
+  if (num_rows == 0) return SV_OK;
+  if (!workspace) return fail(SV_ERR_WORKSPACE, "workspace is NULL");
+  const Layout L = layout(num_rows, 0, 0);
+  if (workspace_bytes < L.list) return fail(SV_ERR_WORKSPACE, "workspace too small for the rows");
+  const int grid = (num_rows + 255) / 256 < 1024 ? (num_rows + 255) / 256 : 1024;
+  launch(9, sv::diagnostics_kernel, dim3(grid), dim3(256), (hipStream_t)stream,
+         (const sv::RowRec*)((const char*)workspace + L.rec), num_rows, row_zk, row_zn, row_pd,
+         row_mode);
+  return check_launch("row diagnostics");
 }
 
 int32_t spec_verify_acceptance_stats(const int32_t* accept_len, const int32_t* verify_len,
@@ -431,12 +465,12 @@ int32_t spec_verify_profile_reset(void) {
     p.pool.push_back(r.b);
   }
   p.pending.clear();
-  for (int k = 0; k < 8; ++k) { p.launches[k] = 0; p.ms[k] = 0.0; }
+  for (int k = 0; k < 10; ++k) { p.launches[k] = 0; p.ms[k] = 0.0; }
   return SV_OK;
 }
 
 int32_t spec_verify_profile_read(int32_t kernel_id, int64_t* launches, double* total_ms) {
-  if (kernel_id < 0 || kernel_id >= 8) return fail(SV_ERR_SHAPE, "kernel id out of range");
+  if (kernel_id < 0 || kernel_id >= 10) return fail(SV_ERR_SHAPE, "kernel id out of range");
   Prof& p = prof();
   std::lock_guard<std::mutex> g(p.mu);
   for (auto& r : p.pending) {

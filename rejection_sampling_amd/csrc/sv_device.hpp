@@ -72,10 +72,9 @@ struct RowRec {
   int32_t nb;     // kModeRange: ties at bkey that are kept (lowest ids)
   int32_t flags;
   float lse;      // log sum exp(x / T_eff) over the row (build path)
-  float pd;       // p(d) of the tested draft (diagnostic)
+  double pd;      // p(d) of the tested draft, as the ratio test used it
   int32_t sample;  // kRecSampled: token emitted when this row is the request's emit row
   int32_t tie_cut; // kRecTieCut: elements at bkey with a smaller id are the kept ties
-  int32_t pad;
 };
 static_assert(sizeof(RowRec) == 64, "RowRec layout");
 

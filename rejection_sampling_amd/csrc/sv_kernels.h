@@ -53,6 +53,10 @@ struct VerifyArgs {
   // every row-pass workgroup is resident at once: rows on one CU are kept
   // level by progress-based wave priorities
   int32_t level;
+  // layout check word written by check_layout_kernel earlier on the stream,
+  // or NULL: when it is nonzero the kernels refuse the call (no qo_indptr
+  // read, refused outputs written)
+  const int32_t* check;
 };
 
 struct BuildOutArgs {
@@ -78,6 +82,9 @@ struct PlanArgs {
   uint64_t* keys;        // workspace [R * block]
 };
 
+__global__ void check_layout_kernel(const int32_t* qo, int32_t R, int32_t rows, int32_t* word);
+__global__ void diagnostics_kernel(const RowRec* rec, int32_t rows, double* zk, double* zn,
+                                   double* pd, int32_t* mode);
 __global__ void row_pass_kernel(VerifyArgs A);
 __global__ void finalize_kernel(VerifyArgs A);
 __global__ void race_segment_kernel(VerifyArgs A);
@@ -103,6 +110,7 @@ constexpr int kRowPassPerCU = 4;     // row-pass workgroups resident per CU (LDS
 constexpr int kPlanBlock = 1024;
 constexpr int kBudgetMaxKeys = 4096; // drafted positions a cost-table budget search sorts in LDS
 constexpr size_t kRowRecBytes = 64;
+constexpr size_t kWsHeader = 256;    // workspace bytes before the row records (check word)
 constexpr int kEstMaxBlock = 64;     // estimator positions per request
 constexpr int kEstRefit = 100;       // estimator observe calls per refit
 constexpr int kEstStateBase = 6;     // estimator state doubles: 6 + 5 * block

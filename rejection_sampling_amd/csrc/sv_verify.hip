@@ -1134,12 +1134,13 @@ __device__ __forceinline__ void greedy_record(RowRec& out, float m, int a, bool 
     out.flags |= kRecTested;
     if (!d_ok) out.flags |= kRecBadDraft;
     if (d == a) out.flags |= kRecAccept;
-    out.pd = d == a ? 1.0f : 0.0f;
+    out.pd = d == a ? 1.0 : 0.0;
   }
 }
 
 template <int DT>
 __device__ __forceinline__ void row_pass(const VerifyArgs& A, RowShared& sh) {
+  if (A.check && *A.check != 0) return;  // refused: qo_indptr failed the layout check
   const int i = A.row_order ? A.row_order[blockIdx.x] : (int)blockIdx.x;
   if (i < 0 || i >= A.num_rows) return;
   const int tid = threadIdx.x;
@@ -1183,7 +1184,7 @@ __device__ __forceinline__ void row_pass(const VerifyArgs& A, RowShared& sh) {
 
   RowRec out = {};
   out.lse = 0.0f;
-  out.pd = 0.0f;
+  out.pd = 0.0;
   const bool need_sum_build = A.build != 0;
   StreamAcc acc;
 
@@ -1401,7 +1402,7 @@ __device__ __forceinline__ void row_pass(const VerifyArgs& A, RowShared& sh) {
 
   if (tested) {
     out.flags |= kRecTested;
-    out.pd = (float)pd;
+    out.pd = pd;
     if (!d_ok) {
       out.flags |= kRecBadDraft;
     } else {
@@ -1526,7 +1527,7 @@ __device__ __forceinline__ void resolve_pending(const VerifyArgs& A, int i, int 
   const uint32_t pos0 = A.position0 ? A.position0[r] : 0u;
   if (tested) {
     out.flags |= kRecTested;
-    out.pd = (float)pd;
+    out.pd = pd;
     if (!d_ok) {
       out.flags |= kRecBadDraft;
     } else {
@@ -2032,6 +2033,24 @@ template <int DT>
 __device__ __forceinline__ void finalize(const VerifyArgs& A, RowShared& sh) {
   const int r = blockIdx.x;
   const int tid = threadIdx.x;
+  if (A.check && *A.check != 0) {
+    // refused call: every request emits nothing; the rows are cleared in
+    // even shares per workgroup (qo_indptr is not trusted)
+    if (tid == 0) {
+      A.accept_len[r] = 0;
+      A.next_token[r] = -1;
+      if (A.race_segs > 0) A.race_job[r] = -1;
+    }
+    const int R = A.num_requests;
+    const int share = (A.num_rows + R - 1) / R;
+    const int lo = r * share;
+    const int hi = lo + share < A.num_rows ? lo + share : A.num_rows;
+    for (int i = lo + tid; i < hi; i += kBlock) {
+      A.out_tokens[i] = -1;
+      if (A.row_flags) A.row_flags[i] = 0;
+    }
+    return;
+  }
   const int s = A.qo[r], e = A.qo[r + 1];
   const int nr = e - s;
   if (nr <= 0) {
@@ -2226,6 +2245,18 @@ __device__ __forceinline__ void build_out(const VerifyArgs& A, const BuildOutArg
   const int i = blockIdx.x;
   const int tid = threadIdx.x;
   const int V = A.vocab;
+  if (A.check && *A.check != 0) {
+    // refused call: per-row outputs marked invalid, probabilities untouched
+    if (tid == 0) {
+      if (B.row_max) B.row_max[i] = __builtin_nanf("");
+      if (B.row_argmax) B.row_argmax[i] = -1;
+      if (B.row_lse) B.row_lse[i] = __builtin_nanf("");
+      if (B.kept_count) B.kept_count[i] = -1;
+    }
+    if (B.kept_idx)
+      for (int t = tid; t < B.kmax; t += kBlock) B.kept_idx[(size_t)i * B.kmax + t] = -1;
+    return;
+  }
   const int r = row_to_request(A.qo, A.num_requests, A.num_rows, i);
   if (A.rec[i].mode == kModePending) resolve_pending<DT>(A, i, r, i - A.qo[r], false, false, sh);
   const RowRec rr = A.rec[i];
@@ -2314,6 +2345,42 @@ __global__ __launch_bounds__(kBlock) void build_out_kernel(VerifyArgs A, BuildOu
   __shared__ RowShared sh;
   if (A.dtype == 1) build_out<1>(A, B, sh);
   else build_out<0>(A, B, sh);
+}
+
+// ------------------------------------------------------ layout check
+// qo_indptr against the packing contract: qo[0] = 0 (bit 1), non-decreasing
+// (bit 2), qo[R] = rows (bit 4).  One workgroup strides over the requests and
+// reads qo[0..R] only, so any contents are safe to check.
+__global__ __launch_bounds__(1024) void check_layout_kernel(const int32_t* qo, int32_t R,
+                                                            int32_t rows, int32_t* word) {
+  __shared__ int bad;
+  if (threadIdx.x == 0) bad = 0;
+  __syncthreads();
+  int mine = 0;
+  for (int r = threadIdx.x; r < R; r += blockDim.x)
+    if (qo[r + 1] < qo[r]) mine = 2;
+  if (threadIdx.x == 0) {
+    if (qo[0] != 0) mine |= 1;
+    if (qo[R] != rows) mine |= 4;
+  }
+  if (mine) atomicOr(&bad, mine);
+  __syncthreads();
+  if (threadIdx.x == 0) *word = bad;
+}
+
+// ------------------------------------------------------ row diagnostics
+// The decision quantities the last call recorded per row: Z_K, Z_N (masses
+// relative to exp(m / T)), p(d) of a tested draft, and the row mode.
+__global__ __launch_bounds__(256) void diagnostics_kernel(const RowRec* rec, int32_t rows,
+                                                          double* zk, double* zn, double* pd,
+                                                          int32_t* mode) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < rows; i += gridDim.x * blockDim.x) {
+    const RowRec r = rec[i];
+    if (zk) zk[i] = r.zk;
+    if (zn) zn[i] = r.zn;
+    if (pd) pd[i] = r.pd;
+    if (mode) mode[i] = r.mode;
+  }
 }
 
 }  // namespace sv

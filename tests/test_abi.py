@@ -116,6 +116,17 @@ def test_host_validation_without_gpu(lib):
     assert lib.spec_verify_plan_budget(fake, 4, 3, 4, fake, 16, None, None, None) == -1
     assert lib.spec_verify_plan_budget(fake, 4, 3, 4, None, 16, fake, None, None) == -1
     assert lib.spec_verify_plan_budget(fake, 2, 3, 4, fake, 16, fake, None, None) == -2
+    # layout check: NULL qo_indptr or word, negative sizes
+    lib.spec_verify_check_layout.argtypes = [c, ctypes.c_int32, ctypes.c_int32, c, c]
+    assert lib.spec_verify_check_layout(None, 3, 9, fake, None) == -1
+    assert lib.spec_verify_check_layout(fake, 3, 9, None, None) == -1
+    assert lib.spec_verify_check_layout(fake, -1, 9, fake, None) == -2
+    # row diagnostics: workspace NULL or too small for the rows; no rows is a no-op
+    lib.spec_verify_row_diagnostics.argtypes = [c, ctypes.c_size_t, ctypes.c_int32, c, c, c, c, c]
+    assert lib.spec_verify_row_diagnostics(None, 1 << 20, 10, fake, None, None, None, None) == -4
+    assert lib.spec_verify_row_diagnostics(ws, 300, 10, fake, None, None, None, None) == -4
+    assert lib.spec_verify_row_diagnostics(ws, 300, -1, fake, None, None, None, None) == -2
+    assert lib.spec_verify_row_diagnostics(None, 0, 0, None, None, None, None, None) == 0
 
 
 def test_workspace_query_grows_with_rows(lib):
@@ -138,27 +149,40 @@ def test_sampling_block_layout_matches_header():
 
 
 def test_row_order_puts_heavy_requests_first():
-    """Host-side row schedule: a permutation of the rows with every row of a
-    heavy request (sampled, top-k off, top-p on; or top-k above the
-    single-pass limit) ahead of the others, each group in natural order."""
-    import torch
+    """Host-side row schedule from host values only: a permutation of the rows
+    with every row of a heavy request (sampled, top-k off, top-p on; or top-k
+    above the single-pass limit) ahead of the others, each group in natural
+    order."""
+    import numpy as np
     from rejection_sampling_amd import binding as B
     V = 1000
-    T = torch.tensor([0.0, 0.8, 1.0, 0.7, 0.9, 1.1])
-    k = torch.tensor([0, 0, 20, 0, 300, 0], dtype=torch.int32)
-    P = torch.tensor([0.9, 0.9, 0.9, 1.0, 1.0, 0.5])
+    T = np.array([0.0, 0.8, 1.0, 0.7, 0.9, 1.1], np.float32)
+    k = np.array([0, 0, 20, 0, 300, 0], np.int32)
+    P = np.array([0.9, 0.9, 0.9, 1.0, 1.0, 0.5], np.float32)
     heavy = [False, True, False, False, True, True]
-    qo = torch.tensor([0, 3, 5, 5, 9, 10, 13], dtype=torch.int32)
+    qo = np.array([0, 3, 5, 5, 9, 10, 13], np.int32)
     p = B.Params.__new__(B.Params)
-    p._host = (T, k, P)
-    assert p.heavy_requests(V).tolist() == heavy
-    order = B.row_order(qo, p, V)
+    p.host = (T, k, P)
+    order = B.heavy_first_order(qo, p, V, device="cpu")
     rows_of = [list(range(int(qo[r]), int(qo[r + 1]))) for r in range(6)]
     first = [i for r in range(6) if heavy[r] for i in rows_of[r]]
     rest = [i for r in range(6) if not heavy[r] for i in rows_of[r]]
     assert order.tolist() == first + rest
     # nothing to reorder when no request (or every request) is heavy
-    p._host = (T, torch.full((6,), 20, dtype=torch.int32), P)
-    assert B.row_order(qo, p, V) is None
-    p._host = (torch.ones(6), torch.zeros(6, dtype=torch.int32), torch.full((6,), 0.9))
-    assert B.row_order(qo, p, V) is None
+    p.host = (T, np.full(6, 20, np.int32), P)
+    assert B.heavy_first_order(qo, p, V, device="cpu") is None
+    p.host = (np.ones(6, np.float32), np.zeros(6, np.int32), np.full(6, 0.9, np.float32))
+    assert B.heavy_first_order(qo, p, V, device="cpu") is None
+
+
+def test_sampling_hints_from_host_values():
+    """The flags Params.from_host sets come from host values only:
+    SV_ALL_GREEDY when no request samples, SV_LIST_BOUNDED when every sampled
+    request has 0 < top_k <= 4096."""
+    import numpy as np
+    from rejection_sampling_amd import binding as B
+    T = np.array([0.0, 0.8, 0.5], np.float32)
+    assert B.sampling_hints(T, np.array([0, 20, 4096], np.int32)) == (False, True)
+    assert B.sampling_hints(T, np.array([0, 20, 0], np.int32)) == (False, False)
+    assert B.sampling_hints(T, np.array([5, 20, 4097], np.int32)) == (False, False)
+    assert B.sampling_hints(np.zeros(3, np.float32), np.zeros(3, np.int32)) == (True, True)

@@ -1,11 +1,13 @@
 """GPU parity of the verify step against the CPU oracle (through the C ABI).
 
-Small cases compare every row; the five workloads run at their full sizes on
-the GPU and are compared with the oracle on sampled requests (each computed
-by the oracle on its own: results are keyed by request id and position, so a
-request's result does not depend on its batch), plus properties that hold for
-every request.  Tolerances: integers bit-exact; probabilities 1e-5 relative;
-lse 1e-4 absolute; decision mismatches only on oracle-flagged near ties.
+Every case compares every request and row with the oracle, the five
+workloads at their full sizes included (the oracle runs sharded by request
+over host threads; each shard is the plain single-threaded oracle, and
+results are keyed by request id and position, so sharding changes nothing).
+Tolerances: integers bit-exact; probabilities 1e-5 relative; lse 1e-4
+absolute; decision mismatches only on oracle-flagged near ties, at most 1e-4
+of the rows.  On the workloads the GPU's own decision quantities (Z_K and the
+ratio) are also checked against the oracle's to half the near-tie bands.
 """
 import os
 
@@ -15,8 +17,9 @@ import torch
 
 from oracle import svref
 from rejection_sampling_amd import workloads as W
-from tests.gpu_common import (compare_build, compare_verify, dev_f32, dev_i32, dev_logits,
-                              gpu_verify, make_drafts, oracle_verify, params_for, progress)
+from tests.gpu_common import (compare_build, compare_margins, compare_verify, dev_f32, dev_i32,
+                              dev_logits, gpu_verify, make_drafts, oracle_verify, params_for,
+                              progress)
 
 pytestmark = pytest.mark.gpu
 
@@ -109,12 +112,13 @@ def test_row_order_hint_changes_nothing():
     q, d = make_drafts(w, qo, THREADS)
     ref = oracle_verify(w, qo, d, q, threads=THREADS)
     prm = params_for(w)
-    assert B.row_order(dev_i32(qo), prm, w.vocab) is not None
+    order = B.heavy_first_order(qo, prm, w.vocab)
+    assert order is not None
     outs = []
     for reorder in (False, True):
         progress(f"row order hint, reorder={reorder}")
         call = B.PreparedRejectionSample(dev_logits(w.logits), dev_i32(qo), dev_i32(d), dev_f32(q),
-                                         prm, reorder=reorder)
+                                         prm, row_order=order if reorder else None)
         o = call()
         torch.cuda.synchronize()
         outs.append({k: v.cpu().numpy() for k, v in o.items()})
@@ -254,20 +258,59 @@ def test_all_greedy_without_draft_probs():
 
 
 # ------------------------------------------------------- build outputs
+def _gpu_build(w, qo, want_probs, kmax):
+    from rejection_sampling_amd import binding as B
+    out = B.build_target_probs(dev_logits(w.logits), dev_i32(qo), params_for(w),
+                               want_probs=want_probs, kmax=kmax)
+    diag = B.row_diagnostics(w.num_rows)
+    torch.cuda.synchronize()
+    gpu = {k: (v.cpu().numpy() if v is not None else None) for k, v in out.items()}
+    gpu.update({"diag_" + k: v.cpu().numpy() for k, v in diag.items()})
+    return gpu
+
+
 @pytest.mark.parametrize("dtype", [W.BF16, W.F32])
 def test_build_target_probs(dtype):
     w = _small(12, 10007, dtype=dtype, R=20)
     qo = w.qo_indptr()
     kmax = 64
     progress(f"build_target_probs dtype={dtype}")
-    from rejection_sampling_amd import binding as B
-    out = B.build_target_probs(dev_logits(w.logits), dev_i32(qo), params_for(w), want_probs=True,
-                               kmax=kmax)
-    torch.cuda.synchronize()
-    gpu = {k: (v.cpu().numpy() if v is not None else None) for k, v in out.items()}
-    ref = svref.build_target_probs(w.logits, qo, w.temperature, w.top_k, w.top_p, w.request_id,
-                                   w.position0, w.seed, want_probs=True, kmax=kmax)
-    compare_build(gpu, ref, ref["row_flags"], qo, w.temperature, kmax, label="build")
+    gpu = _gpu_build(w, qo, True, kmax)
+    ref = svref.parallel_build(w.logits, qo, w.temperature, w.top_k, w.top_p, w.request_id,
+                               w.position0, w.seed, kmax=kmax, prob_rows=range(w.num_rows),
+                               threads=THREADS)
+    compare_build(gpu, ref, label="build")
+
+
+def _build_full(w, qo, label, prob_rows):
+    """Build parity at a workload's full shape: every row's max, argmax, lse,
+    kept count and first 1024 kept ids, dense probabilities on prob_rows, and
+    the GPU's Z_K against the oracle's on every sampled row."""
+    kmax = 1024
+    progress(f"{label}: GPU build ({w.num_rows} rows x {w.vocab})")
+    gpu = _gpu_build(w, qo, True, kmax)
+    progress(f"{label}: oracle build")
+    ref = svref.parallel_build(w.logits, qo, w.temperature, w.top_k, w.top_p, w.request_id,
+                               w.position0, w.seed, kmax=kmax, prob_rows=prob_rows,
+                               threads=THREADS)
+    near, differ = compare_build(gpu, ref, label=label)
+    sampled = np.repeat(w.temperature > 0, np.diff(qo))
+    zk_err = np.abs(gpu["diag_zk"][sampled] / ref["row_zk"][sampled] - 1.0)
+    progress(f"{label}: build ok, near-tie rows {near} (count differs on {differ}), "
+             f"max kept {int(gpu['kept_count'].max())}, max |Z_K rel err| {zk_err.max():.3g}")
+    assert zk_err.max() < 5e-7
+
+
+def test_build_full_shape_workload3():
+    w = W.workload3()
+    qo = w.qo_indptr()
+    _build_full(w, qo, "workload 3 build", prob_rows=range(0, w.num_rows, 97))
+
+
+def test_build_full_shape_workload5():
+    w = W.workload5()
+    vl, qo, _ = svref.plan_windows(w.confidence, w.budget)
+    _build_full(w, qo, "workload 5 build", prob_rows=range(0, w.num_rows, 131))
 
 
 # ------------------------------------------------------------ workloads
@@ -296,14 +339,17 @@ def test_workload2_full():
     compare_verify(gpu, ref, qo, label="workload 2")
 
 
-def _big(w, qo, sample, label, cap=None):
+def _big(w, qo, label, cap=None):
     progress(f"{label}: drafts by the oracle ({w.num_rows} rows)")
     q, d = make_drafts(w, qo, THREADS)
     progress(f"{label}: GPU verify")
-    gpu = gpu_verify(w, qo, d, q, cap)
-    progress(f"{label}: oracle on {len(sample)} sampled requests")
-    ref = oracle_verify(w, qo, d, q, cap, requests=sample, threads=THREADS)
-    mism, flags = compare_verify(gpu, ref, qo, requests=sample, cap=cap, label=label)
+    gpu = gpu_verify(w, qo, d, q, cap, diagnostics=True)
+    progress(f"{label}: oracle on every request")
+    ref = oracle_verify(w, qo, d, q, cap, threads=THREADS)
+    mism, flags = compare_verify(gpu, ref, qo, cap=cap, label=label)
+    zk_err, ratio_err, nz, nr = compare_margins(gpu, ref, qo, d, q, label=label)
+    progress(f"{label}: margins on {nz} built rows / {nr} tested drafts: max |Z_K rel err| "
+             f"{zk_err:.3g}, max |ratio err| {ratio_err:.3g}")
     # properties of every request
     R = w.num_requests
     for r in range(R):
@@ -322,24 +368,14 @@ def _big(w, qo, sample, label, cap=None):
 def test_workload3_full():
     w = W.workload3()
     qo = w.qo_indptr()
-    sample = np.random.default_rng(3).choice(w.num_requests, 24, replace=False)
-    _big(w, qo, sample, "workload 3 128x8 V=248320")
+    _big(w, qo, "workload 3 128x8 V=248320")
 
 
 def test_workload4_full():
     w = W.workload4()
     qo = w.qo_indptr()
-    g = np.random.default_rng(4)
     greedy = np.nonzero(w.temperature == 0)[0]
-    classes = [np.nonzero((w.temperature > 0) & (w.top_k == k) & (w.top_p == p))[0]
-               for k in (0, 20, 50) for p in (np.float32(1.0), np.float32(0.9))]
-    sample = list(g.choice(greedy, 4, replace=False))
-    for c in classes:
-        sample += list(g.choice(c, min(4, len(c)), replace=False))
-    # the hottest top-k-off / top-p requests reach the exact path
-    hot = np.nonzero((w.top_k == 0) & (w.top_p < 1) & (w.temperature > 1.0))[0]
-    sample += list(hot[:4])
-    gpu, q, d = _big(w, qo, sorted(set(int(x) for x in sample)), "workload 4 512x8 V=129280")
+    gpu, q, d = _big(w, qo, "workload 4 512x8 V=129280")
     # greedy requests of the whole batch: emitted token is the row argmax
     x = W.bf16_to_f32(w.logits)
     for r in greedy:
@@ -359,8 +395,7 @@ def test_workload5_planner_and_verify():
     assert np.array_equal(qo_g.cpu().numpy(), qo)
     assert np.array_equal(surv_g.cpu().numpy().view(np.uint32), surv.view(np.uint32))
     assert qo[-1] == w.num_rows
-    sample = np.random.default_rng(5).choice(w.num_requests, 24, replace=False)
-    gpu, _, _ = _big(w, qo, sample, "workload 5 ragged 1792 rows V=248320")
+    gpu, _, _ = _big(w, qo, "workload 5 ragged 1792 rows V=248320")
     # the step's acceptance and trim statistics over the planner's windows
     Bk = w.confidence.shape[1]
     st_g = B.acceptance_stats(dev_i32(gpu["accept_len"]), vl_g, Bk).cpu().numpy()
