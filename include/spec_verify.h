@@ -168,6 +168,29 @@ int32_t spec_verify_rejection_sample(const void* target_logits, sv_dtype dt, int
                                      uint8_t* row_flags, void* workspace,
                                      size_t workspace_bytes, sv_stream_t stream);
 
+/* spec_verify_rejection_sample without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  The call allocates nothing: its
+ * scratch is a static device array of the library, one per device (34 MiB,
+ * placed when the library loads on the device and held until the process
+ * ends), whose address the first call on each device looks up with that
+ * device current.  Limits: num_rows <= 1024 and num_requests <= 1024, else
+ * SV_ERR_SHAPE before any launch.  Every call on one device shares that
+ * device's array: calls that overlap on one device (two streams, two host
+ * threads) race and give undefined results; calls ordered on one stream are
+ * safe.  Arguments, outputs and other errors are spec_verify_rejection_sample's;
+ * SV_CHECK writes its layout word into the shared array, where the caller cannot
+ * read it (the refused outputs still show a failed check). */
+int32_t spec_verify_rejection_sample_noalloc(const void* target_logits, sv_dtype dt,
+                                             int64_t ld_logits, int32_t vocab,
+                                             const int32_t* qo_indptr, int32_t num_requests,
+                                             int32_t num_rows, const int32_t* draft_tokens,
+                                             const float* draft_probs, int64_t ld_q,
+                                             const int32_t* verify_cap, const sv_sampling* sp,
+                                             int32_t* accept_len, int32_t* out_tokens,
+                                             int32_t* next_token, uint8_t* row_flags,
+                                             sv_stream_t stream);
+
 /* Confidence planner (TensorRT-LLM PR #17056, first commit note: prefix
  * survival is the cumulative product of per-position probabilities; the budget
  * goes out by global survival rank with a value-independent tie-break).

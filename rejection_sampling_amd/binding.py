@@ -37,6 +37,7 @@ EXPORTS = [
     "spec_verify_estimator_state_doubles", "spec_verify_estimator_init",
     "spec_verify_estimator_predict", "spec_verify_estimator_observe", "spec_verify_plan_budget",
     "spec_verify_check_layout", "spec_verify_row_diagnostics",
+    "spec_verify_rejection_sample_noalloc",
 ]
 
 
@@ -69,6 +70,9 @@ def load(path: str = LIB_PATH):
     L.spec_verify_rejection_sample.argtypes = [P, i32, i64, i32, P, i32, i32, P, P, i64, P, P, P,
                                                P, P, P, P, sz, P]
     L.spec_verify_rejection_sample.restype = i32
+    L.spec_verify_rejection_sample_noalloc.argtypes = [P, i32, i64, i32, P, i32, i32, P, P, i64,
+                                                       P, P, P, P, P, P, P]
+    L.spec_verify_rejection_sample_noalloc.restype = i32
     L.spec_verify_plan_windows.argtypes = [P, i64, i32, i32, i32, P, P, P, P, sz, P]
     L.spec_verify_plan_windows.restype = i32
     L.spec_verify_plan_budget.argtypes = [P, i64, i32, i32, P, i32, P, P, P]
@@ -301,6 +305,34 @@ def rejection_sample(logits: torch.Tensor, qo_indptr: torch.Tensor, draft_tokens
         _ptr(logits), dt, logits.stride(0), V, _ptr(qo), R, rows, _ptr(d), _ptr(draft_probs), ldq,
         _ptr(cap), ctypes.byref(params.s), _ptr(out["accept_len"]), _ptr(out["out_tokens"]),
         _ptr(out["next_token"]), _ptr(out["row_flags"]), _ptr(ws), ws.numel(), _stream())
+    _check(rc)
+    return out
+
+
+NOALLOC_MAX_ROWS = NOALLOC_MAX_REQUESTS = 1024
+
+
+def rejection_sample_noalloc(logits: torch.Tensor, qo_indptr: torch.Tensor,
+                             draft_tokens: torch.Tensor, draft_probs: Optional[torch.Tensor],
+                             params: Params, out, verify_cap: Optional[torch.Tensor] = None):
+    """spec_verify_rejection_sample_noalloc: the verify step with the
+    library's static per-device scratch instead of a workspace.  `out` holds
+    the caller's output tensors (accept_len, out_tokens, next_token,
+    row_flags), so neither the call nor this wrapper allocates."""
+    dt = _logits(logits)
+    rows, V = logits.shape
+    qo = _dev(qo_indptr, torch.int32, "qo_indptr")
+    R = qo.numel() - 1
+    d = _dev(draft_tokens, torch.int32, "draft_tokens")
+    if draft_probs is not None and (draft_probs.dtype != torch.float32 or
+                                    not draft_probs.is_cuda or draft_probs.stride(1) != 1):
+        raise ValueError("draft_probs must be a 2-D fp32 device tensor")
+    cap = _dev(verify_cap, torch.int32, "verify_cap")
+    ldq = draft_probs.stride(0) if draft_probs is not None else V
+    rc = load().spec_verify_rejection_sample_noalloc(
+        _ptr(logits), dt, logits.stride(0), V, _ptr(qo), R, rows, _ptr(d), _ptr(draft_probs), ldq,
+        _ptr(cap), ctypes.byref(params.s), _ptr(out["accept_len"]), _ptr(out["out_tokens"]),
+        _ptr(out["next_token"]), _ptr(out.get("row_flags")), _stream())
     _check(rc)
     return out
 

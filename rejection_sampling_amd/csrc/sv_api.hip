@@ -23,14 +23,14 @@ int32_t fail(int32_t code, const char* what) {
   return code;
 }
 
-size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+constexpr size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
   size_t rec, list, race_job, race_part, keys, total;
 };
 
-Layout layout(int64_t rows, int64_t R, int64_t block) {
-  Layout L;
+constexpr Layout layout(int64_t rows, int64_t R, int64_t block) {
+  Layout L{};
   L.rec = sv::kWsHeader;  // bytes [0, 4): the layout check word of SV_CHECK
   L.list = L.rec + align256((size_t)rows * sizeof(sv::RowRec));
   L.race_job = L.list + align256((size_t)rows * sv::kListCap * sizeof(sv::ListEntry));
@@ -39,6 +39,20 @@ Layout layout(int64_t rows, int64_t R, int64_t block) {
   L.total = L.keys + align256((size_t)(R * block) * sizeof(uint64_t)) + 256;
   return L;
 }
+
+// ---- scratch of the allocation-free verify entry point
+// One copy per device (the runtime places it when the library's code object
+// loads on that device; it stays until the process ends), sized for
+// kStaticMaxRows rows and kStaticMaxRequests requests.  Host code never uses
+// the symbol's name as an address: the device address comes from
+// hipGetSymbolAddress, looked up once per device.
+constexpr int kStaticMaxRows = 1024;
+constexpr int kStaticMaxRequests = 1024;
+constexpr size_t kStaticScratchBytes = layout(kStaticMaxRows, kStaticMaxRequests, 0).total;
+static_assert(kStaticScratchBytes <= (size_t)34 << 20, "scratch stays modest");
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {};
 
 // Workgroups per full-vocabulary race: none when no request can need one
 // (every request greedy, or every kept set bounded by a list), else one per
@@ -127,6 +141,9 @@ int resident_row_workgroups() {
 }
 
 }  // namespace
+
+// The allocation-free entry point's scratch (see kStaticScratchBytes).
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
 
 extern "C" {
 
@@ -295,6 +312,43 @@ int32_t spec_verify_rejection_sample(const void* target_logits, sv_dtype dt, int
     if ((rc = check_launch("race finish"))) return rc;
   }
   return SV_OK;
+}
+
+int32_t spec_verify_rejection_sample_noalloc(const void* target_logits, sv_dtype dt,
+                                             int64_t ld_logits, int32_t vocab,
+                                             const int32_t* qo_indptr, int32_t num_requests,
+                                             int32_t num_rows, const int32_t* draft_tokens,
+                                             const float* draft_probs, int64_t ld_q,
+                                             const int32_t* verify_cap, const sv_sampling* sp,
+                                             int32_t* accept_len, int32_t* out_tokens,
+                                             int32_t* next_token, uint8_t* row_flags,
+                                             sv_stream_t stream) {
+  if (num_rows > kStaticMaxRows || num_requests > kStaticMaxRequests)
+    return fail(SV_ERR_SHAPE, "the allocation-free entry point takes at most 1024 rows and "
+                              "1024 requests");
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+    return fail(SV_ERR_HIP, "no current device (or a device index above 63)");
+  void* ws = nullptr;
+  {
+    std::lock_guard<std::mutex> g(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+      // first call on this device (it is current): the device's own address
+      // of the scratch array
+      void* p = nullptr;
+      const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || !p) {
+        g_last_error = std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e);
+        return SV_ERR_HIP;
+      }
+      g_scratch_ptr[dev] = p;
+    }
+    ws = g_scratch_ptr[dev];
+  }
+  return spec_verify_rejection_sample(target_logits, dt, ld_logits, vocab, qo_indptr,
+                                      num_requests, num_rows, draft_tokens, draft_probs, ld_q,
+                                      verify_cap, sp, accept_len, out_tokens, next_token,
+                                      row_flags, ws, kStaticScratchBytes, stream);
 }
 
 int32_t spec_verify_plan_windows(const float* confidence, int64_t ld_conf, int32_t num_requests,
