@@ -251,6 +251,111 @@ RaceResult race(const std::vector<int32_t>& cand, WeightFn weight, uint64_t seed
   return res;
 }
 
+/* Block verification of one sampled request (Sun, Mendlovic, Leviathan,
+ * Aharoni, Beirami, Ro, Suresh, "Block Verification Accelerates Speculative
+ * Decoding": the block is accepted jointly, not token by token, and the
+ * correction token comes from a residual reweighted by the block's weight).
+ * Rows s..s+G verify drafts 0..G-1 (G = the verified positions) and row s+G is
+ * the row after them.  In the paper's notation, with M_b the target and M_s
+ * the draft distribution of each row:
+ *   p_0 = 1; p_i = min(p_{i-1} M_b(X_i) / M_s(X_i), 1)        (row i-1, i = 1..G)
+ *   h_i = A_i / (A_i + 1 - p_i), A_i = sum_x max(p_i M_b(x) - M_s(x), 0) over
+ *         row i, for i < G;  h_G = p_G
+ *   tau = the largest i with eta_i < h_i (0 if none)
+ *   emitted: X_1..X_tau, then Y from row tau: M_b when tau = G, otherwise
+ *         the residual max(p_tau M_b - M_s, 0) (normalised).
+ * Readings: eta_i is the acceptance uniform of row i - 1 (so G = 1 is the
+ * token rule with the same uniform, a strict '<' as there); a draft id
+ * outside [0, V) has ratio 0, and when it is the draft of row tau, Y comes
+ * from M_b (nothing was proposed there); q = 0 at the draft gives ratio 1
+ * when M_b(X) > 0 (0 otherwise), p_i = 0 once any ratio was 0; h_i = 1 when
+ * its denominator is 0 (then p_i = 1 and row i's distributions agree, and a
+ * later position is always accepted); an all-zero residual falls back to M_b
+ * (flagged, as in the token rule).  Row flags: ACCEPT on row i - 1 when
+ * eta_i < h_i; NEAR_RATIO when |eta_i - h_i| < 1e-5; ratio / u diagnostics
+ * hold h_i and eta_i. */
+void block_verify_request(const void* logits, int32_t dtype, int64_t ld, int32_t V, int32_t s,
+                          int32_t G, const int32_t* draft_tokens, const float* draft_probs,
+                          int64_t ld_q, const Params& prm, uint64_t seed, uint32_t rid,
+                          uint32_t pos0, int32_t& accept_len, int32_t& next_token,
+                          int32_t* out_tokens, uint8_t* row_flags, double* row_ratio,
+                          double* row_u, double* row_zk, double* row_zn) {
+  std::vector<RowDist> rows((size_t)G + 1);
+  for (int32_t j = 0; j <= G; ++j) {
+    build_row(logits, dtype, ld, s + j, V, prm, rows[j]);
+    if (row_zk) row_zk[s + j] = rows[j].zk;
+    if (row_zn) row_zn[s + j] = rows[j].zn;
+  }
+  auto q_of = [&](int32_t j, int32_t v) { return (double)draft_probs[(int64_t)(s + j) * ld_q + v]; };
+  auto bad = [&](int32_t j) { return draft_tokens[s + j] < 0 || draft_tokens[s + j] >= V; };
+
+  /* the block weights p_0..p_G */
+  std::vector<double> p((size_t)G + 1);
+  p[0] = 1.0;
+  for (int32_t i = 1; i <= G; ++i) {
+    const int32_t j = i - 1;
+    double ratio = 0.0;
+    if (!bad(j)) {
+      const int32_t x = draft_tokens[s + j];
+      const double pb = rows[j].p[x], qs = q_of(j, x);
+      ratio = qs > 0.0 ? pb / qs : (pb > 0.0 ? HUGE_VAL : 0.0);
+    }
+    p[i] = p[i - 1] > 0.0 ? std::min(p[i - 1] * ratio, 1.0) : 0.0;
+  }
+
+  /* the acceptance test of every position; tau is the last one passed */
+  int32_t tau = 0;
+  for (int32_t i = 1; i <= G; ++i) {
+    double h;
+    if (i < G) {
+      double A = 0.0;  /* M_b is zero off the kept set, so only it contributes */
+      for (int32_t x : rows[i].kept) A += std::max(p[i] * rows[i].p[x] - q_of(i, x), 0.0);
+      const double den = A + 1.0 - p[i];
+      h = den > 0.0 ? A / den : 1.0;
+    } else {
+      h = p[G];
+    }
+    const int32_t j = i - 1;
+    const double eta = uniform_accept(seed, rid, pos0 + (uint32_t)j);
+    uint8_t fl = bad(j) ? SVREF_ROW_BAD_DRAFT : 0;
+    if (eta < h) {
+      tau = i;
+      fl |= SVREF_ROW_ACCEPT;
+    }
+    if (std::fabs(eta - h) < 1e-5) fl |= SVREF_ROW_NEAR_RATIO;
+    if (rows[j].near_topp) fl |= SVREF_ROW_NEAR_TOPP;
+    if (row_flags) row_flags[s + j] = fl;
+    if (row_ratio) row_ratio[s + j] = h;
+    if (row_u) row_u[s + j] = eta;
+  }
+
+  /* the emitted token from row tau */
+  const RowDist& dt = rows[tau];
+  const uint32_t pos = pos0 + (uint32_t)tau;
+  uint8_t sfl = SVREF_ROW_SAMPLED | (dt.near_topp ? SVREF_ROW_NEAR_TOPP : 0);
+  RaceResult rr;
+  bool use_p = tau == G || bad(tau);
+  if (!use_p) {
+    const double w = p[tau];
+    auto resid = [&](int32_t v) { return std::max(w * dt.p[v] - q_of(tau, v), 0.0); };
+    rr = race(dt.kept, resid, seed, rid, pos, 1u);
+    if (rr.token < 0) {
+      use_p = true;
+      sfl |= SVREF_ROW_RESID_EMPTY;
+    }
+  }
+  if (use_p) {
+    auto pw = [&](int32_t v) { return dt.p[v]; };
+    rr = race(dt.kept, pw, seed, rid, pos, 1u);
+  }
+  if (rr.near) sfl |= SVREF_ROW_NEAR_RACE;
+  if (row_flags) row_flags[s + tau] |= sfl;
+  for (int32_t j = 0; j < tau; ++j) out_tokens[s + j] = draft_tokens[s + j];
+  out_tokens[s + tau] = rr.token;
+  accept_len = tau;
+  next_token = rr.token;
+}
+
 bool check_layout(const int32_t* qo, int32_t R, int32_t rows) {
   if (R < 0 || rows < 0 || qo == nullptr) return false;
   if (qo[0] != 0 || qo[R] != rows) return false;
@@ -360,6 +465,13 @@ int32_t svref_rejection_sample(const void* logits, int32_t dtype, int64_t ld_log
     if (verify_cap) cap = std::max(0, std::min(verify_cap[r], gamma));
     const uint32_t rid = sp->request_id ? sp->request_id[r] : (uint32_t)r;
     const uint32_t pos0 = sp->position0 ? sp->position0[r] : 0u;
+
+    if ((sp->flags & SVREF_BLOCK_VERIFY) && !prm.greedy) {
+      block_verify_request(logits, dtype, ld_logits, vocab, s, cap, draft_tokens, draft_probs,
+                           ld_q, prm, sp->seed, rid, pos0, accept_len[r], next_token[r],
+                           out_tokens, row_flags, row_ratio, row_u, row_zk, row_zn);
+      continue;
+    }
 
     /* O10/O11: test every draft row inside the cap; the first failure ends
      * the accepted prefix. */

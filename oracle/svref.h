@@ -55,6 +55,11 @@ enum {
   SVREF_ROW_BAD_DRAFT = 64  /* draft id outside [0, V): rejected                 */
 };
 
+/* svref_sampling.flags: verify sampled requests by block verification (Sun et
+ * al., "Block Verification Accelerates Speculative Decoding") instead of the
+ * token-by-token ratio test; greedy requests keep the argmax rule. */
+enum { SVREF_BLOCK_VERIFY = 8 };
+
 typedef struct {
   const float* temperature;  /* [R]  T <= 0 or NaN: greedy                    */
   const int32_t* top_k;      /* [R]  k <= 0 or k >= V: off; NULL: off         */
@@ -62,7 +67,7 @@ typedef struct {
   const uint32_t* request_id;/* [R]  Philox counter word; NULL: r             */
   const uint32_t* position0; /* [R]  absolute position of window row 0; NULL: 0 */
   uint64_t seed;             /* Philox key                                    */
-  uint32_t flags;            /* unused by the oracle                          */
+  uint32_t flags;            /* SVREF_BLOCK_VERIFY or 0                       */
 } svref_sampling;
 
 /* Philox4x32-10 block function: out = Philox(key, ctr). */

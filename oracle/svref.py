@@ -121,14 +121,17 @@ def uniform_race(seed: int, rid: int, pos: int, tag: int, token: int) -> float:
 class _Params:
     """Keeps the per-request arrays alive while the C struct points at them."""
 
-    def __init__(self, T, k, P, rid, pos0, seed):
+    def __init__(self, T, k, P, rid, pos0, seed, flags=0):
         self.T = _c(T, np.float32)
         self.k = _c(k, np.int32)
         self.P = _c(P, np.float32)
         self.rid = _c(rid, np.uint32)
         self.pos0 = _c(pos0, np.uint32)
         self.s = Sampling(_p(self.T), _p(self.k), _p(self.P), _p(self.rid), _p(self.pos0),
-                          int(seed), 0)
+                          int(seed), int(flags))
+
+
+BLOCK_VERIFY = 8
 
 
 def _dt(logits):
@@ -174,7 +177,9 @@ def build_target_probs(logits, qo, T, k=None, P=None, rid=None, pos0=None, seed=
 
 
 def rejection_sample(logits, qo, drafts, q, T, k=None, P=None, rid=None, pos0=None, seed=0,
-                     verify_cap=None):
+                     verify_cap=None, block=False):
+    """The verify step; block=True verifies sampled requests by block
+    verification instead of the token-by-token ratio test."""
     logits = np.ascontiguousarray(logits)
     rows, V = logits.shape
     R = len(qo) - 1
@@ -182,7 +187,7 @@ def rejection_sample(logits, qo, drafts, q, T, k=None, P=None, rid=None, pos0=No
     drafts = _c(drafts, np.int32)
     q = _c(q, np.float32)
     cap = _c(verify_cap, np.int32)
-    prm = _Params(T, k, P, rid, pos0, seed)
+    prm = _Params(T, k, P, rid, pos0, seed, BLOCK_VERIFY if block else 0)
     out = {
         "accept_len": np.zeros(R, np.int32),
         "out_tokens": np.zeros(rows, np.int32),
@@ -388,7 +393,7 @@ def parallel_argmax(logits, qo, threads=None):
 
 
 def parallel_rejection_sample(logits, qo, drafts, q, T, k, P, rid, pos0, seed, verify_cap=None,
-                              requests=None, threads=None):
+                              requests=None, threads=None, block=False):
     """Oracle verify over all requests, or over the listed ``requests`` only
     (each one as its own single-request call).  Returns per-request arrays and,
     for rows of covered requests, per-row arrays (rows of uncovered requests are
@@ -416,7 +421,7 @@ def parallel_rejection_sample(logits, qo, drafts, q, T, k, P, rid, pos0, seed, v
         out = rejection_sample(logits[s0:s1], qo[r0:r1 + 1] - qo[r0], drafts[s0:s1],
                                None if q is None else q[s0:s1], _sub(T, r0, r1),
                                _sub(k, r0, r1), _sub(P, r0, r1), _sub(rid, r0, r1),
-                               _sub(pos0, r0, r1), seed, _sub(verify_cap, r0, r1))
+                               _sub(pos0, r0, r1), seed, _sub(verify_cap, r0, r1), block)
         res["accept_len"][r0:r1] = out["accept_len"]
         res["next_token"][r0:r1] = out["next_token"]
         for key in ("out_tokens", "row_flags", "row_ratio", "row_u", "row_zk", "row_zn"):

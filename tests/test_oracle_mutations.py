@@ -86,6 +86,22 @@ CASES = [
      "(best - second) / best < 1e-5", ["test_oracle_near_ties.py::test_race_band"]),
     ("race forgets the replaced best", "      second = best;\n      best = key;",
      "      best = key;", ["test_oracle_near_ties.py::test_race_band_sees_a_replaced_best"]),
+    ("block test weighs row i with the previous position's weight",
+     "A += std::max(p[i] * rows[i].p[x] - q_of(i, x), 0.0);",
+     "A += std::max(p[i - 1] * rows[i].p[x] - q_of(i, x), 0.0);",
+     ["test_oracle_block.py::test_generated_sequences_follow_the_target",
+      "test_oracle_block.py::test_mean_accepted_length_matches_enumeration"]),
+    ("block stops at the first failed position", "      tau = i;\n      fl |= SVREF_ROW_ACCEPT;",
+     "      if (tau == i - 1) tau = i;\n      fl |= SVREF_ROW_ACCEPT;",
+     ["test_oracle_block.py::test_generated_sequences_follow_the_target",
+      "test_oracle_block.py::test_mean_accepted_length_matches_enumeration"]),
+    ("block residual not reweighted by the block weight",
+     "std::max(w * dt.p[v] - q_of(tau, v), 0.0)", "std::max(dt.p[v] - q_of(tau, v), 0.0)",
+     ["test_oracle_block.py::test_generated_sequences_follow_the_target"]),
+    ("block tests the last position like the others", "    if (i < G) {\n      double A",
+     "    if (i <= G) {\n      double A",
+     ["test_oracle_block.py::test_generated_sequences_follow_the_target",
+      "test_oracle_block.py::test_mean_accepted_length_matches_enumeration"]),
 ]
 
 
