@@ -70,12 +70,18 @@ enum {
                          row_flags 0 on every row, spec_verify_build_target_probs
                          writes row_max / row_lse NaN, row_argmax -1,
                          kept_count -1, kept_idx -1 and leaves probs untouched. */
-  SV_LIST_BOUNDED = 4u /* every sampled request has 0 < top_k <= 4096, so no
+  SV_LIST_BOUNDED = 4u, /* every sampled request has 0 < top_k <= 4096, so no
                          correction or bonus token is sampled over the whole
                          vocabulary: the call skips the two launches that split
                          such samples over workgroups.  A performance hint only:
                          a request that breaks it is still sampled exactly (by
                          one workgroup). */
+  SV_BLOCK_VERIFY = 8u /* spec_verify_rejection_sample verifies sampled requests
+                         by block verification (Sun et al., "Block Verification
+                         Accelerates Speculative Decoding"; the consolidation
+                         study's rejection_sample_method "block", sections 2, 4,
+                         6) instead of token by token; greedy requests keep the
+                         argmax rule.  See spec_verify_rejection_sample. */
 };
 
 /* Bits of the layout check word (SV_CHECK, spec_verify_check_layout). */
@@ -99,7 +105,8 @@ typedef struct {
   const uint32_t* request_id;/* [R] device or NULL (r): Philox counter word         */
   const uint32_t* position0; /* [R] device or NULL (0): absolute position of row 0  */
   uint64_t seed;             /* Philox4x32-10 key                                   */
-  uint32_t flags;            /* SV_ALL_GREEDY | SV_CHECK | SV_LIST_BOUNDED          */
+  uint32_t flags;            /* SV_ALL_GREEDY | SV_CHECK | SV_LIST_BOUNDED |
+                                SV_BLOCK_VERIFY                                     */
   const int32_t* row_order;  /* [num_rows] device or NULL (natural order): the order
                                 in which rows are scheduled, a permutation of
                                 0..num_rows-1 (anything else leaves the results
@@ -157,6 +164,15 @@ int32_t spec_verify_build_target_probs(const void* logits, sv_dtype dt, int64_t 
  *   accept_len [R]; out_tokens [num_rows]: row s_r + j holds draft j for
  *              j < L, the sampled token at j = L, -1 after; next_token [R]: the
  *              sampled (correction or bonus) token; row_flags [num_rows] or NULL.
+ * With SV_BLOCK_VERIFY a sampled request is verified as a block: weights
+ * p_0 = 1, p_i = min(p_{i-1} p(d_{i-1}) / q(d_{i-1}), 1); position i passes when
+ * u_{i-1} < h_i, h_i = A_i / (A_i + 1 - p_i) with A_i the residual mass
+ * sum_x max(p_i p_i(x) - q_i(x), 0) of row i (h = p at the last verified
+ * position); accept_len is the last position passed, and the emitted token
+ * comes from the residual max(p_L p - q, 0) of row L, or from p when every
+ * position passed.  row_flags bit 0 then marks the positions passed.  Rows
+ * whose kept set is not a list (top-k and top-p off, or a kept set over 4096)
+ * cost one extra pass over the row and its draft probabilities in the finalize.
  * Returns SV_ERR_NULL when draft_probs is NULL without SV_ALL_GREEDY. */
 int32_t spec_verify_rejection_sample(const void* target_logits, sv_dtype dt, int64_t ld_logits,
                                      int32_t vocab, const int32_t* qo_indptr,

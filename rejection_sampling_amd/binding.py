@@ -21,6 +21,7 @@ SV_F32, SV_BF16 = 0, 1
 SV_ALL_GREEDY = 1
 SV_CHECK = 2
 SV_LIST_BOUNDED = 4
+SV_BLOCK_VERIFY = 8
 LAYOUT_START, LAYOUT_ORDER, LAYOUT_END = 1, 2, 4
 LIST_CAP = 4096  # kept-set entries a row can list (top-k bound of SV_LIST_BOUNDED)
 TOPK_SINGLE_PASS = 256  # largest top-k the streaming pass selects by itself
@@ -181,7 +182,7 @@ class Params:
 
     def __init__(self, temperature, top_k=None, top_p=None, request_id=None, position0=None,
                  seed: int = 0, all_greedy: bool = False, list_bounded: bool = False,
-                 check: bool = False):
+                 check: bool = False, block: bool = False):
         self.T = _dev(temperature, torch.float32, "temperature")
         self.k = _dev(top_k, torch.int32, "top_k")
         self.P = _dev(top_p, torch.float32, "top_p")
@@ -191,13 +192,13 @@ class Params:
         self.pos0 = _dev(position0, torch.int32, "position0")
         self.host = None   # (T, k, P) host arrays when built by from_host
         flags = ((SV_ALL_GREEDY if all_greedy else 0) | (SV_LIST_BOUNDED if list_bounded else 0) |
-                 (SV_CHECK if check else 0))
+                 (SV_CHECK if check else 0) | (SV_BLOCK_VERIFY if block else 0))
         self.s = Sampling(_ptr(self.T), _ptr(self.k), _ptr(self.P), _ptr(self.rid),
                           _ptr(self.pos0), int(seed) & ((1 << 64) - 1), flags, None)
 
     @classmethod
     def from_host(cls, temperature, top_k=None, top_p=None, request_id=None, position0=None,
-                  seed: int = 0, device="cuda", check: bool = False):
+                  seed: int = 0, device="cuda", check: bool = False, block: bool = False):
         """Build from host (numpy or CPU) arrays: every request greedy sets
         SV_ALL_GREEDY, every sampled request with 0 < top_k <= 4096 sets
         SV_LIST_BOUNDED.  The arrays are uploaded once, here."""
@@ -215,7 +216,7 @@ class Params:
             return None if a is None else torch.from_numpy(
                 np.ascontiguousarray(a, np.uint32).view(np.int32)).to(device)
         prm = cls(up(T, np.float32), up(k, np.int32), up(P, np.float32), u32(request_id),
-                  u32(position0), seed, all_greedy, list_bounded, check)
+                  u32(position0), seed, all_greedy, list_bounded, check, block)
         prm.host = (T, kk, np.ones(R, np.float32) if P is None else P)
         return prm
 

@@ -26,7 +26,7 @@ int32_t fail(int32_t code, const char* what) {
 constexpr size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t rec, list, race_job, race_part, keys, total;
+  size_t rec, list, race_job, race_part, race_zn, block_w, keys, total;
 };
 
 constexpr Layout layout(int64_t rows, int64_t R, int64_t block) {
@@ -35,7 +35,9 @@ constexpr Layout layout(int64_t rows, int64_t R, int64_t block) {
   L.list = L.rec + align256((size_t)rows * sizeof(sv::RowRec));
   L.race_job = L.list + align256((size_t)rows * sv::kListCap * sizeof(sv::ListEntry));
   L.race_part = L.race_job + align256((size_t)R * sizeof(int32_t));
-  L.keys = L.race_part + align256((size_t)R * sv::kMaxRaceSegs * sizeof(sv::RacePart));
+  L.race_zn = L.race_part + align256((size_t)R * sv::kMaxRaceSegs * sizeof(sv::RacePart));
+  L.block_w = L.race_zn + align256((size_t)R * sizeof(double));
+  L.keys = L.block_w + align256((size_t)rows * 2 * sizeof(double));
   L.total = L.keys + align256((size_t)(R * block) * sizeof(uint64_t)) + 256;
   return L;
 }
@@ -209,6 +211,9 @@ static sv::VerifyArgs base_args(const void* logits, sv_dtype dt, int64_t ld, int
   A.list = (sv::ListEntry*)((char*)ws + L.list);
   A.race_job = (int32_t*)((char*)ws + L.race_job);
   A.race_part = (sv::RacePart*)((char*)ws + L.race_part);
+  A.race_zn = (double*)((char*)ws + L.race_zn);
+  A.block_w = (double*)((char*)ws + L.block_w);
+  A.block = (sp->flags & SV_BLOCK_VERIFY) ? 1 : 0;
   A.check = (sp->flags & SV_CHECK) ? (const int32_t*)ws : nullptr;
   return A;
 }
@@ -301,7 +306,8 @@ int32_t spec_verify_rejection_sample(const void* target_logits, sv_dtype dt, int
   if (A.check && (rc = launch_check(qo_indptr, num_requests, num_rows, workspace, s))) return rc;
   if (num_rows > 0) launch(0, sv::row_pass_kernel, dim3(num_rows), dim3(sv::kRowBlock), s, A);
   if ((rc = check_launch("row pass"))) return rc;
-  launch(1, sv::finalize_kernel, dim3(num_requests), dim3(sv::kRowBlock), s, A);
+  launch(1, A.block ? sv::finalize_block_kernel : sv::finalize_kernel, dim3(num_requests),
+         dim3(sv::kRowBlock), s, A);
   if ((rc = check_launch("finalize"))) return rc;
   if (A.race_segs > 0) {
     const int items = A.race_segs * num_requests;

@@ -50,6 +50,10 @@ struct VerifyArgs {
   int32_t race_segs;
   int32_t* race_job;      // [num_requests]: 2 * row + residual, or -1
   RacePart* race_part;    // [num_requests, race_segs]
+  double* race_zn;        // [num_requests]: Z_N the split race divides by
+  // block verification of sampled requests (0: the token rule)
+  int32_t block;
+  double* block_w;        // [num_rows, 2]: block weight p_i and test bound h_i per row
   // every row-pass workgroup is resident at once: rows on one CU are kept
   // level by progress-based wave priorities
   int32_t level;
@@ -87,6 +91,7 @@ __global__ void diagnostics_kernel(const RowRec* rec, int32_t rows, double* zk, 
                                    double* pd, int32_t* mode);
 __global__ void row_pass_kernel(VerifyArgs A);
 __global__ void finalize_kernel(VerifyArgs A);
+__global__ void finalize_block_kernel(VerifyArgs A);
 __global__ void race_segment_kernel(VerifyArgs A);
 __global__ void race_finish_kernel(VerifyArgs A);
 __global__ void build_out_kernel(VerifyArgs A, BuildOutArgs B);

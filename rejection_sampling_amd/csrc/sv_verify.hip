@@ -1415,7 +1415,9 @@ __device__ __forceinline__ void row_pass(const VerifyArgs& A, RowShared& sh) {
   // the token this row emits if it is its request's emit row: after a
   // rejection (residual race; p for an out-of-range draft) or as the bonus
   const bool rejected = tested && !(out.flags & kRecAccept);
-  if (rejected || (!A.build && j == cap_eff)) {
+  // (a block-verified request's token depends on the whole block: its
+  // finalize races it)
+  if ((rejected || (!A.build && j == cap_eff)) && !A.block) {
     bool empty = false;
     if (vec_mode) {
       out.sample = wave_kept_race(kk, rejected && d_ok, A.seed, rid, pos0 + (uint32_t)j, empty);
@@ -1539,7 +1541,7 @@ __device__ __forceinline__ void resolve_pending(const VerifyArgs& A, int i, int 
   }
   // the emitted token if this row is its request's emit row (listed sets only)
   const bool rejected = tested && !(out.flags & kRecAccept);
-  if (listed && (rejected || bonus)) {
+  if (listed && (rejected || bonus) && !A.block) {
     bool empty = false;
     const float* qrow = A.draft_probs + (size_t)i * (size_t)A.ld_q;
     out.sample = block_kept_race(out.nkeep, out.m, out.zn, T, qrow, rejected && d_ok, A.seed,
@@ -1848,7 +1850,8 @@ __device__ __forceinline__ void race_segment(const VerifyArgs& A, int r, int sg,
   const void* row = (const char*)A.logits + (size_t)is * (size_t)A.ld_logits * (DT == 1 ? 2 : 4);
   const float* qrow = A.draft_probs + (size_t)is * (size_t)A.ld_q;
   const bool range = rr.mode == kModeRange;
-  RaceBounds rb(rr.m, rr.zn, T, range ? rr.bkey : 0u, range ? rr.tie_cut : 0x7FFFFFFF,
+  const double zn = A.race_zn[r];  // Z_N, or Z_N / p_tau for a block-verified residual
+  RaceBounds rb(rr.m, zn, T, range ? rr.bkey : 0u, range ? rr.tie_cut : 0x7FFFFFFF,
                 residual, qrow, seed, rid, pos);
   const RowSplit<DT> sp(row, V);
   const int v0 = (int)((long long)sp.nvec * sg / S);
@@ -1924,7 +1927,7 @@ __device__ __forceinline__ void race_segment(const VerifyArgs& A, int r, int sg,
       if (nc <= kCandCap) {
         for (int t = tid; t < nc; t += kBlock) {
           const int v = cand[t];
-          race_exact(Vec<DT>::load1(row, v), v, rr.m, rr.zn, Td, qrow, residual, seed, rid, pos, b);
+          race_exact(Vec<DT>::load1(row, v), v, rr.m, zn, Td, qrow, residual, seed, rid, pos, b);
         }
       } else {
         // more candidates than the list holds: every element of the segment
@@ -1936,7 +1939,7 @@ __device__ __forceinline__ void race_segment(const VerifyArgs& A, int r, int sg,
           const float x = Vec<DT>::load1(row, v);
           float lo, up;
           if (rb.bounds(x, v, B, lo, up) && up >= B)
-            race_exact(x, v, rr.m, rr.zn, Td, qrow, residual, seed, rid, pos, b);
+            race_exact(x, v, rr.m, zn, Td, qrow, residual, seed, rid, pos, b);
         }
       }
       break;
@@ -1955,7 +1958,7 @@ __device__ __forceinline__ void race_segment(const VerifyArgs& A, int r, int sg,
       const int v = t == 0 ? t2.id1 : t2.id2;
       const float u = t == 0 ? t2.up1 : t2.up2;
       if (v < 0 || !(u >= B)) continue;
-      race_exact(Vec<DT>::load1(row, v), v, rr.m, rr.zn, Td, qrow, residual, seed, rid, pos, b);
+      race_exact(Vec<DT>::load1(row, v), v, rr.m, zn, Td, qrow, residual, seed, rid, pos, b);
     }
     break;
   }
@@ -2028,8 +2031,201 @@ __device__ int list_race(const ListEntry* L, const RowRec& rr, float T, const fl
   return w.key > 0.0 ? w.id : -1;
 }
 
-// ------------------------------------------------------- finalize kernel
+// ------------------------------------------------ block verification
+// Test bound of one block position from its residual mass A and weight p.
+__device__ __forceinline__ double block_bound(double a, double p) {
+  const double den = a + 1.0 - p;
+  return den > 0.0 ? a / den : 1.0;  // 0 / 0: p = 1 and the row's p and q agree
+}
+
+// Residual mass sum max(w p(x) - q(x), 0) of this thread's share of a row whose
+// kept set is the whole row or a key range (every thread must call it: the
+// ranked walk synchronises the block).
 template <int DT>
+__device__ double row_residual_mass(const VerifyArgs& A, int i, const RowRec& rr, double w,
+                                    double Td, RowShared& sh) {
+  const void* row = (const char*)A.logits + (size_t)i * (size_t)A.ld_logits * (DT == 1 ? 2 : 4);
+  const float* qrow = A.draft_probs + (size_t)i * (size_t)A.ld_q;
+  const int V = A.vocab;
+  double a = 0.0;
+  auto term = [&](float x, int v) {
+    const double pv = exp(((double)x - (double)rr.m) / Td) / rr.zn;
+    a += fmax(w * pv - (double)qrow[v], 0.0);
+  };
+  if (rr.mode == kModeRange && !(rr.flags & kRecTieCut)) {
+    const uint32_t bkey = rr.bkey;
+    const int nb = rr.nb;
+    for_each_element_ranked<DT>(
+        row, V, [&](float x) { return fkey(x) == bkey; },
+        [&](float x, int v, int rank) {
+          const uint32_t k = fkey(x);
+          if (k > bkey || (k == bkey && rank < nb)) term(x, v);
+        },
+        sh);
+  } else {
+    const bool range = rr.mode == kModeRange;
+    const uint32_t bkey = rr.bkey;
+    const int cut = rr.tie_cut;
+    for_each_element<DT>(row, V, [&](float x, int v) {
+      if (range) {
+        const uint32_t k = fkey(x);
+        if (!(k > bkey || (k == bkey && v < cut))) return;
+      }
+      term(x, v);
+    });
+  }
+  return a;
+}
+
+// Block verification of one sampled request (Sun, Mendlovic, Leviathan,
+// Aharoni, Beirami, Ro, Suresh, "Block Verification Accelerates Speculative
+// Decoding") over its G verified positions, rows s..s+G, every row resolved.
+// Block weights p_0 = 1, p_i = min(p_{i-1} p(d)/q(d), 1) at row i - 1; the test
+// of position i is u_{i-1} < h_i with h_i = A_i / (A_i + 1 - p_i), A_i the
+// residual mass of row i at weight p_i (h_G = p_G); tau = the last position
+// passed.  The token comes from row tau: the residual max(p_tau p - q, 0) (raced
+// as max(p' - q, 0) with p' over Z_N / p_tau), or p when tau = G or row tau's
+// draft is out of range.  p_i and h_i go to the workspace (block_w).
+template <int DT>
+__device__ void block_finalize(const VerifyArgs& A, RowShared& sh, int r, int s, int nr, int G) {
+  const int tid = threadIdx.x;
+  const int V = A.vocab;
+  const float T = A.temperature[r];
+  const double Td = T;
+  const uint32_t rid = A.request_id ? A.request_id[r] : (uint32_t)r;
+  const uint32_t pos0 = A.position0 ? A.position0[r] : 0u;
+  double* bw = A.block_w;
+  double* ratio = (double*)sh.buf;  // one chunk of ratios
+  // weights: the ratios of a chunk of positions gathered in parallel, their
+  // clamped running product by thread 0
+  double p = 1.0;
+  if (tid == 0) bw[2 * (size_t)s] = 1.0;
+  for (int c0 = 0; c0 < G; c0 += kBlock) {
+    const int j = c0 + tid;
+    if (j < G) {
+      const int d = A.draft_tokens[s + j];
+      double rt = 0.0;
+      if (d >= 0 && d < V) {
+        const double pb = A.rec[s + j].pd;
+        const double q = (double)A.draft_probs[(size_t)(s + j) * (size_t)A.ld_q + d];
+        rt = q > 0.0 ? pb / q : (pb > 0.0 ? __builtin_inf() : 0.0);
+      }
+      ratio[tid] = rt;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      const int n = G - c0 < kBlock ? G - c0 : kBlock;
+      for (int t = 0; t < n; ++t) {
+        p = p > 0.0 ? fmin(p * ratio[t], 1.0) : 0.0;
+        bw[2 * (size_t)(s + c0 + t + 1)] = p;
+      }
+    }
+    __syncthreads();
+  }
+  __threadfence_block();
+  __syncthreads();
+  // test bounds: listed rows one wave each, lanes over the kept entries
+  for (int i = 1 + wave_id(); i < G; i += kWaves) {
+    const RowRec rr = A.rec[s + i];
+    if (rr.mode != kModeList) continue;
+    const double w = bw[2 * (size_t)(s + i)];
+    const ListEntry* Lst = A.list + (size_t)(s + i) * kListCap;
+    const float* qrow = A.draft_probs + (size_t)(s + i) * (size_t)A.ld_q;
+    double a = 0.0;
+    for (int t = lane_id(); t < rr.nkeep; t += 64) {
+      const ListEntry le = Lst[t];
+      const double pv = exp(((double)le.x - (double)rr.m) / Td) / rr.zn;
+      a += fmax(w * pv - (double)qrow[le.idx], 0.0);
+    }
+    a = wave_sum_d(a);
+    if (lane_id() == 0) bw[2 * (size_t)(s + i) + 1] = block_bound(a, w);
+  }
+  // the other rows by the whole workgroup
+  for (int i = 1; i < G; ++i) {
+    const RowRec rr = A.rec[s + i];
+    if (rr.mode == kModeList) continue;
+    const double w = bw[2 * (size_t)(s + i)];
+    const double a = block_sum_d(row_residual_mass<DT>(A, s + i, rr, w, Td, sh), sh.dscr);
+    if (tid == 0) bw[2 * (size_t)(s + i) + 1] = block_bound(a, w);
+    __syncthreads();
+  }
+  if (tid == 0 && G > 0) bw[2 * (size_t)(s + G) + 1] = bw[2 * (size_t)(s + G)];
+  __threadfence_block();
+  __syncthreads();
+  // the last position passed
+  int last = 0;
+  for (int i = 1 + tid; i <= G; i += kBlock) {
+    const double u = accept_uniform(A.seed, rid, pos0 + (uint32_t)(i - 1));
+    if (u < bw[2 * (size_t)(s + i) + 1]) last = i;
+  }
+  const int tau = (int)block_max_u64((uint64_t)last, sh.uscr);
+  // the emitted token of row tau
+  const int is = s + tau;
+  const RowRec rr = A.rec[is];
+  const int dtau = tau < G ? A.draft_tokens[is] : -1;
+  bool residual = tau < G && dtau >= 0 && dtau < V;
+  bool resid_empty = false;
+  const double wt = bw[2 * (size_t)is];
+  if (residual && !(wt > 0.0)) {  // zero weight: the residual is empty
+    residual = false;
+    resid_empty = true;
+  }
+  RowRec rs = rr;
+  if (residual) rs.zn = rr.zn / wt;
+  const float* qrow = A.draft_probs + (size_t)is * (size_t)A.ld_q;
+  const uint32_t pos = pos0 + (uint32_t)tau;
+  int sample;
+  int job = -1;
+  if (rr.mode == kModeList) {
+    const ListEntry* Lst = A.list + (size_t)is * kListCap;
+    sample = list_race(Lst, rs, T, qrow, residual, A.seed, rid, pos, sh);
+    if (residual && sample < 0) {
+      resid_empty = true;
+      sample = list_race(Lst, rr, T, qrow, false, A.seed, rid, pos, sh);
+    }
+  } else if (A.race_segs > 0 &&
+             (rr.mode == kModeAll || (rr.mode == kModeRange && (rr.flags & kRecTieCut)))) {
+    job = 2 * is + (residual ? 1 : 0);
+    if (tid == 0) A.race_zn[r] = rs.zn;
+    sample = -1;
+  } else {
+    const void* row = (const char*)A.logits + (size_t)is * (size_t)A.ld_logits * (DT == 1 ? 2 : 4);
+    auto race = [&](const RowRec& rx, bool resid) {
+      int smp = -2;
+      if (rx.mode == kModeAll || (rx.mode == kModeRange && (rx.flags & kRecTieCut)))
+        smp = stream_race_all<DT>(row, V, rx.m, rx.zn, rx.mode == kModeRange ? rx.bkey : 0u,
+                                  rx.mode == kModeRange ? rx.tie_cut : 0x7FFFFFFF, T, qrow, resid,
+                                  A.seed, rid, pos, sh);
+      if (smp == -2) smp = stream_race<DT>(row, V, rx, T, qrow, resid, A.seed, rid, pos, sh);
+      return smp;
+    };
+    sample = race(rs, residual);
+    if (residual && sample < 0) {
+      resid_empty = true;
+      sample = race(rr, false);
+    }
+  }
+  for (int j = tid; j < nr; j += kBlock) {
+    const int i = s + j;
+    A.out_tokens[i] = j < tau ? A.draft_tokens[i] : (j == tau ? sample : -1);
+    if (A.row_flags) {
+      uint8_t f = 0;
+      if (j < G && accept_uniform(A.seed, rid, pos0 + (uint32_t)j) < bw[2 * (size_t)(i + 1) + 1])
+        f |= 1;
+      if (j == tau) f |= 2;
+      if (j == tau && resid_empty) f |= 32;
+      A.row_flags[i] = f;
+    }
+  }
+  if (tid == 0) {
+    A.accept_len[r] = tau;
+    A.next_token[r] = sample;
+    if (A.race_segs > 0) A.race_job[r] = job;
+  }
+}
+
+// ------------------------------------------------------- finalize kernel
+template <int DT, bool BLK>
 __device__ __forceinline__ void finalize(const VerifyArgs& A, RowShared& sh) {
   const int r = blockIdx.x;
   const int tid = threadIdx.x;
@@ -2067,9 +2263,11 @@ __device__ __forceinline__ void finalize(const VerifyArgs& A, RowShared& sh) {
     int cv = A.verify_cap[r];
     cap_eff = cv < 0 ? 0 : (cv > gamma ? gamma : cv);
   }
+  // block verification (its own kernel instantiation) for sampled requests
+  const bool blk = BLK && A.temperature && A.temperature[r] > 0.0f;
   // fast path: every record read in one round by wave 0; taken when no row
   // is pending and the emit row's token is already known
-  if (nr <= 64) {
+  if (nr <= 64 && !blk) {
     if (wave_id() == 0) {
       const int j = lane_id();
       const bool in = j < nr;
@@ -2111,6 +2309,12 @@ __device__ __forceinline__ void finalize(const VerifyArgs& A, RowShared& sh) {
   for (int j = 0; j <= cap_eff; ++j) {
     if (A.rec[s + j].mode == kModePending)
       resolve_pending<DT>(A, s + j, r, j, j < cap_eff, j == cap_eff, sh);
+  }
+  if constexpr (BLK) {
+    if (blk) {
+      block_finalize<DT>(A, sh, r, s, nr, cap_eff);
+      return;
+    }
   }
   // accepted prefix: first row j < cap_eff whose test rejected (wave 0 ballots)
   if (wave_id() == 0) {
@@ -2154,6 +2358,7 @@ __device__ __forceinline__ void finalize(const VerifyArgs& A, RowShared& sh) {
     } else if (A.race_segs > 0 &&
                (rr.mode == kModeAll || (rr.mode == kModeRange && (rr.flags & kRecTieCut)))) {
       job = 2 * is + (residual ? 1 : 0);
+      if (tid == 0) A.race_zn[r] = rr.zn;
       sample = -1;
     } else {
       auto race = [&](bool resid) {
@@ -2194,8 +2399,14 @@ __device__ __forceinline__ void finalize(const VerifyArgs& A, RowShared& sh) {
 
 __global__ __launch_bounds__(kBlock) void finalize_kernel(VerifyArgs A) {
   __shared__ RowShared sh;
-  if (A.dtype == 1) finalize<1>(A, sh);
-  else finalize<0>(A, sh);
+  if (A.dtype == 1) finalize<1, false>(A, sh);
+  else finalize<0, false>(A, sh);
+}
+
+__global__ __launch_bounds__(kBlock) void finalize_block_kernel(VerifyArgs A) {
+  __shared__ RowShared sh;
+  if (A.dtype == 1) finalize<1, true>(A, sh);
+  else finalize<0, true>(A, sh);
 }
 
 // Grid-stride over the (request, segment) items of the requests that have a

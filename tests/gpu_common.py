@@ -63,21 +63,24 @@ def make_drafts(w, qo, threads=None):
     return q, d
 
 
-def oracle_verify(w, qo, drafts, q, verify_cap=None, requests=None, threads=None):
+def oracle_verify(w, qo, drafts, q, verify_cap=None, requests=None, threads=None, block=False):
     return svref.parallel_rejection_sample(w.logits, qo, drafts, q, w.temperature, w.top_k,
                                            w.top_p, w.request_id, w.position0, w.seed,
                                            verify_cap=verify_cap, requests=requests,
-                                           threads=threads)
+                                           threads=threads, block=block)
 
 
 def gpu_verify(w, qo, drafts, q, verify_cap=None, all_greedy=False, list_bounded=None,
-               diagnostics=False):
+               diagnostics=False, block=False):
     """One verify call through the C ABI; with diagnostics, also the per-row
-    records (Z_K, Z_N, p(d), mode) the call left in the workspace."""
+    records (Z_K, Z_N, p(d), mode) the call left in the workspace; block:
+    block verification (SV_BLOCK_VERIFY)."""
     lg = dev_logits(w.logits)
     qt = dev_f32(q) if q is not None else None
-    out = B.rejection_sample(lg, dev_i32(qo), dev_i32(drafts), qt,
-                             params_for(w, all_greedy, list_bounded),
+    prm = params_for(w, all_greedy, list_bounded)
+    if block:
+        prm.s.flags |= B.SV_BLOCK_VERIFY
+    out = B.rejection_sample(lg, dev_i32(qo), dev_i32(drafts), qt, prm,
                              dev_i32(verify_cap) if verify_cap is not None else None)
     res = {k: v for k, v in out.items()}
     if diagnostics:
@@ -86,8 +89,10 @@ def gpu_verify(w, qo, drafts, q, verify_cap=None, all_greedy=False, list_bounded
     return {k: v.cpu().numpy() for k, v in res.items()}
 
 
-def compare_verify(gpu, ref, qo, requests=None, cap=None, label=""):
+def compare_verify(gpu, ref, qo, requests=None, cap=None, label="", block=False):
     """Check GPU verify outputs against the oracle under the near-tie rules.
+    Under block verification the accepted length is the last position passed,
+    so a length mismatch is explained by a near tie at any tested position.
     Returns (number of mismatching requests, flag counts)."""
     qo = np.asarray(qo)
     R = len(qo) - 1
@@ -122,6 +127,9 @@ def compare_verify(gpu, ref, qo, requests=None, cap=None, label=""):
         # the first difference must be explained at the deciding position
         j = min(ga, ra)
         expl = False
+        if block and ga != ra and np.any(rf[:cap_eff] & (svref.ROW_NEAR_RATIO |
+                                                            svref.ROW_NEAR_TOPP)):
+            expl = True
         if j < e - s:
             f = rf[j]
             if ga != ra and f & (svref.ROW_NEAR_RATIO | svref.ROW_NEAR_TOPP):
