@@ -56,11 +56,15 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
+def traffic_file(workload: str) -> str:
+    return TRAFFIC_FILE if workload == "c3" else TRAFFIC_FILE.replace(".json", f"_{workload}.json")
+
+
+def measured_traffic(workload: str = "c3"):
     """HBM bytes per row-pass launch from the committed counter runs, or None
     when the kernels changed since the counters were taken."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic_file(workload)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -69,44 +73,61 @@ def measured_traffic():
     return t.get("bytes_per_launch")
 
 
-def _counter_means(path, counter):
-    """Mean value per dispatch of `counter` for the row pass and for the
-    512 MiB calibration copy, from a rocprofv3 counter_collection.csv."""
+def _counter_means(path, counter, rows):
+    """Mean value per dispatch of `counter` for the verify row pass (its grid
+    holds `rows` workgroups; the draft-build dispatches of the input setup
+    are left out), for the 512 MiB calibration copy and for the 512 MiB
+    calibration sum (read only), from a rocprofv3 counter_collection.csv."""
     import csv
-    rp, cp = [], []
+    recs = []
     with open(path) as f:
         for r in csv.DictReader(f):
-            if r["Counter_Name"] != counter:
-                continue
-            name, v = r["Kernel_Name"], float(r["Counter_Value"])
-            if "row_pass_kernel" in name:
-                rp.append(v)
-            elif "copyBuffer" in name and int(r["Grid_Size"]) > 65536:
-                cp.append(v)
-    if not rp or not cp:
-        raise SystemExit(f"{path}: no {counter} values for the row pass or the copy kernel")
-    return sum(rp) / len(rp), sum(cp) / len(cp), len(rp)
+            if r["Counter_Name"] == counter:
+                recs.append((int(r["Dispatch_Id"]), r["Kernel_Name"], int(r["Grid_Size"]),
+                             float(r["Counter_Value"])))
+    recs.sort()
+    # the calibration copy, then the first reduction after it (the sum); the
+    # verify row passes come after them (earlier row passes are the input
+    # setup's draft builds)
+    copy_at = next((i for i, (_, n, g, _v) in enumerate(recs)
+                    if "copyBuffer" in n and g > 65536), None)
+    if copy_at is None:
+        raise SystemExit(f"{path}: no {counter} value for the calibration copy")
+    cp = recs[copy_at][3]
+    sm = next((v for _, n, _g, v in recs[copy_at + 1:] if "reduce_kernel" in n), None)
+    rp = [v for _, n, g, v in recs[copy_at + 1:] if "row_pass_kernel" in n and g == rows * 256]
+    if not rp or sm is None:
+        raise SystemExit(f"{path}: no {counter} values for the row pass or the calibration sum")
+    return sum(rp) / len(rp), cp, sm, len(rp)
 
 
-def summarize_counters(fetch_csv, write_csv):
+def summarize_counters(fetch_csv, write_csv, workload="c3"):
     """HBM bytes per row-pass launch: each counter (KiB per dispatch) is scaled
-    by what it reads for a plain copy of known size (512 MiB read + written)."""
+    by what it reads for a plain copy of known size (512 MiB read + written);
+    a read-only sum of 512 MiB checks the read scale on another kernel."""
+    R, nb, V, _ = WORKLOADS[workload]
+    rows = 1792 if workload == "c5" else R * nb
+    alg = rows * V * (4 if workload == "c1" else 2)
     copy_kib = float(512 << 10)
-    f_rp, f_cp, n_f = _counter_means(fetch_csv, "FETCH_SIZE")
-    w_rp, w_cp, n_w = _counter_means(write_csv, "WRITE_SIZE")
+    f_rp, f_cp, f_sm, n_f = _counter_means(fetch_csv, "FETCH_SIZE", rows)
+    w_rp, w_cp, _, n_w = _counter_means(write_csv, "WRITE_SIZE", rows)
     f_scale, w_scale = copy_kib / f_cp, copy_kib / w_cp
     fetch_b = f_rp * f_scale * 1024.0
     write_b = w_rp * w_scale * 1024.0
-    out = {"source_hash": kernel_source_hash(),
+    out = {"workload": workload, "source_hash": kernel_source_hash(),
            "bytes_per_launch": round(fetch_b + write_b),
            "fetch_bytes": round(fetch_b), "write_bytes": round(write_b),
            "fetch_kib_raw": round(f_rp, 3), "write_kib_raw": round(w_rp, 3),
            "copy_fetch_kib_raw": round(f_cp, 3), "copy_write_kib_raw": round(w_cp, 3),
+           "sum_fetch_kib_raw": round(f_sm, 3),
            "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+           "sum_fetch_scale": round(copy_kib / f_sm, 4),
            "dispatches": [n_f, n_w],
-           "algorithmic_bytes": ROWS * VOCAB * 2}
-    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
-    with open(TRAFFIC_FILE, "w") as f:
+           "algorithmic_bytes": alg,
+           "ratio_to_algorithmic": round((fetch_b + write_b) / alg, 4)}
+    path = traffic_file(workload)
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
     print(json.dumps(out))
@@ -308,10 +329,11 @@ def main():
                     help="also run a plain 512 MiB device copy (counter calibration)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
-                         "script with --calibrate-copy into profiles/row_pass_traffic.json")
+                         "script with --calibrate-copy into profiles/row_pass_traffic.json "
+                         "(c3) or profiles/row_pass_traffic_<workload>.json")
     args = ap.parse_args()
     if args.summarize_counters:
-        summarize_counters(*args.summarize_counters)
+        summarize_counters(*args.summarize_counters, workload=args.workload)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the verify step "
@@ -352,10 +374,12 @@ def main():
         calls[i % len(calls)]()
 
     if args.calibrate_copy:
-        a = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        a = torch.zeros(512 << 20, dtype=torch.uint8, device="cuda")
         b = torch.empty_like(a)
         torch.cuda.synchronize()
         b.copy_(a)   # a plain device copy of known size (runtime copy kernel)
+        torch.cuda.synchronize()
+        a.view(torch.float32).sum()   # a read-only pass over the same 512 MiB
         torch.cuda.synchronize()
         del a, b
 
@@ -456,7 +480,7 @@ def main():
         "config": config,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": measured_traffic() if wl == "c3" else None,
+                     "traffic": measured_traffic(wl),
                      "kernel": "row_pass_kernel", "kernel_ms": round(kern_ms, 5),
                      "algorithmic_bytes": alg_bytes,
                      # the same bytes over the whole step (every launch of the call)
