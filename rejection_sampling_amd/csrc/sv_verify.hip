@@ -811,46 +811,165 @@ __device__ __forceinline__ void resolve_pending(const VerifyArgs& A, int i, int 
 // elements above T* written to sh.buf[0, n) as entries; returns n, or -1 when
 // they do not fit (the row then takes the exact path).  Block level.
 constexpr int kMatVecPerThread = 8;
-template <int DT>
-__device__ __forceinline__ int topp_certified(const void* row, int V, RowShared& sh) {
-  constexpr int PE = Vec<DT>::kEpv;
-  const RowSplit<DT> sp(row, V);
-  const int tid = threadIdx.x, w = wave_id();
-  float tstar = sh.wtau[0];
+
+// Fixed-point mass walk over bf16 values by their 16-bit order codes: counts
+// per code in the window [code0, code0 + kCodeBins) (one 32-bit LDS atomic per
+// item, spread over the codes), the mass of a code being its count times the
+// fixed-point weight of its value (as an item-by-item sum would give).  Wave 0
+// walks the bins from the top to the first code where the running mass
+// reaches target.  Block level; the counts live in sh.mhist.  Returns false
+// when an item falls outside the window or the items stay below target;
+// otherwise sets code, the mass and item count above it, and its count.
+constexpr int kCodeBins = 512;
+struct CodeWalk {
+  uint32_t code;
+  double above;
+  int cnt_above, count;
+};
+// The walk over counts already in sh.mhist (block level).
+__device__ __forceinline__ bool code_walk_bins(RowShared& sh, uint32_t code0, float m, float c,
+                                               double scale, double target, CodeWalk& o) {
+  const uint32_t* cnt = (const uint32_t*)sh.mhist;
+  if (wave_id() == 0) {
+    const int l = lane_id();
+    constexpr int kPer = kCodeBins / 64;
+    double h[kPer];
+    int cc[kPer];
+    double loc = 0.0;
+    int cloc = 0;
 #pragma unroll
-  for (int q = 1; q < kWaves; ++q) tstar = fmaxf(tstar, sh.wtau[q]);
-  const uint32_t tkey = fkey(tstar);
-  {
-    uint64_t* seg = sh.buf + w * kWaveCap;
-    int nw = sh.wcount[w];
-    nw = tkey == 0xFFFFFFFFu ? 0 : wave_keep_ge(seg, nw, tkey + 1u);
-    __syncthreads();  // every wave has read its count
-    if (lane_id() == 0) sh.wcount[w] = nw;
+    for (int q = 0; q < kPer; ++q) {
+      const int b = kCodeBins - 1 - kPer * l - q;  // lane 0 holds the top codes
+      cc[q] = (int)cnt[b];
+      h[q] = 0.0;
+      if (cc[q] > 0) {
+        const float v = bf16_code_value(code0 + (uint32_t)b);
+        const unsigned long long wf = (unsigned long long)((double)exp2f((v - m) * c) * scale);
+        h[q] = (double)((unsigned long long)cc[q] * wf);
+      }
+      loc += h[q];
+      cloc += cc[q];
+    }
+    const double incl = wave_inclusive_sum(loc);
+    const int cincl = wave_inclusive_sum(cloc);
+    const double excl = incl - loc;
+    const uint64_t mk = __ballot(excl < target && target <= incl);
+    if (l == 0) sh.sel_exact = mk ? 1 : 0;
+    if (mk) {
+      const int src = __ffsll((unsigned long long)mk) - 1;
+      if (l == src) {
+        double acc = excl;
+        int cacc = cincl - cloc, q = 0;
+        while (q < kPer - 1 && !(acc + h[q] >= target)) {
+          acc += h[q];
+          cacc += cc[q];
+          ++q;
+        }
+        sh.sel_digit = kCodeBins - 1 - kPer * l - q;
+        sh.zn_shared = acc;
+        sh.sel_need = cacc;
+        sh.count = cc[q];
+      }
+    }
   }
   __syncthreads();
-  int base[kWaves];
-  int nv = 0;
-#pragma unroll
-  for (int q = 0; q < kWaves; ++q) {
-    base[q] = nv;
-    nv += sh.wcount[q];
+  if (!sh.sel_exact) return false;
+  o.code = code0 + (uint32_t)sh.sel_digit;
+  o.above = sh.zn_shared;
+  o.cnt_above = sh.sel_need;
+  o.count = sh.count;
+  __syncthreads();
+  return true;
+}
+
+// Counts of the items' codes (key16_at(t) for t < nitems; 0xFFFFFFFF skips an
+// item), then the walk.
+template <class KeyAt>
+__device__ __forceinline__ bool code_walk(RowShared& sh, KeyAt&& key16_at, int nitems,
+                                          uint32_t code0, float m, float c, double scale,
+                                          double target, CodeWalk& o) {
+  uint32_t* cnt = (uint32_t*)sh.mhist;
+  for (int b = threadIdx.x; b < kCodeBins; b += kBlock) cnt[b] = 0u;
+  if (threadIdx.x == 0) sh.found = 0;
+  __syncthreads();
+  for (int t = threadIdx.x; t < nitems; t += kBlock) {
+    const uint32_t k = key16_at(t);
+    if (k == 0xFFFFFFFFu) continue;
+    const uint32_t b = k - code0;
+    if (b < (uint32_t)kCodeBins) atomicAdd(&cnt[b], 1u);
+    else sh.found = 1;  // outside the window
   }
-  if (nv > kBlock * kMatVecPerThread) return -1;
+  __syncthreads();
+  if (sh.found) return false;
+  return code_walk_bins(sh, code0, m, c, scale, target, o);
+}
+
+// Lower bound on the top-p boundary from the candidate vectors' maxima (bf16
+// rows): the vectors whose maximum is at least v hold, in their maxima alone,
+// a mass M(v) that is at most the mass of all elements at least v, so when
+// M(v) reaches the target the boundary value is at least v.  The code walk
+// over the maxima of the entries above T* gives the largest such v.  Every
+// element the selection needs is then in a vector whose maximum reaches v.
+template <int DT>
+__device__ __forceinline__ int topp_certified(const void* row, int V, float m, float T, float P,
+                                              double Z, RowShared& sh, uint32_t& code_lo) {
+  constexpr int PE = Vec<DT>::kEpv;
+  const RowSplit<DT> sp(row, V);
+  const int tid = threadIdx.x;
+  float tstar = sh.wtau[0];
+  bool fits = sh.wcount[0] <= kTopPEnd;
+#pragma unroll
+  for (int q = 1; q < kWaves; ++q) {
+    tstar = fmaxf(tstar, sh.wtau[q]);
+    fits = fits && sh.wcount[q] <= kTopPEnd;
+  }
+  if (!fits) return -1;  // (segments end the stream with at most kTopPEnd entries)
+  const uint32_t tkey = fkey(tstar);
+  // elements at or above klo go to the selection: those above T*, or (bf16)
+  // those at or above the vector-maximum mass bound
+  uint32_t klo = tkey == 0xFFFFFFFFu ? 0xFFFFFFFFu : tkey + 1u;
+  code_lo = 0xFFFFFFFFu;
+  if (DT == 1 && tkey != 0xFFFFFFFFu) {
+    const uint32_t code0 = tkey >> 16;
+    const uint32_t cmax = fkey(m) >> 16;
+    if (cmax >= code0 && cmax - code0 < (uint32_t)kCodeBins) {
+      int lg = 0;
+      while ((1ll << lg) < (long long)V + 1) ++lg;
+      const double scale = ldexp(1.0, 62 - lg);
+      auto vkey16 = [&](int g) -> uint32_t {
+        const int q = g / kTopPEnd, j = g - q * kTopPEnd;
+        if (j >= sh.wcount[q]) return 0xFFFFFFFFu;
+        const uint32_t key = (uint32_t)(sh.buf[q * kWaveCap + j] >> 32);
+        return key > tkey ? (key >> 16) : 0xFFFFFFFFu;
+      };
+      CodeWalk cw;
+      if (code_walk(sh, vkey16, kWaves * kTopPEnd, code0, m, kLog2e / T, scale,
+                    (double)P * Z * scale, cw)) {
+        klo = key_of_prefix(cw.code << 16, true);
+        code_lo = cw.code;
+      } else {
+        code_lo = code0;  // every element above T* has a code at least this
+      }
+    }
+  }
+  // fkey(x) >= klo, as a float compare (the next float above T* when no bound)
+  const float vlo = key_to_float(klo);
+  static_assert(kWaves * kTopPEnd == kBlock * kMatVecPerThread, "one re-read slot per entry");
   uint4 raw[kMatVecPerThread];
   int vid[kMatVecPerThread];
   int cnt = 0;
 #pragma unroll
   for (int r = 0; r < kMatVecPerThread; ++r) {
     const int g = r * kBlock + tid;
+    const int q = g / kTopPEnd, j = g - q * kTopPEnd;
     vid[r] = -1;
     raw[r] = make_uint4(0u, 0u, 0u, 0u);
-    if (g < nv) {
-      int q = 0;
-#pragma unroll
-      for (int t = 1; t < kWaves; ++t)
-        if (g >= base[t]) q = t;
-      vid[r] = entry_idx(sh.buf[q * kWaveCap + (g - base[q])]);
-      raw[r] = __ldg(sp.vbase + vid[r]);
+    if (j < sh.wcount[q]) {
+      const uint64_t e = sh.buf[q * kWaveCap + j];
+      if ((uint32_t)(e >> 32) >= klo) {
+        vid[r] = entry_idx(e);
+        raw[r] = __ldg(sp.vbase + vid[r]);
+      }
     }
   }
   // the unvectorised head and tail elements are candidates too
@@ -859,13 +978,13 @@ __device__ __forceinline__ int topp_certified(const void* row, int V, RowShared&
   const bool ts = tid >= 8 && tid - 8 < ntail;
   const int is = hs ? tid : sp.tail0 + tid - 8;
   const float xs = (hs || ts) ? Vec<DT>::load1(row, is) : 0.0f;
-  const bool sp_in = (hs || ts) && xs > tstar;
+  const bool sp_in = (hs || ts) && xs >= vlo;
 #pragma unroll
   for (int r = 0; r < kMatVecPerThread; ++r) {
     float x[PE];
     Vec<DT>::unpack(raw[r], x);
 #pragma unroll
-    for (int e = 0; e < PE; ++e) cnt += (vid[r] >= 0 && x[e] > tstar) ? 1 : 0;
+    for (int e = 0; e < PE; ++e) cnt += (vid[r] >= 0 && x[e] >= vlo) ? 1 : 0;
   }
   cnt += sp_in ? 1 : 0;
   int total;
@@ -878,7 +997,7 @@ __device__ __forceinline__ int topp_certified(const void* row, int V, RowShared&
     const int id0 = sp.head + vid[r] * PE;
 #pragma unroll
     for (int e = 0; e < PE; ++e)
-      if (vid[r] >= 0 && x[e] > tstar) sh.buf[pos++] = make_entry(x[e], id0 + e);
+      if (vid[r] >= 0 && x[e] >= vlo) sh.buf[pos++] = make_entry(x[e], id0 + e);
   }
   if (sp_in) sh.buf[pos++] = make_entry(xs, is);
   __syncthreads();
@@ -889,14 +1008,16 @@ __device__ __forceinline__ int topp_certified(const void* row, int V, RowShared&
 // the boundary value by a fixed-point mass walk over 8-bit digits of the order
 // key (exact integer sums, no sort), ties at the boundary by id, then the kept
 // entries compacted to sh.buf[0, nkeep) (sorted only when `sorted`).  Returns
-// false when the certified mass does not reach P * Z.
+// false when the certified mass does not reach P * Z.  code_lo, when not
+// 0xFFFFFFFF, is a bf16 code at or below every entry's code.
 struct TopPOut {
   int nkeep, a;
   double zn, pd;
 };
 template <int DT>
 __device__ __forceinline__ bool topp_select(RowShared& sh, int n, float m, float T, float P,
-                                            double Z, int d, bool sorted, TopPOut& o) {
+                                            double Z, int d, bool sorted, uint32_t code_lo,
+                                            TopPOut& o) {
   constexpr bool kBf = DT == 1;
   const int tid = threadIdx.x;
   const float c = kLog2e / T;
@@ -907,16 +1028,41 @@ __device__ __forceinline__ bool topp_select(RowShared& sh, int n, float m, float
   auto wfx = [&](uint64_t e) {
     return (unsigned long long)((double)exp2f((entry_val(e) - m) * c) * scale);
   };
-  double wsum = 0.0;
-  for (int t = tid; t < n; t += kBlock) wsum += (double)wfx(sh.buf[t]);
   const double target = (double)P * Z * scale;
-  if (block_sum_d(wsum, sh.dscr) < target) return false;
   unsigned long long* mh = (unsigned long long*)sh.mhist;
   uint32_t* ch = sh.whist[0];
   uint32_t prefix = 0, pmask = 0;
   double above = 0.0;
   int above_cnt = 0, avail = 0;
-  const int nlev = kBf ? 2 : 4;
+  int nlev = kBf ? 2 : 4;
+  bool walked = false;
+  if (kBf && n > 0) {
+    // one walk over the values' codes, in a window from the smallest code
+    uint32_t code0 = code_lo;
+    if (code0 == 0xFFFFFFFFu) {
+      uint32_t cmin = 0xFFFFu;
+      for (int t = tid; t < n; t += kBlock) {
+        const uint32_t k16 = (uint32_t)(sh.buf[t] >> 48);
+        cmin = k16 < cmin ? k16 : cmin;
+      }
+      code0 = (uint32_t)block_min_u64(cmin, sh.uscr);
+    }
+    CodeWalk cw;
+    if (code_walk(sh, [&](int t) { return (uint32_t)(sh.buf[t] >> 48); }, n, code0, m, c, scale,
+                  target, cw)) {
+      above = cw.above;
+      above_cnt = cw.cnt_above;
+      avail = cw.count;
+      prefix = cw.code << 16;
+      nlev = 0;
+      walked = true;
+    }
+  }
+  if (!walked) {
+    double wsum = 0.0;
+    for (int t = tid; t < n; t += kBlock) wsum += (double)wfx(sh.buf[t]);
+    if (block_sum_d(wsum, sh.dscr) < target) return false;
+  }
   for (int lev = 0; lev < nlev; ++lev) {
     const int shift = 24 - 8 * lev;
     for (int b = tid; b < 256; b += kBlock) { ch[b] = 0u; mh[b] = 0ull; }
@@ -1254,6 +1400,7 @@ __device__ __forceinline__ void row_pass(const VerifyArgs& A, RowShared& sh) {
   double pd = 0.0;
   bool exact = !buf_mode && !all_mode && !vec_mode;
   VecKept kk = {};
+  uint32_t cert_code0 = 0xFFFFFFFFu;  // lowest bf16 code of the certified elements (or unknown)
 
   if (vec_mode) {
     if (sh.woverflow) {
@@ -1294,7 +1441,7 @@ __device__ __forceinline__ void row_pass(const VerifyArgs& A, RowShared& sh) {
     if (sh.woverflow) {
       exact = true;
     } else if (topp_mode) {
-      n = topp_certified<DT>(row, V, sh);
+      n = topp_certified<DT>(row, V, m, T, P, Z, sh, cert_code0);
       if (n < 0) exact = true;
     } else {
       n = merge_segments(sh);
@@ -1307,7 +1454,7 @@ __device__ __forceinline__ void row_pass(const VerifyArgs& A, RowShared& sh) {
     }
     if (!exact && topp_mode) {
       TopPOut tp;
-      if (!topp_select<DT>(sh, n, m, T, P, Z, d_ok ? d : -1, A.build != 0, tp)) {
+      if (!topp_select<DT>(sh, n, m, T, P, Z, d_ok ? d : -1, A.build != 0, cert_code0, tp)) {
         exact = true;  // the certified candidates do not reach the top-p mass
       } else {
         out.a = tp.a;
