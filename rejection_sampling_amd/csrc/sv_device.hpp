@@ -93,8 +93,10 @@ __device__ __forceinline__ uint4 philox4x32_10(uint32_t k0, uint32_t k1, uint4 c
       k0 += W0;
       k1 += W1;
     }
-    const uint32_t lo0 = M0 * c.x, hi0 = __umulhi(M0, c.x);
-    const uint32_t lo1 = M1 * c.z, hi1 = __umulhi(M1, c.z);
+    // one 32 x 32 -> 64-bit product per multiplier (both halves at once)
+    const uint64_t p0 = (uint64_t)M0 * c.x, p1 = (uint64_t)M1 * c.z;
+    const uint32_t lo0 = (uint32_t)p0, hi0 = (uint32_t)(p0 >> 32);
+    const uint32_t lo1 = (uint32_t)p1, hi1 = (uint32_t)(p1 >> 32);
     c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
   }
   return c;

@@ -1848,11 +1848,8 @@ struct RaceBounds {
   }
   // the same with the element's draft probability q (residual rows) given
   __device__ __forceinline__ bool bounds(float x, int v, float q, float bl, float& lo, float& up) {
-    constexpr float kNegInf = -__builtin_huge_valf();
-    const float y = (x - m) * c - l2zn;  // log2 of p (residual) or of the relative weight
-    if (!(y + 24.0f + 2.0f * kEta >= bl)) return false;
-    const uint32_t key = fkey(x);
-    if (key < kmin || (key == kmin && v >= tie_cut)) return false;
+    float y;
+    if (!prefilter(x, v, bl, y)) return false;
     const uint32_t g = (uint32_t)v >> 2;
     if (g != gcache) {
       oc = philox4x32_10(k0, k1, make_uint4(pos, rid, 1u, g));
@@ -1860,12 +1857,44 @@ struct RaceBounds {
     }
     const uint32_t ln = (uint32_t)v & 3u;
     const uint32_t wv = ln == 0 ? oc.x : (ln == 1 ? oc.y : (ln == 2 ? oc.z : oc.w));
+    return from_word(y, wv, q, bl, lo, up);
+  }
+  // Generator block of group g (elements 4g .. 4g+3).
+  __device__ __forceinline__ uint4 words(uint32_t g) const {
+    return philox4x32_10(k0, k1, make_uint4(pos, rid, 1u, g));
+  }
+  // The checks that need no generator word: y = log2 of p (residual) or of
+  // the relative weight; false when the element is outside the kept range or
+  // cannot reach bl even with E at its smallest.
+  __device__ __forceinline__ bool prefilter(float x, int v, float bl, float& y) const {
+    y = (x - m) * c - l2zn;
+    if (!(y + 24.0f + 2.0f * kEta >= bl)) return false;
+    const uint32_t key = fkey(x);
+    return !(key < kmin || (key == kmin && v >= tie_cut));
+  }
+  // Bounds from the element's generator word wv.
+  __device__ __forceinline__ bool from_word(float y, uint32_t wv, float q, float bl, float& lo,
+                                           float& up) const {
+    constexpr float kNegInf = -__builtin_huge_valf();
     // E = -ln U >= 1 - U = D 2^-24 (D an integer in [1, 2^24)), so log2 E >=
     // floor(log2 D) - 24: an element that cannot reach bl even then is done
     // without the logarithms
     const uint32_t Dlt = 0x1000000u - (2u * (wv >> 9) + 1u);
-    const float e_lo = (float)(7 - (int)__clz(Dlt));
-    if (!(y + (residual ? 2.0e-4f : 0.0f) - e_lo + 2.0f * kEta >= bl)) return false;
+    const int e_lo = 7 - (int)__clz(Dlt);
+    if (!(y + (residual ? 2.0e-4f : 0.0f) - (float)e_lo + 2.0f * kEta >= bl)) return false;
+    float p32 = 0.0f, rhi = 0.0f;
+    if (residual) {
+      // the residual's upper bound with q, still without logarithms: the
+      // key is at most rhi / 2^e_lo (an exact scaling by a power of two
+      // while the result stays normal)
+      p32 = exp2f(y);
+      rhi = p32 * (1.0f + 2.0f * kRelP) - q;  // 2 kRelP: room for the rounding of the difference
+      if (!(rhi > 0.0f)) return false;
+      if (bl > -100.0f) {
+        const float kup = ldexpf(rhi, -e_lo);
+        if (kup < exp2f(bl - 2.0f * kEta)) return false;
+      }
+    }
     // log2 E, E = -ln U, within far less than kEta: a short series for U near 1
     const float U = (float)(2u * (wv >> 9) + 1u) * 0x1.0p-24f;
     const float dlt = 1.0f - U;  // exact
@@ -1878,10 +1907,7 @@ struct RaceBounds {
       return true;
     }
     if (!(y + 2.0e-4f - l2e + kEta >= bl)) return false;  // even with q = 0
-    const float p32 = exp2f(y);
-    const float rhi = p32 * (1.0f + kRelP) - q;
-    if (!(rhi > 0.0f)) return false;
-    const float rlo = p32 * (1.0f - kRelP) - q;
+    const float rlo = p32 * (1.0f - 2.0f * kRelP) - q;
     up = log2f(rhi) - l2e + kEta;
     lo = rlo > 0.0f ? log2f(rlo) - l2e - kEta : kNegInf;
     return true;
@@ -2022,6 +2048,18 @@ __device__ __forceinline__ void race_segment(const VerifyArgs& A, int r, int sg,
       if (slot < kCandCap) cand[slot] = v;
     }
   };
+  // visit with the element's generator word given
+  auto visit_w = [&](float x, int v, float q, uint32_t wv) {
+    float lo, up, y;
+    const float bl = second ? B : t2.best_lo;
+    if (!rb.prefilter(x, v, bl, y) || !rb.from_word(y, wv, q, bl, lo, up)) return;
+    if (!second) {
+      t2.add(lo, up, v);
+    } else if (up >= B) {
+      const int slot = atomicAdd(&sh.count, 1);
+      if (slot < kCandCap) cand[slot] = v;
+    }
+  };
   auto qload = [&](int vi, float* q) {
 #pragma unroll
     for (int e = 0; e < P; ++e) q[e] = (residual && vi < v1) ? qrow[sp.head + vi * P + e] : 0.0f;
@@ -2036,29 +2074,74 @@ __device__ __forceinline__ void race_segment(const VerifyArgs& A, int r, int sg,
     uint4 w2 = vi + 2 * kBlock < v1 ? __ldg(sp.vbase + vi + 2 * kBlock) : z;
     float q0[P];
     qload(vi, q0);
-    for (; vi < v1; vi += kBlock) {
+    // wave-uniform trip count (a wave runs while its first lane has a
+    // vector), so the bound can be shared across the wave after each vector
+    for (; vi - lane_id() < v1; vi += kBlock) {
       const uint4 w3 = vi + 3 * kBlock < v1 ? __ldg(sp.vbase + vi + 3 * kBlock) : z;
       float q1[P];
       qload(vi + kBlock, q1);
       float x[P];
       Vec<DT>::unpack(w0, x);
-      if (rb.vector_may_reach(vec_max<P>(x), second ? B : t2.best_lo)) {
-        const int e0 = sp.head + vi * P;
-        // one 32-bit word at a time (fewer live registers than all P at once)
+      const bool act = vi < v1 && rb.vector_may_reach(vec_max<P>(x), second ? B : t2.best_lo);
+      const int e0 = sp.head + vi * P;
+      if ((e0 & 3) == 0) {  // the same in every lane (the row's head offset)
+        // the vector is whole groups of four: each group's generator block
+        // once per vector (the same block in every lane, so the wave runs it
+        // once), one block live at a time
 #pragma unroll 1
-        for (int h = 0; h < 4; ++h) {
-          const uint32_t wd = h == 0 ? w0.x : (h == 1 ? w0.y : (h == 2 ? w0.z : w0.w));
+        for (int gh = 0; gh < P / 4; ++gh) {
+          if (!__ballot(act)) break;
+          const uint4 o = rb.words((uint32_t)(e0 >> 2) + (uint32_t)gh);
+          const uint32_t ws[4] = {o.x, o.y, o.z, o.w};
+          float xs[4], qs[4];
           if (DT == 1) {
-            const float qa = h == 0 ? q0[0] : (h == 1 ? q0[2] : (h == 2 ? q0[4] : q0[6 % P]));
-            const float qb = h == 0 ? q0[1] : (h == 1 ? q0[3] : (h == 2 ? q0[5] : q0[7 % P]));
-            visit(bf16_lo(wd), e0 + 2 * h, qa);
-            visit(bf16_hi(wd), e0 + 2 * h + 1, qb);
+            const uint32_t wa = gh == 0 ? w0.x : w0.z, wb = gh == 0 ? w0.y : w0.w;
+            xs[0] = bf16_lo(wa);
+            xs[1] = bf16_hi(wa);
+            xs[2] = bf16_lo(wb);
+            xs[3] = bf16_hi(wb);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) qs[t] = gh == 0 ? q0[t] : q0[(4 + t) % P];
           } else {
-            const float qa = h == 0 ? q0[0] : (h == 1 ? q0[1 % P] : (h == 2 ? q0[2 % P] : q0[3 % P]));
-            visit(__uint_as_float(wd), e0 + h, qa);
+            xs[0] = __uint_as_float(w0.x);
+            xs[1] = __uint_as_float(w0.y);
+            xs[2] = __uint_as_float(w0.z);
+            xs[3] = __uint_as_float(w0.w);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) qs[t] = q0[t % P];
+          }
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            if (act) visit_w(xs[t], e0 + 4 * gh + t, qs[t], ws[t]);
+        }
+      } else if (act) {
+        {
+          // a vector across group boundaries (rows that do not start on a
+          // group of four): each element's block on its own, no state kept
+          auto word_of = [&](int v) {
+            const uint4 o = rb.words((uint32_t)v >> 2);
+            const int ln = v & 3;
+            return ln == 0 ? o.x : (ln == 1 ? o.y : (ln == 2 ? o.z : o.w));
+          };
+#pragma unroll 1
+          for (int h = 0; h < 4; ++h) {
+            const uint32_t wd = h == 0 ? w0.x : (h == 1 ? w0.y : (h == 2 ? w0.z : w0.w));
+            if (DT == 1) {
+              const float qa = h == 0 ? q0[0] : (h == 1 ? q0[2] : (h == 2 ? q0[4] : q0[6 % P]));
+              const float qb = h == 0 ? q0[1] : (h == 1 ? q0[3] : (h == 2 ? q0[5] : q0[7 % P]));
+              visit_w(bf16_lo(wd), e0 + 2 * h, qa, word_of(e0 + 2 * h));
+              visit_w(bf16_hi(wd), e0 + 2 * h + 1, qb, word_of(e0 + 2 * h + 1));
+            } else {
+              const float qa = h == 0 ? q0[0] : (h == 1 ? q0[1 % P] : (h == 2 ? q0[2 % P] : q0[3 % P]));
+              visit_w(__uint_as_float(wd), e0 + h, qa, word_of(e0 + h));
+            }
           }
         }
       }
+      // every lane's best lower bound belongs to an element of this segment
+      // that its own lane keeps (or whose drop forces the second pass), so
+      // the wave's best is a valid filter for every lane
+      if (!second) t2.best_lo = wave_max_f(t2.best_lo);
       w0 = w1;
       w1 = w2;
       w2 = w3;
