@@ -238,12 +238,18 @@ int32_t spec_verify_plan_windows(const float* confidence, int64_t ld_conf, int32
  *              range is non-positive or non-finite
  *   theta      [1] fp64, device, written (NULL: skipped): Theta(budget), 0 with
  *              no table, NaN with an invalid one
- * R*B must be at most 4096.  One workgroup, no host synchronisation: the
- * budget stays on the device.  Errors (host-side checks, returned before any
- * launch): SV_ERR_SHAPE, SV_ERR_NULL. */
+ *   workspace  device scratch of at least spec_verify_workspace_bytes(0, 1, R,
+ *              block) bytes, 256-byte aligned; needed only when R*B > 4096
+ *              (may be NULL otherwise); its contents afterwards are meaningless
+ * R*B must be at most 2^20.  Up to 4096 positions one workgroup sorts the
+ * survivals in LDS; beyond, three launches (tile sorts, a rank placement by
+ * binary search, one scanning workgroup).  No host synchronisation: the budget
+ * stays on the device.  Errors (host-side checks, returned before any launch):
+ * SV_ERR_SHAPE, SV_ERR_NULL, SV_ERR_WORKSPACE. */
 int32_t spec_verify_plan_budget(const float* confidence, int64_t ld_conf, int32_t num_requests,
                                 int32_t block, const float* cost, int32_t ncost, int32_t* budget,
-                                double* theta, sv_stream_t stream);
+                                double* theta, void* workspace, size_t workspace_bytes,
+                                sv_stream_t stream);
 
 /* Accepted prefix from per-row accept bytes (greedy accept with precomputed
  * argmax ids, DFLASH-through-DSpark commit note): accept_len[r] = first j <

@@ -25,6 +25,8 @@ SV_BLOCK_VERIFY = 8
 LAYOUT_START, LAYOUT_ORDER, LAYOUT_END = 1, 2, 4
 LIST_CAP = 4096  # kept-set entries a row can list (top-k bound of SV_LIST_BOUNDED)
 TOPK_SINGLE_PASS = 256  # largest top-k the streaming pass selects by itself
+BUDGET_ONE_GROUP = 4096  # drafted positions plan_budget sorts in one workgroup (no workspace)
+BUDGET_MAX = 1 << 20     # drafted positions plan_budget accepts
 ROW_ACCEPT, ROW_SAMPLED, ROW_RESID_EMPTY = 1, 2, 32
 KERNEL_IDS = {"row_pass": 0, "finalize": 1, "build_out": 2, "planner": 3, "accept_prefix": 4,
               "race_segment": 5, "race_finish": 6, "acceptance_stats": 7, "check_layout": 8,
@@ -76,7 +78,7 @@ def load(path: str = LIB_PATH):
     L.spec_verify_rejection_sample_noalloc.restype = i32
     L.spec_verify_plan_windows.argtypes = [P, i64, i32, i32, i32, P, P, P, P, sz, P]
     L.spec_verify_plan_windows.restype = i32
-    L.spec_verify_plan_budget.argtypes = [P, i64, i32, i32, P, i32, P, P, P]
+    L.spec_verify_plan_budget.argtypes = [P, i64, i32, i32, P, i32, P, P, P, sz, P]
     L.spec_verify_plan_budget.restype = i32
     L.spec_verify_check_layout.argtypes = [P, i32, i32, P, P]
     L.spec_verify_check_layout.restype = i32
@@ -409,9 +411,11 @@ def plan_budget(confidence: torch.Tensor, cost: Optional[torch.Tensor]):
     tb = _dev(cost, torch.float32, "cost")
     budget = torch.empty(1, dtype=torch.int32, device=conf.device)
     theta = torch.empty(1, dtype=torch.float64, device=conf.device)
+    ws = workspace(0, 1, R, B, conf.device) if R * B > BUDGET_ONE_GROUP else None
     rc = load().spec_verify_plan_budget(_ptr(conf), B, R, B, _ptr(tb),
                                         0 if tb is None else tb.numel(), _ptr(budget),
-                                        _ptr(theta), _stream())
+                                        _ptr(theta), _ptr(ws), 0 if ws is None else ws.numel(),
+                                        _stream())
     _check(rc)
     return budget, theta
 

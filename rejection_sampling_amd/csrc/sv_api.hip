@@ -389,19 +389,43 @@ int32_t spec_verify_plan_windows(const float* confidence, int64_t ld_conf, int32
 
 int32_t spec_verify_plan_budget(const float* confidence, int64_t ld_conf, int32_t num_requests,
                                 int32_t block, const float* cost, int32_t ncost, int32_t* budget,
-                                double* theta, sv_stream_t stream) {
+                                double* theta, void* workspace, size_t workspace_bytes,
+                                sv_stream_t stream) {
   if (num_requests < 0 || block < 0 || ncost < 0) return fail(SV_ERR_SHAPE, "negative size");
   const int64_t n = (int64_t)num_requests * block;
-  if (n > sv::kBudgetMaxKeys) return fail(SV_ERR_SHAPE, "num_requests * block must be <= 4096");
+  if (n > sv::kBudgetMaxN) return fail(SV_ERR_SHAPE, "num_requests * block must be <= 2^20");
   if (!budget) return fail(SV_ERR_NULL, "budget is NULL");
   if (n > 0 && !confidence) return fail(SV_ERR_NULL, "confidence is NULL");
   if (num_requests > 0 && ld_conf < block) return fail(SV_ERR_SHAPE, "ld_conf < block");
   if (ncost > 0 && !cost) return fail(SV_ERR_NULL, "cost is NULL with ncost > 0");
   if (cost && ncost > 0 && (int64_t)ncost < n + num_requests + 1)
     return fail(SV_ERR_SHAPE, "cost table shorter than num_requests * block + num_requests + 1");
-  launch(3, sv::budget_kernel, dim3(1), dim3(sv::kPlanBlock), (hipStream_t)stream, confidence,
-         ld_conf, num_requests, block, ncost > 0 ? cost : nullptr, budget, theta);
-  return check_launch("cost-table budget");
+  hipStream_t s = (hipStream_t)stream;
+  const float* tab = ncost > 0 ? cost : nullptr;
+  if (n <= sv::kBudgetMaxKeys) {
+    launch(3, sv::budget_kernel, dim3(1), dim3(sv::kPlanBlock), s, confidence, ld_conf,
+           num_requests, block, tab, budget, theta);
+    return check_launch("cost-table budget");
+  }
+  // tiles and the rank-ordered keys share the planner's key region (8 bytes
+  // per position)
+  const Layout L = layout(0, num_requests, block);
+  if (!workspace) return fail(SV_ERR_WORKSPACE, "workspace is NULL (R * block > 4096)");
+  if (workspace_bytes < L.total) return fail(SV_ERR_WORKSPACE, "workspace too small");
+  if (!aligned(workspace, 256)) return fail(SV_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  uint32_t* tiles = (uint32_t*)((char*)workspace + L.keys);
+  uint32_t* sorted = tiles + n;
+  const int nt = (int)((n + sv::kBudgetMaxKeys - 1) / sv::kBudgetMaxKeys);
+  int32_t rc;
+  launch(3, sv::budget_tile_kernel, dim3(nt), dim3(sv::kPlanBlock), s, confidence, ld_conf,
+         num_requests, block, tiles);
+  if ((rc = check_launch("budget tiles"))) return rc;
+  launch(3, sv::budget_rank_kernel, dim3((unsigned)((n + sv::kPlanBlock - 1) / sv::kPlanBlock)),
+         dim3(sv::kPlanBlock), s, (const uint32_t*)tiles, (int32_t)n, sorted);
+  if ((rc = check_launch("budget ranks"))) return rc;
+  launch(3, sv::budget_scan_kernel, dim3(1), dim3(sv::kPlanBlock), s, (const uint32_t*)sorted,
+         num_requests, (int32_t)n, tab, budget, theta);
+  return check_launch("budget scan");
 }
 
 int32_t spec_verify_accept_prefix(const uint8_t* accepted, const int32_t* qo_indptr,

@@ -98,6 +98,11 @@ __global__ void build_out_kernel(VerifyArgs A, BuildOutArgs B);
 __global__ void plan_kernel(PlanArgs A);
 __global__ void budget_kernel(const float* conf, int64_t ld_conf, int32_t R, int32_t B,
                               const float* cost, int32_t* budget, double* theta);
+__global__ void budget_tile_kernel(const float* conf, int64_t ld_conf, int32_t R, int32_t B,
+                                   uint32_t* tiles);
+__global__ void budget_rank_kernel(const uint32_t* tiles, int32_t n, uint32_t* sorted);
+__global__ void budget_scan_kernel(const uint32_t* sorted, int32_t R, int32_t n, const float* cost,
+                                   int32_t* budget, double* theta);
 __global__ void accept_prefix_kernel(const uint8_t* accepted, const int32_t* qo, int32_t R,
                                      const int32_t* verify_cap, int32_t* accept_len);
 __global__ void acceptance_stats_kernel(const int32_t* accept_len, const int32_t* verify_len,
@@ -113,7 +118,8 @@ __global__ void est_observe_kernel(const double* feature, const int32_t* accept_
 constexpr int kRowBlock = SV_BLOCK;
 constexpr int kRowPassPerCU = 4;     // row-pass workgroups resident per CU (LDS and VGPR bound)
 constexpr int kPlanBlock = 1024;
-constexpr int kBudgetMaxKeys = 4096; // drafted positions a cost-table budget search sorts in LDS
+constexpr int kBudgetMaxKeys = 4096; // drafted positions one workgroup sorts in LDS (budget search)
+constexpr int kBudgetMaxN = 1 << 20;  // drafted positions of a budget search (tiles of kBudgetMaxKeys)
 constexpr size_t kRowRecBytes = 64;
 constexpr size_t kWsHeader = 256;    // workspace bytes before the row records (check word)
 constexpr int kEstMaxBlock = 64;     // estimator positions per request

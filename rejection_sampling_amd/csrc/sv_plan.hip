@@ -176,48 +176,35 @@ __global__ __launch_bounds__(kPB) void plan_kernel(PlanArgs A) {
 // since the table is a staircase; no profiled table, no trim).  tau(b) = R +
 // the b best survivals in the planner's rank order; budget b packs b + R
 // verify rows, so Theta(b) = tau(b) / cost[b + R]; the smallest b with the
-// largest Theta wins.  One workgroup: the survivals sorted in LDS (bitonic,
-// 32-bit: tau depends on the values only, so the planner's index tie-break
-// among equal survivals needs no place in the key), summed in that order by a
-// block scan (fp64), and a block argmax.  A table equal over [R, R*B + R], or none, gives R*B;
-// a non-positive or non-finite cost in that range gives budget -1.
-__global__ __launch_bounds__(kPB) void budget_kernel(const float* conf, int64_t ld_conf, int32_t R,
-                                                     int32_t B, const float* cost, int32_t* budget,
-                                                     double* theta) {
-  __shared__ uint32_t keys[kBudgetMaxKeys];  // ~bits(S): ascending = S descending
-  __shared__ double wtot[kPW];
-  __shared__ double wth[kPW];
-  __shared__ int wb[kPW];
-  __shared__ int bad_s, flat_s;
-  const int tid = threadIdx.x, w = wave_id(), l = lane_id();
-  const int n = R * B;
-  int np = 1;
-  while (np < n) np <<= 1;
+// largest Theta wins.  The survivals are sorted as 32-bit keys ~bits(S)
+// (ascending key = S descending; tau depends on the values only, so the
+// planner's index tie-break among equal survivals needs no place in the key),
+// summed in that order by a block scan (fp64), and a block argmax picks the
+// budget.  Up to kBudgetMaxKeys positions one workgroup sorts them in LDS;
+// beyond, tiles of kBudgetMaxKeys are sorted by one workgroup each, every key
+// is placed at its global rank by binary search in the other tiles, and one
+// workgroup scans the sorted keys.  A table equal over [R, R*B + R], or none,
+// gives R*B; a non-positive or non-finite cost in that range gives budget -1.
 
-  for (int r = tid; r < R; r += kPB) {
-    float acc = 1.0f;
-    for (int j = 0; j < B; ++j) {
-      float cf = conf[(size_t)r * ld_conf + j];
-      cf = (cf > 0.0f) ? (cf < 1.0f ? cf : 1.0f) : 0.0f;
-      acc = (j == 0) ? cf : __fmul_rn(acc, cf);
-      keys[j * R + r] = ~__float_as_uint(acc);  // acc >= +0: bits order = value order
-    }
+// Survival of position (r, j): the planner's left-to-right fp32 product of the
+// clamped confidences (NaN -> 0), bit for bit.
+__device__ __forceinline__ float survival_at(const float* conf, int64_t ld_conf, int r, int j) {
+  float acc = 1.0f;
+  for (int t = 0; t <= j; ++t) {
+    float cf = conf[(size_t)r * ld_conf + t];
+    cf = (cf > 0.0f) ? (cf < 1.0f ? cf : 1.0f) : 0.0f;
+    acc = (t == 0) ? cf : __fmul_rn(acc, cf);
   }
-  for (int t = n + tid; t < np; t += kPB) keys[t] = 0xFFFFFFFFu;  // padding sorts last
-  if (tid == 0) { bad_s = 0; flat_s = 1; }
-  __syncthreads();
-  if (cost) {
-    const float c0 = cost[R];
-    for (int t = R + tid; t <= n + R; t += kPB) {
-      const float c = cost[t];
-      if (!(c > 0.0f) || !isfinite(c)) atomicOr(&bad_s, 1);
-      if (c != c0) atomicAnd(&flat_s, 0);
-    }
-  }
-  // Bitonic sort with the keys in registers: thread t owns i = t + m * kPB
-  // (np <= 4 * kPB) and computes each stage's new value of its own elements.
-  // The partner i ^ jj is in the same thread for jj >= kPB, in the same wave
-  // for jj < 64 (a shuffle), and otherwise read through LDS between barriers.
+  return acc;
+}
+
+// Ascending bitonic sort of keys[0, np) (np a power of two <= 4 kPB; padding
+// 0xFFFFFFFF sorts last) with the keys in registers: thread t owns
+// i = t + m * kPB and computes each stage's new value of its own elements.  The
+// partner i ^ jj is in the same thread for jj >= kPB, in the same wave for
+// jj < 64 (a shuffle), and otherwise read through LDS between barriers.
+__device__ void sort_keys_lds(uint32_t* keys, int np) {
+  const int tid = threadIdx.x;
   uint32_t kv[4];
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
@@ -260,12 +247,34 @@ __global__ __launch_bounds__(kPB) void budget_kernel(const float* conf, int64_t 
   for (int m = 0; m < 4; ++m)
     if (tid + m * kPB < np) keys[tid + m * kPB] = kv[m];
   __syncthreads();
+}
+
+// tau scan and block argmax over the n sorted keys key_at(i) (rank i holds the
+// (i+1)-th best survival); writes budget and theta.  One workgroup.
+template <class KeyAt>
+__device__ void budget_argmax(KeyAt&& key_at, int n, int R, const float* cost, int32_t* budget,
+                              double* theta) {
+  __shared__ double wtot[kPW];
+  __shared__ double wth[kPW];
+  __shared__ int wb[kPW];
+  __shared__ int bad_s, flat_s;
+  const int tid = threadIdx.x, w = wave_id(), l = lane_id();
+  if (tid == 0) { bad_s = 0; flat_s = 1; }
+  __syncthreads();
+  if (cost) {
+    const float c0 = cost[R];
+    for (int t = R + tid; t <= n + R; t += kPB) {
+      const float c = cost[t];
+      if (!(c > 0.0f) || !isfinite(c)) atomicOr(&bad_s, 1);
+      if (c != c0) atomicAnd(&flat_s, 0);
+    }
+  }
   // thread t holds ranks [t * C, t * C + C): their survivals' sum, then a block scan
   const int C = (n + kPB - 1) / kPB;
   double loc = 0.0;
   for (int c = 0; c < C; ++c) {
     const int i = tid * C + c;
-    if (i < n) loc += (double)__uint_as_float(~keys[i]);
+    if (i < n) loc += (double)__uint_as_float(~key_at(i));
   }
   const double incl = wave_scan_dpp(loc);
   if (l == 63) wtot[w] = incl;
@@ -280,7 +289,12 @@ __global__ __launch_bounds__(kPB) void budget_kernel(const float* conf, int64_t 
     for (int c = 0; c < C; ++c) {
       const int i = tid * C + c;
       if (i >= n) break;
-      pre += (double)__uint_as_float(~keys[i]);
+      const float sv = __uint_as_float(~key_at(i));
+      pre += (double)sv;
+      // a zero survival on a stair that does not fall leaves Theta where the
+      // budget before it had it: that smaller budget keeps the tie (tau is
+      // rebuilt per thread, so its rounding must not decide here)
+      if (sv == 0.0f && !(cost[i + 1 + R] < cost[i + R])) continue;
       const double th = pre / (double)cost[i + 1 + R];
       if (th > best_th) { best_th = th; best_b = i + 1; }
     }
@@ -311,6 +325,88 @@ __global__ __launch_bounds__(kPB) void budget_kernel(const float* conf, int64_t 
     *budget = bb;
     if (theta) *theta = bt;
   }
+}
+
+__global__ __launch_bounds__(kPB) void budget_kernel(const float* conf, int64_t ld_conf, int32_t R,
+                                                     int32_t B, const float* cost, int32_t* budget,
+                                                     double* theta) {
+  __shared__ uint32_t keys[kBudgetMaxKeys];  // ~bits(S): ascending = S descending
+  const int tid = threadIdx.x;
+  const int n = R * B;
+  int np = 1;
+  while (np < n) np <<= 1;
+  for (int r = tid; r < R; r += kPB) {
+    float acc = 1.0f;
+    for (int j = 0; j < B; ++j) {
+      float cf = conf[(size_t)r * ld_conf + j];
+      cf = (cf > 0.0f) ? (cf < 1.0f ? cf : 1.0f) : 0.0f;
+      acc = (j == 0) ? cf : __fmul_rn(acc, cf);
+      keys[j * R + r] = ~__float_as_uint(acc);  // acc >= +0: bits order = value order
+    }
+  }
+  for (int t = n + tid; t < np; t += kPB) keys[t] = 0xFFFFFFFFu;  // padding sorts last
+  __syncthreads();
+  sort_keys_lds(keys, np);
+  budget_argmax([&](int i) { return keys[i]; }, n, R, cost, budget, theta);
+}
+
+// Large batches, step 1: tile t (flat positions t * kBudgetMaxKeys + i, i.e.
+// (r, j) = divmod(position, B)) sorted in LDS and written to tiles[t * kBudgetMaxKeys ..].
+__global__ __launch_bounds__(kPB) void budget_tile_kernel(const float* conf, int64_t ld_conf,
+                                                          int32_t R, int32_t B, uint32_t* tiles) {
+  __shared__ uint32_t keys[kBudgetMaxKeys];
+  const int n = R * B;
+  const int t0 = blockIdx.x * kBudgetMaxKeys;
+  const int len = n - t0 < kBudgetMaxKeys ? n - t0 : kBudgetMaxKeys;
+  int np = 1;
+  while (np < len) np <<= 1;
+  for (int i = threadIdx.x; i < np; i += kPB) {
+    uint32_t key = 0xFFFFFFFFu;
+    if (i < len) {
+      const int pidx = t0 + i;
+      key = ~__float_as_uint(survival_at(conf, ld_conf, pidx / B, pidx % B));
+    }
+    keys[i] = key;
+  }
+  __syncthreads();
+  sort_keys_lds(keys, np);
+  for (int i = threadIdx.x; i < len; i += kPB) tiles[t0 + i] = keys[i];
+}
+
+// Large batches, step 2: key i of tile t goes to its global rank: i, plus the
+// keys of every earlier tile at or below it, plus those of every later tile
+// strictly below it (equal keys: earlier tiles first), found by binary search.
+__global__ __launch_bounds__(kPB) void budget_rank_kernel(const uint32_t* tiles, int32_t n,
+                                                          uint32_t* sorted) {
+  const int g = blockIdx.x * kPB + threadIdx.x;
+  if (g >= n) return;
+  const int T = (n + kBudgetMaxKeys - 1) / kBudgetMaxKeys;
+  const int t = g / kBudgetMaxKeys;
+  const uint32_t k = tiles[g];
+  int rank = g - t * kBudgetMaxKeys;
+  for (int u = 0; u < T; ++u) {
+    if (u == t) continue;
+    const uint32_t* tk = tiles + (size_t)u * kBudgetMaxKeys;
+    const int len = n - u * kBudgetMaxKeys < kBudgetMaxKeys ? n - u * kBudgetMaxKeys : kBudgetMaxKeys;
+    // first index whose key is > k (u < t) or >= k (u > t)
+    int lo = 0, hi = len;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      const uint32_t km = tk[mid];
+      const bool before = u < t ? km <= k : km < k;
+      if (before) lo = mid + 1;
+      else hi = mid;
+    }
+    rank += lo;
+  }
+  sorted[rank] = k;
+}
+
+// Large batches, step 3: the scan and argmax over the sorted keys.
+__global__ __launch_bounds__(kPB) void budget_scan_kernel(const uint32_t* sorted, int32_t R,
+                                                          int32_t n, const float* cost,
+                                                          int32_t* budget, double* theta) {
+  budget_argmax([&](int i) { return sorted[i]; }, n, R, cost, budget, theta);
 }
 
 // One wave per request: accept_len = first j < min(gamma, cap) with a zero byte.

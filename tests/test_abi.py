@@ -105,17 +105,27 @@ def test_host_validation_without_gpu(lib):
     assert lib.spec_verify_estimator_init(fake, 65, None) == -2
     assert lib.spec_verify_estimator_init(None, 8, None) == -1
     assert lib.spec_verify_estimator_state_doubles(8) == 6 + 5 * 8
-    # cost-table budget: more than 4096 positions, a table too short, NULL budget,
-    # a NULL table with entries
+    # cost-table budget: more than 2^20 positions, a table too short, NULL budget,
+    # a NULL table with entries, more than 4096 positions without a workspace or
+    # with one too small or misaligned
     c = ctypes.c_void_p
     lib.spec_verify_plan_budget.argtypes = [c, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, c,
-                                            ctypes.c_int32, c, c, c]
-    assert lib.spec_verify_plan_budget(fake, 64, 65, 64, fake, 5000, fake, None, None) == -2
-    assert lib.spec_verify_plan_budget(fake, 4, 3, 4, fake, 15, fake, None, None) == -2
+                                            ctypes.c_int32, c, c, c, ctypes.c_size_t, c]
+    assert lib.spec_verify_plan_budget(fake, 1024, 1025, 1024, fake, 1 << 21, fake, None,
+                                       None, 0, None) == -2
+    assert b"2^20" in lib.spec_verify_last_error()
+    assert lib.spec_verify_plan_budget(fake, 4, 3, 4, fake, 15, fake, None, None, 0, None) == -2
     assert b"cost table" in lib.spec_verify_last_error()
-    assert lib.spec_verify_plan_budget(fake, 4, 3, 4, fake, 16, None, None, None) == -1
-    assert lib.spec_verify_plan_budget(fake, 4, 3, 4, None, 16, fake, None, None) == -1
-    assert lib.spec_verify_plan_budget(fake, 2, 3, 4, fake, 16, fake, None, None) == -2
+    assert lib.spec_verify_plan_budget(fake, 4, 3, 4, fake, 16, None, None, None, 0, None) == -1
+    assert lib.spec_verify_plan_budget(fake, 4, 3, 4, None, 16, fake, None, None, 0, None) == -1
+    assert lib.spec_verify_plan_budget(fake, 2, 3, 4, fake, 16, fake, None, None, 0, None) == -2
+    big = lib.spec_verify_workspace_bytes(0, 1, 65, 64)
+    assert lib.spec_verify_plan_budget(fake, 64, 65, 64, fake, 5000, fake, None, None, 0,
+                                       None) == -4
+    assert lib.spec_verify_plan_budget(fake, 64, 65, 64, fake, 5000, fake, None, fake, big - 1,
+                                       None) == -4
+    assert lib.spec_verify_plan_budget(fake, 64, 65, 64, fake, 5000, fake, None,
+                                       ctypes.c_void_p(0x10008), big, None) == -4
     # layout check: NULL qo_indptr or word, negative sizes
     lib.spec_verify_check_layout.argtypes = [c, ctypes.c_int32, ctypes.c_int32, c, c]
     assert lib.spec_verify_check_layout(None, 3, 9, fake, None) == -1
