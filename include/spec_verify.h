@@ -207,9 +207,10 @@ int32_t spec_verify_rejection_sample_noalloc(const void* target_logits, sv_dtype
                                              int32_t* next_token, uint8_t* row_flags,
                                              sv_stream_t stream);
 
-/* Confidence planner (TensorRT-LLM PR #17056, first commit note: prefix
- * survival is the cumulative product of per-position probabilities; the budget
- * goes out by global survival rank with a value-independent tie-break).
+/* Confidence planner (method: TensorRT-LLM PR #17056, first commit note): a
+ * position's survival is the product of its request's confidences up to it,
+ * and one global ranking of all positions by survival, with ties ordered by
+ * position and request rather than by value, decides which are verified.
  * Confidences are clamped to [0,1] (NaN -> 0); S[r][j] = c[r][0]*...*c[r][j] in
  * fp32, left to right; all (r, j) are ranked by (S desc, j asc, r asc) and the
  * first min(budget, R*block) are verified.
@@ -223,13 +224,13 @@ int32_t spec_verify_plan_windows(const float* confidence, int64_t ld_conf, int32
                                  int32_t* qo_indptr, float* survival, void* workspace,
                                  size_t workspace_bytes, sv_stream_t stream);
 
-/* Verify budget from a step-cost table (TensorRT-LLM PR #17056, description:
- * the planner's budget is a global argmax of tau/cost over a profiled
- * step-cost table, not a first descent, because the table is a staircase;
- * without a profiled table it does not trim).  Survivals and their rank order
- * are spec_verify_plan_windows's.  For b in [0, R*B]: tau(b) = R + the b best
- * survivals (fp64), the step packs b + R verify rows (bonus rows included), and
- * Theta(b) = tau(b) / cost[b + R]; the smallest b with the largest Theta wins.
+/* Verify budget from a step-cost table (method: TensorRT-LLM PR #17056,
+ * description).  Survivals and their rank order are spec_verify_plan_windows's.
+ * Every b in [0, R*B] is scored: tau(b) = R + the b largest survivals (fp64),
+ * the step runs b + R verify rows (bonus rows included), and Theta(b) = tau(b) /
+ * cost[b + R]; the largest Theta wins, the smaller b on equal Theta.  Scoring
+ * every b (not stopping at the first drop) matters because the cost rises in
+ * steps.  Without a table nothing is trimmed.
  *   confidence [R, ld_conf] fp32, device (as spec_verify_plan_windows)
  *   cost       [ncost] fp32, device: step cost by packed verify row count; NULL
  *              or ncost 0: no table.  ncost must reach R*B + R + 1.

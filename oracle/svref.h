@@ -19,9 +19,9 @@
  *    iff draft == target argmax; temperature > 0 runs the Leviathan ratio test;
  *    Gumbel noise keyed by position.  Sections 3-4: fp64 acceptance uniforms.
  *  - TensorRT-LLM PR #17056 "DSpark confidence scheduling", first commit note and
- *    description: prefix survival is a cumulative product of per-position
- *    probabilities, the budget goes out by global survival rank with a
- *    value-independent tie-break, windows are packed with a qo_indptr; the
+ *    description: survival of a position as a running product of confidences,
+ *    one batch-wide ranking by survival (ties by position and request) that
+ *    decides the verified positions, windows packed with a qo_indptr; the
  *    review-pass note: tokens submitted per request are verify_len + 1.
  *  - Philox4x32-10: Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As
  *    Easy as 1, 2, 3", SC'11.
@@ -125,9 +125,9 @@ int32_t svref_plan_windows(const float* confidence, int64_t ld_conf, int32_t num
 int32_t svref_accept_prefix(const uint8_t* accepted, const int32_t* qo_indptr,
                             int32_t num_requests, const int32_t* verify_cap, int32_t* accept_len);
 
-/* Verify budget from a step-cost table (TensorRT-LLM PR #17056, description:
- * the planner's budget is a global argmax of tau/cost over a profiled
- * step-cost table, not a first descent, since the table is a staircase).
+/* Verify budget from a step-cost table (method: TensorRT-LLM PR #17056,
+ * description): every budget is scored by tau/cost and the best score wins,
+ * since a cost that rises in steps leaves a local peak at each step.
  * Survivals S and their rank order are those of svref_plan_windows.  For a
  * budget b in [0, R*B], tau(b) = R + (sum of the b first survivals in rank
  * order, fp64, in that order) is the expected count of tokens the step emits

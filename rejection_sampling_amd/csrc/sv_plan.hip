@@ -1,12 +1,12 @@
 // sv_plan.hip -- confidence planner and accepted-prefix kernels (gfx950).
 //
-// Planner (TensorRT-LLM PR #17056, first commit note): prefix survival is the
-// cumulative product of per-position probabilities, and the batch's verify
-// budget is handed out by global survival rank with a value-independent
-// tie-break.  Each (r, j) gets one 64-bit key whose ascending order is
-// (S desc, j asc, r asc); a radix select finds the budget-th smallest key and
-// every request's window is the count of its keys at or below it -- always a
-// prefix, since S is non-increasing along j.  One workgroup, no host sync.
+// Planner (method: TensorRT-LLM PR #17056, first commit note).  S[r, j] is
+// the running fp32 product of request r's clamped confidences up to position
+// j.  Every (r, j) gets one 64-bit key, ordered by S descending, then j, then
+// r, so equal values are ranked by position and request, never by value
+// noise.  A radix select finds the budget-th smallest key; request r verifies
+// the positions whose keys are at or below it, which are always its first
+// ones because S never grows along j.  One workgroup, no host sync.
 #include "sv_device.hpp"
 #include "sv_kernels.h"
 
@@ -171,12 +171,12 @@ __global__ __launch_bounds__(kPB) void plan_kernel(PlanArgs A) {
   if (tid == 0) A.qo_indptr[R] = carry;
 }
 
-// Verify budget from a step-cost table (TensorRT-LLM PR #17056, description:
-// the budget is a global argmax of tau/cost over a profiled step-cost table,
-// since the table is a staircase; no profiled table, no trim).  tau(b) = R +
-// the b best survivals in the planner's rank order; budget b packs b + R
-// verify rows, so Theta(b) = tau(b) / cost[b + R]; the smallest b with the
-// largest Theta wins.  The survivals are sorted as 32-bit keys ~bits(S)
+// Verify budget from a step-cost table (method: TensorRT-LLM PR #17056,
+// description).  Expected tokens per unit of step cost are scored at every
+// budget b in [0, R*B]: tau(b) = R + the b largest survivals, the step runs
+// b + R verify rows, Theta(b) = tau(b) / cost[b + R].  Every b is scored
+// because cost rises in steps, so Theta has a local peak at each step's right
+// end; the largest Theta wins, the smaller budget on equal Theta.  The survivals are sorted as 32-bit keys ~bits(S)
 // (ascending key = S descending; tau depends on the values only, so the
 // planner's index tie-break among equal survivals needs no place in the key),
 // summed in that order by a block scan (fp64), and a block argmax picks the

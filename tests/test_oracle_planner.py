@@ -1,9 +1,9 @@
 """Pins of the oracle's confidence planner.
 
-TensorRT-LLM PR #17056 (first commit note and description): prefix survival is
-the cumulative product of per-position probabilities, and the batch budget is
-handed out by global survival rank with a value-independent tie-break; windows
-are packed with a qo_indptr, one bonus row per request (review-pass note:
+TensorRT-LLM PR #17056 (first commit note and description): a position's
+survival is the running product of its request's confidences; one batch-wide
+ranking by survival, ties ordered by position and request, decides the verified
+positions; windows are packed with a qo_indptr, one bonus row per request (review-pass note:
 tokens submitted are verify_len + 1 per request).  The consolidation study's
 section 1 prints per-position acceptance and accepted tokens per draft, whose
 relation (expected accepted length = sum of survivals) is the planner's
