@@ -958,32 +958,41 @@ __device__ __forceinline__ void for_each_vector_deep(const void* row, int V, FV&
   const RowSplit<DT> sp(row, V);
   const int tid = threadIdx.x;
   if (tid < sp.head) elem(Vec<DT>::load1(row, tid), tid);
+  // every load is issued (past the end: the last vector again, not used), so
+  // the number of loads in flight is fixed and each wait covers only the
+  // group being visited, not the one being fetched
   auto load = [&](int v0, uint4* w) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int vi = v0 + u * kBlock;
-      w[u] = vi < sp.nvec ? __ldg(sp.vbase + vi) : make_uint4(0u, 0u, 0u, 0u);
+      w[u] = __ldg(sp.vbase + (vi < sp.nvec ? vi : sp.nvec - 1));
     }
   };
   auto visit = [&](int v0, const uint4* w) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+      // the vector's registers are read on every path (an empty statement
+      // that takes them as inputs), so its load is waited for here in every
+      // lane, never left pending into the next iteration
+      asm volatile("" ::"v"(w[u].x), "v"(w[u].y), "v"(w[u].z), "v"(w[u].w));
       const int vi = v0 + u * kBlock;
-      if (vi >= sp.nvec) break;
-      float x[P];
-      Vec<DT>::unpack(w[u], x);
-      vec(x, sp.head + vi * P);
+      if (vi < sp.nvec) {
+        float x[P];
+        Vec<DT>::unpack(w[u], x);
+        vec(x, sp.head + vi * P);
+      }
     }
   };
   constexpr int G = kBlock * U;  // vectors per group
   uint4 wa[U], wb[U];
-  load(tid, wa);
-  for (int v0 = tid; v0 < sp.nvec; v0 += 2 * G) {
-    if (v0 + G < sp.nvec) load(v0 + G, wb);
-    visit(v0, wa);
-    if (v0 + G >= sp.nvec) break;
-    if (v0 + 2 * G < sp.nvec) load(v0 + 2 * G, wa);
-    visit(v0 + G, wb);
+  if (sp.nvec > 0) load(tid, wa);
+  // the trip count is the same in every lane (groups, not this lane's
+  // vectors), which keeps the waits partial
+  for (int b0 = 0; b0 < sp.nvec; b0 += 2 * G) {
+    load(b0 + G + tid, wb);
+    visit(b0 + tid, wa);
+    load(b0 + 2 * G + tid, wa);
+    visit(b0 + G + tid, wb);  // (vectors past the end are skipped inside)
   }
   if (sp.tail0 + tid < V) elem(Vec<DT>::load1(row, sp.tail0 + tid), sp.tail0 + tid);
 }

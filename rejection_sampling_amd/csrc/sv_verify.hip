@@ -235,9 +235,12 @@ __device__ void exact_kept_set(const void* row, int V, float m, float T, int k_e
 // further down is summed in registers.  A block scan over the bins from the
 // top finds the boundary value; a second pass, when needed, lists the kept set
 // (when it fits a list) and collects the ids of the ties at the boundary,
-// ranked to give the cut when only some of them are kept.  Returns false when
-// the boundary lies below the binned values or the ties overflow their buffer
-// (the caller then runs the general path).
+// ranked to give the cut when only some of them are kept.  zk_stream, when
+// positive, is the row's mass Z_K (relative to exp(m/T)) that the streaming
+// pass already summed: the target is then P times it and the elements below
+// the binned values are not visited at all.  Returns false when the boundary
+// lies below the binned values or the ties overflow their buffer (the caller
+// then runs the general path).
 constexpr int kNbCodes = 4 * kBlock;
 constexpr int kTieBuf = kWaves * 256;
 
@@ -248,9 +251,9 @@ __device__ __forceinline__ float bf16_code_value(uint32_t k16) {
 
 template <int DT>
 __device__ __forceinline__ bool exact_topp_codes(const void* row, int V, float m, float T, float P,
-                                                 int d, float xd, bool sorted, ListEntry* L,
-                                                 RowShared& sh, ExactOut& o, int& tie_cut,
-                                                 bool& listed) {
+                                                 int d, float xd, double zk_stream, bool sorted,
+                                                 ListEntry* L, RowShared& sh, ExactOut& o,
+                                                 int& tie_cut, bool& listed) {
   static_assert(DT == 1, "bf16 rows only");
   const int tid = threadIdx.x;
   if (!(m > -INFINITY) || !(m < INFINITY)) return false;
@@ -267,13 +270,14 @@ __device__ __forceinline__ bool exact_topp_codes(const void* row, int V, float m
   // the lowest binned value: elements below it are summed, not binned
   const float x_lo = mk16 >= (uint32_t)(kNbCodes - 1)
                          ? bf16_code_value(mk16 - (uint32_t)(kNbCodes - 1)) : -INFINITY;
+  const bool sum_below = !(zk_stream > 0.0);
   double below = 0.0;  // sum of the fp32 weights of the unbinned elements
   int amin = 0x7FFFFFFF, tied = 0;
   auto count = [&](float x, int i) {
     if (x >= x_lo) {
       atomicAdd(&cnt[mk16 - (fkey(x) >> 16)], 1u);
       if (x == m && i < amin) amin = i;
-    } else {
+    } else if (sum_below) {
       below += (double)exp2f((x - m) * c);
     }
   };
@@ -283,12 +287,28 @@ __device__ __forceinline__ bool exact_topp_codes(const void* row, int V, float m
   };
   for_each_vector_deep<DT, 2>(row, V, [&](const float* x, int i0) {
     const float vmax = vec_max<8>(x);
-    if (vmax < x_lo) {  // the common case: no element is binned
+    if (vmax < x_lo) {  // no element is binned
+      if (sum_below) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) below += (double)exp2f((x[e] - m) * c);
+        for (int e = 0; e < 8; ++e) below += (double)exp2f((x[e] - m) * c);
+      }
     } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) count(x[e], i0 + e);
+      for (int e = 0; e < 8; ++e) {
+        // the bin from the value's bf16 bits (its order code, -0 as +0):
+        // in the window iff the bin index is below kNbCodes
+        uint32_t h = __float_as_uint(x[e]) >> 16;
+        h = h == 0x8000u ? 0u : h;
+        const uint32_t code = (h & 0x8000u) ? (~h & 0xFFFFu) : (h | 0x8000u);
+        const uint32_t bin = mk16 - code;
+        if (bin < (uint32_t)kNbCodes) atomicAdd(&cnt[bin], 1u);
+        else if (sum_below) below += (double)exp2f((x[e] - m) * c);
+      }
+      if (vmax == m) {  // the lowest id reaching the maximum
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (x[e] == m && i0 + e < amin) amin = i0 + e;
+      }
     }
     if (i0 < d && vmax >= xd) {
 #pragma unroll
@@ -344,8 +364,8 @@ __device__ __forceinline__ bool exact_topp_codes(const void* row, int V, float m
   // the unbinned elements in the same fixed-point units (their weights are
   // summed in fp64 from fp32 values: within one unit per element of the
   // per-element truncation)
-  const uint64_t zk_fx = tot + (uint64_t)(blw * scale);
-  const double target = (double)P * (double)zk_fx;
+  const double zk_fx = sum_below ? (double)(tot + (uint64_t)(blw * scale)) : zk_stream * scale;
+  const double target = (double)P * zk_fx;
   {
     uint64_t above = base + incl - loc;
     uint32_t cab = cbase + cincl - lcnt;
@@ -377,7 +397,7 @@ __device__ __forceinline__ bool exact_topp_codes(const void* row, int V, float m
   o.nb = nb;
   o.ntie = avail;
   o.nkeep = cnt_above + nb;
-  o.zk = (double)zk_fx / scale;
+  o.zk = zk_fx / scale;
   o.zn = ((double)above + (double)nb * (double)fw) / scale;
   o.argmax = 0x7FFFFFFF - (int)(uint32_t)block_max_u64((uint64_t)(uint32_t)(0x7FFFFFFF - amin),
                                                       sh.uscr);
@@ -1268,6 +1288,23 @@ __device__ __forceinline__ RowParams row_params(const VerifyArgs& A, int r) {
   }
   return p;
 }
+// What the exact path of a row needs to know up front: the row max and the
+// streamed Z_K (0 when none), its request's sampling values, its draft token
+// with that token's logit and draft probability, and the uniform's key.  The
+// rest of the row's record is read from the workspace at the end.
+struct PendingIn {
+  float m;
+  double zk;
+  RowParams rp;
+  int d;
+  float xd, qd;
+  uint32_t rid, pos0;
+};
+
+template <int DT>
+__device__ __forceinline__ void resolve_pending_in(const VerifyArgs& A, int i, int j, bool tested,
+                                                   bool bonus, const PendingIn& in, RowShared& sh);
+
 // Greedy verify with every tested draft: accept iff it equals the argmax.
 __device__ __forceinline__ void greedy_record(RowRec& out, float m, int a, bool tested, int d,
                                               bool d_ok) {
@@ -1538,12 +1575,23 @@ __device__ __forceinline__ void row_pass(const VerifyArgs& A, RowShared& sh) {
   }
 
   if (exact) {
-    // the multi-pass exact path, run by this row's workgroup
+    // the multi-pass exact path, run by this row's workgroup; Z_K of the
+    // stream goes with the record (0 when the row summed nothing)
     out.mode = kModePending;
+    out.zk = need_sum ? Z : 0.0;
     if (tid == 0) *rec = out;
+    PendingIn pin;
+    pin.m = m;
+    pin.zk = out.zk;
+    pin.rp = rp;
+    pin.d = d;
+    pin.xd = d_ok ? Vec<DT>::load1(row, d) : 0.0f;
+    pin.qd = qd;
+    pin.rid = rid;
+    pin.pos0 = pos0;
     __threadfence_block();
     __syncthreads();
-    resolve_pending<DT>(A, i, r, j, tested, !A.build && j == cap_eff, sh);
+    resolve_pending_in<DT>(A, i, j, tested, !A.build && j == cap_eff, pin, sh);
     return;
   }
 
@@ -1589,36 +1637,50 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
 // Exact kept set of a row the streaming pass could not settle (candidate
 // overflow, a top-p mass beyond the buffer, or top-k above the buffer), then
 // p(d) and the ratio test of its draft.  Rewrites the row record.
+// The exact path of a pending row, its inputs loaded from the record and the
+// request's arrays (the finalize and build kernels).
 template <int DT>
 __device__ __forceinline__ void resolve_pending(const VerifyArgs& A, int i, int r, int j,
                                                 bool tested, bool bonus, RowShared& sh) {
-  RowRec out = A.rec[i];
-  const int V = A.vocab;
-  const float T = A.temperature ? A.temperature[r] : 0.0f;
-  const int k = A.top_k ? A.top_k[r] : 0;
-  const float P = A.top_p ? A.top_p[r] : 1.0f;
-  int k_eff = (k > 0 && k < V) ? k : V;
-  bool topp_on = P < 1.0f;
-  if (!(P > 0.0f) && !(P != P)) {
-    k_eff = 1;
-    topp_on = false;
-  }
+  PendingIn in;
+  in.m = A.rec[i].m;
+  in.zk = A.rec[i].zk;
+  in.rp = row_params(A, r);
+  in.d = tested ? A.draft_tokens[i] : -1;
+  const bool d_ok = in.d >= 0 && in.d < A.vocab;
   const void* row = (const char*)A.logits + (size_t)i * (size_t)A.ld_logits * (DT == 1 ? 2 : 4);
-  const int d = tested ? A.draft_tokens[i] : -1;
+  in.xd = d_ok ? Vec<DT>::load1(row, in.d) : 0.0f;
+  in.qd = tested && d_ok ? A.draft_probs[(size_t)i * (size_t)A.ld_q + in.d] : 0.0f;
+  in.rid = A.request_id ? A.request_id[r] : (uint32_t)r;
+  in.pos0 = A.position0 ? A.position0[r] : 0u;
+  resolve_pending_in<DT>(A, i, j, tested, bonus, in, sh);
+}
+
+template <int DT>
+__device__ __forceinline__ void resolve_pending_in(const VerifyArgs& A, int i, int j, bool tested,
+                                                   bool bonus, const PendingIn& in, RowShared& sh) {
+  const int V = A.vocab;
+  const float T = in.rp.T;
+  const int k_eff = in.rp.k_eff;
+  const bool topp_on = in.rp.topp_on;
+  const float P = in.rp.P;
+  const void* row = (const char*)A.logits + (size_t)i * (size_t)A.ld_logits * (DT == 1 ? 2 : 4);
+  const int d = in.d;
   const bool d_ok = d >= 0 && d < V;
-  const float xd = d_ok ? Vec<DT>::load1(row, d) : 0.0f;
+  const float xd = in.xd;
   ExactOut eo;
   bool listed = false, done = false;
+  int tie_cut = V;
   if constexpr (DT == 1) {
     if (k_eff == V && topp_on) {
       int tcut = V;
-      done = exact_topp_codes<DT>(row, V, out.m, T, P, d_ok ? d : -1, xd, A.build != 0,
+      done = exact_topp_codes<DT>(row, V, in.m, T, P, d_ok ? d : -1, xd, in.zk, A.build != 0,
                                   A.list + (size_t)i * kListCap, sh, eo, tcut, listed);
-      out.tie_cut = tcut;
+      tie_cut = tcut;
     }
   }
   if (!done) {
-    exact_kept_set<DT>(row, V, out.m, T, k_eff, topp_on ? P : 1.0f, d_ok ? d : -1, xd, sh, eo);
+    exact_kept_set<DT>(row, V, in.m, T, k_eff, topp_on ? P : 1.0f, d_ok ? d : -1, xd, sh, eo);
     // one ranked pass: the kept entries (when they fit a list) and the id
     // just past the last kept tie at the boundary; a kept set that fits
     // becomes an explicit list, sorted
@@ -1643,7 +1705,7 @@ __device__ __forceinline__ void resolve_pending(const VerifyArgs& A, int i, int 
         sh);
     __syncthreads();
     const int n = sh.count;
-    out.tie_cut = sh.found;
+    tie_cut = sh.found;
     __syncthreads();
     if (fits && n == eo.nkeep) {
       sort_desc(sh, n);
@@ -1658,6 +1720,8 @@ __device__ __forceinline__ void resolve_pending(const VerifyArgs& A, int i, int 
       listed = true;
     }
   }
+  RowRec out = A.rec[i];  // the row's record as the streaming pass left it
+  out.tie_cut = tie_cut;
   out.mode = listed ? kModeList : kModeRange;
   out.a = eo.argmax;
   out.bkey = eo.bkey;
@@ -1672,15 +1736,15 @@ __device__ __forceinline__ void resolve_pending(const VerifyArgs& A, int i, int 
     const bool in = kd > eo.bkey || (kd == eo.bkey && eo.tie_d < eo.nb);
     pd = in ? exp(((double)xd - (double)out.m) / (double)T) / eo.zn : 0.0;
   }
-  const uint32_t rid = A.request_id ? A.request_id[r] : (uint32_t)r;
-  const uint32_t pos0 = A.position0 ? A.position0[r] : 0u;
+  const uint32_t rid = in.rid;
+  const uint32_t pos0 = in.pos0;
   if (tested) {
     out.flags |= kRecTested;
     out.pd = pd;
     if (!d_ok) {
       out.flags |= kRecBadDraft;
     } else {
-      const double q = (double)A.draft_probs[(size_t)i * (size_t)A.ld_q + d];
+      const double q = (double)in.qd;
       const double ratio = q > 0.0 ? fmin(1.0, pd / q) : (pd > 0.0 ? 1.0 : 0.0);
       const double u = accept_uniform(A.seed, rid, pos0 + (uint32_t)j);
       if (u < ratio) out.flags |= kRecAccept;
@@ -2060,24 +2124,35 @@ __device__ __forceinline__ void race_segment(const VerifyArgs& A, int r, int sg,
       if (slot < kCandCap) cand[slot] = v;
     }
   };
+  // loads past the segment's end read its last vector again (not used), so
+  // every iteration issues the same loads and each wait covers only the
+  // vector being visited
+  const int vlast = v1 - 1;
   auto qload = [&](int vi, float* q) {
+    const int vq = vi < v1 ? vi : vlast;
 #pragma unroll
-    for (int e = 0; e < P; ++e) q[e] = (residual && vi < v1) ? qrow[sp.head + vi * P + e] : 0.0f;
+    for (int e = 0; e < P; ++e) q[e] = residual ? qrow[sp.head + vq * P + e] : 0.0f;
   };
   for (int pass = 0; pass < 2; ++pass) {
     if (sg == 0 && tid < sp.head)
       visit(Vec<DT>::load1(row, tid), tid, residual ? qrow[tid] : 0.0f);
-    const uint4 z = make_uint4(0u, 0u, 0u, 0u);
     int vi = v0 + tid;
-    uint4 w0 = vi < v1 ? __ldg(sp.vbase + vi) : z;
-    uint4 w1 = vi + kBlock < v1 ? __ldg(sp.vbase + vi + kBlock) : z;
-    uint4 w2 = vi + 2 * kBlock < v1 ? __ldg(sp.vbase + vi + 2 * kBlock) : z;
+    auto vload = [&](int v) { return __ldg(sp.vbase + (v < v1 ? v : vlast)); };
+    const bool any = v1 > v0;  // an empty segment loads nothing
+    uint4 w0 = make_uint4(0u, 0u, 0u, 0u), w1 = w0, w2 = w0;
     float q0[P];
-    qload(vi, q0);
+#pragma unroll
+    for (int e = 0; e < P; ++e) q0[e] = 0.0f;
+    if (any) {
+      w0 = vload(vi);
+      w1 = vload(vi + kBlock);
+      w2 = vload(vi + 2 * kBlock);
+      qload(vi, q0);
+    }
     // wave-uniform trip count (a wave runs while its first lane has a
     // vector), so the bound can be shared across the wave after each vector
     for (; vi - lane_id() < v1; vi += kBlock) {
-      const uint4 w3 = vi + 3 * kBlock < v1 ? __ldg(sp.vbase + vi + 3 * kBlock) : z;
+      const uint4 w3 = vload(vi + 3 * kBlock);
       float q1[P];
       qload(vi + kBlock, q1);
       float x[P];
