@@ -31,7 +31,8 @@ struct Layout {
 
 constexpr Layout layout(int64_t rows, int64_t R, int64_t block) {
   Layout L{};
-  L.rec = sv::kWsHeader;  // bytes [0, 4): the layout check word of SV_CHECK
+  L.rec = sv::kWsHeader;  // bytes [0, 4): the layout check word of SV_CHECK; [4, 8): the
+                          // split race's segment count
   L.list = L.rec + align256((size_t)rows * sizeof(sv::RowRec));
   L.race_job = L.list + align256((size_t)rows * sv::kListCap * sizeof(sv::ListEntry));
   L.race_part = L.race_job + align256((size_t)R * sizeof(int32_t));
@@ -212,6 +213,7 @@ static sv::VerifyArgs base_args(const void* logits, sv_dtype dt, int64_t ld, int
   A.race_job = (int32_t*)((char*)ws + L.race_job);
   A.race_part = (sv::RacePart*)((char*)ws + L.race_part);
   A.race_zn = (double*)((char*)ws + L.race_zn);
+  A.race_nseg = (int32_t*)((char*)ws + 4);  // header bytes [4, 8)
   A.block_w = (double*)((char*)ws + L.block_w);
   A.block = (sp->flags & SV_BLOCK_VERIFY) ? 1 : 0;
   A.check = (sp->flags & SV_CHECK) ? (const int32_t*)ws : nullptr;

@@ -47,9 +47,10 @@ struct VerifyArgs {
   uint8_t* row_flags;
   // full-vocabulary samples split over workgroups (race_segs 0: finalize runs
   // them in one workgroup)
-  int32_t race_segs;
+  int32_t race_segs;      // segments per race at most (kMaxRaceSegs at most)
   int32_t* race_job;      // [num_requests]: 2 * row + residual, or -1
-  RacePart* race_part;    // [num_requests, race_segs]
+  RacePart* race_part;    // [num_requests, kMaxRaceSegs]
+  int32_t* race_nseg;     // one int (workspace): segments per race this call
   double* race_zn;        // [num_requests]: Z_N the split race divides by
   // block verification of sampled requests (0: the token rule)
   int32_t block;

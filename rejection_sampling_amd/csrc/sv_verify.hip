@@ -845,6 +845,7 @@ struct CodeWalk {
   uint32_t code;
   double above;
   int cnt_above, count;
+  double total;  // the mass of every counted item (-1 when an item left the window)
 };
 // The walk over counts already in sh.mhist (block level).
 __device__ __forceinline__ bool code_walk_bins(RowShared& sh, uint32_t code0, float m, float c,
@@ -875,6 +876,7 @@ __device__ __forceinline__ bool code_walk_bins(RowShared& sh, uint32_t code0, fl
     const double excl = incl - loc;
     const uint64_t mk = __ballot(excl < target && target <= incl);
     if (l == 0) sh.sel_exact = mk ? 1 : 0;
+    if (l == 63) sh.dscr[0] = incl;
     if (mk) {
       const int src = __ffsll((unsigned long long)mk) - 1;
       if (l == src) {
@@ -893,13 +895,16 @@ __device__ __forceinline__ bool code_walk_bins(RowShared& sh, uint32_t code0, fl
     }
   }
   __syncthreads();
-  if (!sh.sel_exact) return false;
-  o.code = code0 + (uint32_t)sh.sel_digit;
-  o.above = sh.zn_shared;
-  o.cnt_above = sh.sel_need;
-  o.count = sh.count;
+  const bool ok = sh.sel_exact != 0;
+  o.total = sh.dscr[0];
+  if (ok) {
+    o.code = code0 + (uint32_t)sh.sel_digit;
+    o.above = sh.zn_shared;
+    o.cnt_above = sh.sel_need;
+    o.count = sh.count;
+  }
   __syncthreads();
-  return true;
+  return ok;
 }
 
 // Counts of the items' codes (key16_at(t) for t < nitems; 0xFFFFFFFF skips an
@@ -920,7 +925,10 @@ __device__ __forceinline__ bool code_walk(RowShared& sh, KeyAt&& key16_at, int n
     else sh.found = 1;  // outside the window
   }
   __syncthreads();
-  if (sh.found) return false;
+  if (sh.found) {
+    o.total = -1.0;
+    return false;
+  }
   return code_walk_bins(sh, code0, m, c, scale, target, o);
 }
 
@@ -963,11 +971,18 @@ __device__ __forceinline__ int topp_certified(const void* row, int V, float m, f
         return key > tkey ? (key >> 16) : 0xFFFFFFFFu;
       };
       CodeWalk cw;
-      if (code_walk(sh, vkey16, kWaves * kTopPEnd, code0, m, kLog2e / T, scale,
-                    (double)P * Z * scale, cw)) {
+      const double target = (double)P * Z * scale;
+      if (code_walk(sh, vkey16, kWaves * kTopPEnd, code0, m, kLog2e / T, scale, target, cw)) {
         klo = key_of_prefix(cw.code << 16, true);
         code_lo = cw.code;
       } else {
+        // every element above T* lies in one of these vectors (or is one of
+        // the at most 16 head and tail elements) and weighs at most its
+        // vector's maximum: when eight times the maxima's mass, the head and
+        // tail at full weight and a unit per truncated weight stay below the
+        // target, the certified elements cannot reach it
+        if (cw.total >= 0.0 && 8.0 * cw.total + 16.0 * scale + 8.0 * kWaves * kTopPEnd < target)
+          return -1;
         code_lo = code0;  // every element above T* has a code at least this
       }
     }
@@ -1936,29 +1951,27 @@ struct RaceBounds {
     const uint32_t key = fkey(x);
     return !(key < kmin || (key == kmin && v >= tie_cut));
   }
-  // Bounds from the element's generator word wv.
-  __device__ __forceinline__ bool from_word(float y, uint32_t wv, float q, float bl, float& lo,
-                                           float& up) const {
-    constexpr float kNegInf = -__builtin_huge_valf();
+  // The checks on the generator word wv that need no logarithm: false when
+  // the element cannot reach bl.
+  __device__ __forceinline__ bool cheap(float y, uint32_t wv, float q, float bl) const {
     // E = -ln U >= 1 - U = D 2^-24 (D an integer in [1, 2^24)), so log2 E >=
-    // floor(log2 D) - 24: an element that cannot reach bl even then is done
-    // without the logarithms
+    // floor(log2 D) - 24
     const uint32_t Dlt = 0x1000000u - (2u * (wv >> 9) + 1u);
     const int e_lo = 7 - (int)__clz(Dlt);
     if (!(y + (residual ? 2.0e-4f : 0.0f) - (float)e_lo + 2.0f * kEta >= bl)) return false;
-    float p32 = 0.0f, rhi = 0.0f;
     if (residual) {
-      // the residual's upper bound with q, still without logarithms: the
-      // key is at most rhi / 2^e_lo (an exact scaling by a power of two
-      // while the result stays normal)
-      p32 = exp2f(y);
-      rhi = p32 * (1.0f + 2.0f * kRelP) - q;  // 2 kRelP: room for the rounding of the difference
+      // the residual's upper bound with q: the key is at most rhi / 2^e_lo
+      // (an exact scaling by a power of two while the result stays normal)
+      const float rhi = exp2f(y) * (1.0f + 2.0f * kRelP) - q;  // 2 kRelP: room for the rounding of the difference
       if (!(rhi > 0.0f)) return false;
-      if (bl > -100.0f) {
-        const float kup = ldexpf(rhi, -e_lo);
-        if (kup < exp2f(bl - 2.0f * kEta)) return false;
-      }
+      if (bl > -100.0f && ldexpf(rhi, -e_lo) < exp2f(bl - 2.0f * kEta)) return false;
     }
+    return true;
+  }
+  // The bounds with the logarithms (after cheap() passed).
+  __device__ __forceinline__ bool full(float y, uint32_t wv, float q, float bl, float& lo,
+                                      float& up) const {
+    constexpr float kNegInf = -__builtin_huge_valf();
     // log2 E, E = -ln U, within far less than kEta: a short series for U near 1
     const float U = (float)(2u * (wv >> 9) + 1u) * 0x1.0p-24f;
     const float dlt = 1.0f - U;  // exact
@@ -1971,10 +1984,17 @@ struct RaceBounds {
       return true;
     }
     if (!(y + 2.0e-4f - l2e + kEta >= bl)) return false;  // even with q = 0
+    const float p32 = exp2f(y);
+    const float rhi = p32 * (1.0f + 2.0f * kRelP) - q;
     const float rlo = p32 * (1.0f - 2.0f * kRelP) - q;
     up = log2f(rhi) - l2e + kEta;
     lo = rlo > 0.0f ? log2f(rlo) - l2e - kEta : kNegInf;
     return true;
+  }
+  // Bounds from the element's generator word wv.
+  __device__ __forceinline__ bool from_word(float y, uint32_t wv, float q, float bl, float& lo,
+                                           float& up) const {
+    return cheap(y, wv, q, bl) && full(y, wv, q, bl, lo, up);
   }
 };
 
@@ -2071,10 +2091,10 @@ __device__ int stream_race_all(const void* row, int V, float m, double zn, uint3
 // dropped bound reaches the segment's best lower bound B, a second pass over
 // the segment evaluates exactly every element whose upper bound reaches B.
 template <int DT>
-__device__ __forceinline__ void race_segment(const VerifyArgs& A, int r, int sg, RowShared& sh) {
+__device__ __forceinline__ void race_segment(const VerifyArgs& A, int r, int sg, int S,
+                                             RowShared& sh) {
   constexpr int P = Vec<DT>::kEpv;
   constexpr float kNegInf = -__builtin_huge_valf();
-  const int S = A.race_segs;
   const int job = A.race_job[r];
   const int is = job >> 1;
   const bool residual = (job & 1) != 0;
@@ -2128,35 +2148,36 @@ __device__ __forceinline__ void race_segment(const VerifyArgs& A, int r, int sg,
   // every iteration issues the same loads and each wait covers only the
   // vector being visited
   const int vlast = v1 - 1;
+  // q of a vector's elements in 16-byte loads when the row's q starts on 16
+  // bytes at the first vector (the same for every vector of the row)
+  const bool qvec = residual && P % 4 == 0 && ((uintptr_t)(qrow + sp.head) & 15u) == 0;
   auto qload = [&](int vi, float* q) {
     const int vq = vi < v1 ? vi : vlast;
+    if (qvec) {
+      const float4* qp = (const float4*)(qrow + sp.head + vq * P);
 #pragma unroll
-    for (int e = 0; e < P; ++e) q[e] = residual ? qrow[sp.head + vq * P + e] : 0.0f;
+      for (int h = 0; h < P / 4; ++h) {
+        const float4 t = __ldg(qp + h);
+        q[4 * h] = t.x;
+        q[(4 * h + 1) % P] = t.y;
+        q[(4 * h + 2) % P] = t.z;
+        q[(4 * h + 3) % P] = t.w;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < P; ++e) q[e] = residual ? qrow[sp.head + vq * P + e] : 0.0f;
+    }
   };
   for (int pass = 0; pass < 2; ++pass) {
     if (sg == 0 && tid < sp.head)
       visit(Vec<DT>::load1(row, tid), tid, residual ? qrow[tid] : 0.0f);
-    int vi = v0 + tid;
-    auto vload = [&](int v) { return __ldg(sp.vbase + (v < v1 ? v : vlast)); };
     const bool any = v1 > v0;  // an empty segment loads nothing
-    uint4 w0 = make_uint4(0u, 0u, 0u, 0u), w1 = w0, w2 = w0;
-    float q0[P];
-#pragma unroll
-    for (int e = 0; e < P; ++e) q0[e] = 0.0f;
-    if (any) {
-      w0 = vload(vi);
-      w1 = vload(vi + kBlock);
-      w2 = vload(vi + 2 * kBlock);
-      qload(vi, q0);
-    }
-    // wave-uniform trip count (a wave runs while its first lane has a
-    // vector), so the bound can be shared across the wave after each vector
-    for (; vi - lane_id() < v1; vi += kBlock) {
-      const uint4 w3 = vload(vi + 3 * kBlock);
-      float q1[P];
-      qload(vi + kBlock, q1);
+    auto vload = [&](int v) { return __ldg(sp.vbase + (v < v1 ? v : vlast)); };
+    // one vector of this lane (vi; past the segment's end it only takes part
+    // in the wave's ballots and bound sharing)
+    auto vec_step = [&](int vi, const uint4& w, const float* q) {
       float x[P];
-      Vec<DT>::unpack(w0, x);
+      Vec<DT>::unpack(w, x);
       const bool act = vi < v1 && rb.vector_may_reach(vec_max<P>(x), second ? B : t2.best_lo);
       const int e0 = sp.head + vi * P;
       if ((e0 & 3) == 0) {  // the same in every lane (the row's head offset)
@@ -2170,20 +2191,20 @@ __device__ __forceinline__ void race_segment(const VerifyArgs& A, int r, int sg,
           const uint32_t ws[4] = {o.x, o.y, o.z, o.w};
           float xs[4], qs[4];
           if (DT == 1) {
-            const uint32_t wa = gh == 0 ? w0.x : w0.z, wb = gh == 0 ? w0.y : w0.w;
-            xs[0] = bf16_lo(wa);
-            xs[1] = bf16_hi(wa);
-            xs[2] = bf16_lo(wb);
-            xs[3] = bf16_hi(wb);
+            const uint32_t w01 = gh == 0 ? w.x : w.z, w23 = gh == 0 ? w.y : w.w;
+            xs[0] = bf16_lo(w01);
+            xs[1] = bf16_hi(w01);
+            xs[2] = bf16_lo(w23);
+            xs[3] = bf16_hi(w23);
 #pragma unroll
-            for (int t = 0; t < 4; ++t) qs[t] = gh == 0 ? q0[t] : q0[(4 + t) % P];
+            for (int t = 0; t < 4; ++t) qs[t] = gh == 0 ? q[t] : q[(4 + t) % P];
           } else {
-            xs[0] = __uint_as_float(w0.x);
-            xs[1] = __uint_as_float(w0.y);
-            xs[2] = __uint_as_float(w0.z);
-            xs[3] = __uint_as_float(w0.w);
+            xs[0] = __uint_as_float(w.x);
+            xs[1] = __uint_as_float(w.y);
+            xs[2] = __uint_as_float(w.z);
+            xs[3] = __uint_as_float(w.w);
 #pragma unroll
-            for (int t = 0; t < 4; ++t) qs[t] = q0[t % P];
+            for (int t = 0; t < 4; ++t) qs[t] = q[t % P];
           }
 #pragma unroll
           for (int t = 0; t < 4; ++t)
@@ -2200,15 +2221,15 @@ __device__ __forceinline__ void race_segment(const VerifyArgs& A, int r, int sg,
           };
 #pragma unroll 1
           for (int h = 0; h < 4; ++h) {
-            const uint32_t wd = h == 0 ? w0.x : (h == 1 ? w0.y : (h == 2 ? w0.z : w0.w));
+            const uint32_t wd = h == 0 ? w.x : (h == 1 ? w.y : (h == 2 ? w.z : w.w));
             if (DT == 1) {
-              const float qa = h == 0 ? q0[0] : (h == 1 ? q0[2] : (h == 2 ? q0[4] : q0[6 % P]));
-              const float qb = h == 0 ? q0[1] : (h == 1 ? q0[3] : (h == 2 ? q0[5] : q0[7 % P]));
-              visit_w(bf16_lo(wd), e0 + 2 * h, qa, word_of(e0 + 2 * h));
-              visit_w(bf16_hi(wd), e0 + 2 * h + 1, qb, word_of(e0 + 2 * h + 1));
+              const float qlo = h == 0 ? q[0] : (h == 1 ? q[2] : (h == 2 ? q[4] : q[6 % P]));
+              const float qhi = h == 0 ? q[1] : (h == 1 ? q[3] : (h == 2 ? q[5] : q[7 % P]));
+              visit_w(bf16_lo(wd), e0 + 2 * h, qlo, word_of(e0 + 2 * h));
+              visit_w(bf16_hi(wd), e0 + 2 * h + 1, qhi, word_of(e0 + 2 * h + 1));
             } else {
-              const float qa = h == 0 ? q0[0] : (h == 1 ? q0[1 % P] : (h == 2 ? q0[2 % P] : q0[3 % P]));
-              visit_w(__uint_as_float(wd), e0 + h, qa, word_of(e0 + h));
+              const float qlo = h == 0 ? q[0] : (h == 1 ? q[1 % P] : (h == 2 ? q[2 % P] : q[3 % P]));
+              visit_w(__uint_as_float(wd), e0 + h, qlo, word_of(e0 + h));
             }
           }
         }
@@ -2217,12 +2238,27 @@ __device__ __forceinline__ void race_segment(const VerifyArgs& A, int r, int sg,
       // that its own lane keeps (or whose drop forces the second pass), so
       // the wave's best is a valid filter for every lane
       if (!second) t2.best_lo = wave_max_f(t2.best_lo);
-      w0 = w1;
-      w1 = w2;
-      w2 = w3;
+    };
+    // two load buffers in turn, each consumed in place (no register copies
+    // of loads in flight), the trip count the same in every lane of a wave
+    int vi = v0 + tid;
+    uint4 wa = make_uint4(0u, 0u, 0u, 0u), wb = wa;
+    float qa[P], qb[P];
 #pragma unroll
-      for (int e = 0; e < P; ++e) q0[e] = q1[e];
+    for (int e = 0; e < P; ++e) qa[e] = qb[e] = 0.0f;
+    if (any) {
+      wa = vload(vi);
+      qload(vi, qa);
     }
+    for (; vi - lane_id() < v1; vi += 2 * kBlock) {
+      wb = vload(vi + kBlock);
+      qload(vi + kBlock, qb);
+      vec_step(vi, wa, qa);
+      wa = vload(vi + 2 * kBlock);
+      qload(vi + 2 * kBlock, qa);
+      vec_step(vi + kBlock, wb, qb);
+    }
+
     if (sg == S - 1 && sp.tail0 + tid < V)
       visit(Vec<DT>::load1(row, sp.tail0 + tid), sp.tail0 + tid,
             residual ? qrow[sp.tail0 + tid] : 0.0f);
@@ -2273,7 +2309,7 @@ __device__ __forceinline__ void race_segment(const VerifyArgs& A, int r, int sg,
     pt.key = w.key;
     pt.id = w.id;
     pt.pad = 0;
-    A.race_part[(size_t)r * S + sg] = pt;
+    A.race_part[(size_t)r * kMaxRaceSegs + sg] = pt;
   }
 }
 
@@ -2286,10 +2322,10 @@ __device__ __forceinline__ void race_finish(const VerifyArgs& A, RowShared& sh) 
   if (job < 0) return;
   const int is = job >> 1;
   const bool residual = (job & 1) != 0;
-  const int S = A.race_segs;
+  const int S = *A.race_nseg;  // as the segment kernel split the races
   RaceBest b = {-1.0, 0x7FFFFFFF};
   for (int t = threadIdx.x; t < S; t += kBlock) {
-    const RacePart pt = A.race_part[(size_t)r * S + t];
+    const RacePart pt = A.race_part[(size_t)r * kMaxRaceSegs + t];
     if (pt.key > 0.0 && race_better(pt.key, pt.id, b.key, b.id)) {
       b.key = pt.key;
       b.id = pt.id;
@@ -2723,7 +2759,6 @@ constexpr int kRaceJobList = 2048;
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) void race_segment_kernel(VerifyArgs A) {
   __shared__ RowShared sh;
   __shared__ int jobs[kRaceJobList];
-  const int S = A.race_segs;
   const int R = A.num_requests;
   const bool listed = R <= kRaceJobList;
   int nj = 0;
@@ -2738,13 +2773,24 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     }
     __syncthreads();
   }
+  // segments per race: with the jobs counted, as many as keep every
+  // workgroup at two items at most (segments of 1024 elements at least);
+  // otherwise the size-based count
+  int S = A.race_segs;
+  if (listed && nj > 0) {
+    const int by_grid = 2 * (int)gridDim.x / nj;
+    const int by_size = (A.vocab + 1023) / 1024;
+    const int hi = by_size < kMaxRaceSegs ? by_size : kMaxRaceSegs;
+    S = by_grid < 2 ? 2 : (by_grid > hi ? hi : by_grid);
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) *A.race_nseg = S;
   const int items = (listed ? nj : R) * S;
   for (int it = blockIdx.x; it < items; it += gridDim.x) {
     const int j = it / S;
     const int r = listed ? jobs[j] : j;
     if (!listed && A.race_job[r] < 0) continue;
-    if (A.dtype == 1) race_segment<1>(A, r, it - j * S, sh);
-    else race_segment<0>(A, r, it - j * S, sh);
+    if (A.dtype == 1) race_segment<1>(A, r, it - j * S, S, sh);
+    else race_segment<0>(A, r, it - j * S, S, sh);
     __syncthreads();
   }
 }
