@@ -1594,19 +1594,13 @@ __device__ __forceinline__ void row_pass(const VerifyArgs& A, RowShared& sh) {
     // stream goes with the record (0 when the row summed nothing)
     out.mode = kModePending;
     out.zk = need_sum ? Z : 0.0;
+    // (the record and the request's values are read back by the exact path:
+    // handing them over in registers raised the whole kernel's register count
+    // and slowed the streaming loop of every other row)
     if (tid == 0) *rec = out;
-    PendingIn pin;
-    pin.m = m;
-    pin.zk = out.zk;
-    pin.rp = rp;
-    pin.d = d;
-    pin.xd = d_ok ? Vec<DT>::load1(row, d) : 0.0f;
-    pin.qd = qd;
-    pin.rid = rid;
-    pin.pos0 = pos0;
     __threadfence_block();
     __syncthreads();
-    resolve_pending_in<DT>(A, i, j, tested, !A.build && j == cap_eff, pin, sh);
+    resolve_pending<DT>(A, i, r, j, tested, !A.build && j == cap_eff, sh);
     return;
   }
 
