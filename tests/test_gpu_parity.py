@@ -102,6 +102,36 @@ def test_split_race_and_one_workgroup_race():
         compare_verify(gpu, ref, qo, label=f"list_bounded={bounded}")
 
 
+def test_zero_residual_race_falls_back_to_p():
+    """Draft probabilities at twice the target's on every token (q is then no
+    distribution, which neither side needs): every rejection leaves a residual
+    that is zero on the whole kept set, so the emitted token is raced over p.
+    Whole-vocabulary kept sets (top-k off; top-p off, or 0.999 on flat rows
+    for kept sets beyond the list) take that race split over workgroups, where
+    the workgroup that ends a race runs the race over p by itself; with the
+    bounded-list hint one workgroup runs both.  Both match the oracle."""
+    from rejection_sampling_amd import binding as B
+    g = np.random.default_rng(3)
+    R = 16
+    T = g.uniform(0.6, 1.2, size=R).astype(np.float32)
+    P = np.where(np.arange(R) % 2 == 0, 1.0, 0.999).astype(np.float32)
+    w = W.small_prob_workload(57, R, g.integers(1, 6, size=R), 30011, sigma=1.0, T=T, k=0, P=P)
+    qo = w.qo_indptr()
+    p = svref.parallel_draft_probs(w.logits, qo, w.temperature, w.top_k, w.top_p, w.request_id,
+                                   w.position0, w.seed, THREADS)
+    q = (2.0 * p).astype(np.float32)
+    d = svref.sample_probs(q, qo, w.request_id, w.position0, w.seed, tag=2)
+    ref = oracle_verify(w, qo, d, q, threads=THREADS)
+    emitted = np.array([qo[r] + ref["accept_len"][r] for r in range(R)])
+    assert np.sum(ref["row_flags"][emitted] & svref.ROW_RESID_EMPTY) >= 4
+    for bounded in (False, True):
+        progress(f"zero residual, list_bounded={bounded}")
+        gpu = gpu_verify(w, qo, d, q, list_bounded=bounded)
+        compare_verify(gpu, ref, qo, label=f"zero residual, list_bounded={bounded}")
+        assert np.array_equal(gpu["row_flags"] & B.ROW_RESID_EMPTY,
+                              ref["row_flags"] & svref.ROW_RESID_EMPTY)
+
+
 def test_row_order_hint_changes_nothing():
     """Rows of heavy requests scheduled first give the same outputs, bit for
     bit, as the natural order (every result is keyed by request and position),
