@@ -261,7 +261,7 @@ int32_t spec_verify_accept_prefix(const uint8_t* accepted, const int32_t* qo_ind
 
 /* Layout check of a packed qo_indptr (the check SV_CHECK runs inside a call),
  * for callers that build qo_indptr on the device (e.g. with
- * spec_verify_plan_windows) and want the verdict before any verify call:
+ * spec_verify_plan_windows) and want the result before any verify call:
  * writes 0 or the violated SV_LAYOUT_* bits to error_word (one int32, device).
  * Reads qo_indptr[0..R] only.  One workgroup, no synchronisation. */
 int32_t spec_verify_check_layout(const int32_t* qo_indptr, int32_t num_requests,
