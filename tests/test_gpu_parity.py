@@ -312,6 +312,32 @@ def test_build_target_probs(dtype):
     compare_build(gpu, ref, label="build")
 
 
+@pytest.mark.parametrize("V", [20000, 32768, 20003])
+def test_build_quantized_ties_top_p(V):
+    """Integer-valued logits with top-k off and kept sets beyond the list:
+    thousands of elements tie at the top-p boundary value, and the kept ones
+    are the lowest ids (more ties than the exact path's tie buffer send a row
+    to the generic multi-pass kept set).  The dense probabilities of every row
+    (zero for a dropped tie) and the kept counts match the oracle, with
+    vocabularies of whole 16-byte vectors and one with a scalar tail."""
+    g = np.random.default_rng(V)
+    R = 12
+    T = g.uniform(0.5, 1.5, size=R).astype(np.float32)
+    P = np.array([0.3, 0.6, 0.9, 0.999] * 3, np.float32)
+    w = W.small_prob_workload(V, R, g.integers(0, 3, size=R), V, T=T, k=0, P=P)
+    x = g.integers(0, 8, size=w.logits.shape).astype(np.float32)
+    w.logits = W.bf16_bits(x)
+    qo = w.qo_indptr()
+    kmax = 64
+    progress(f"quantized build V={V} rows={w.num_rows}")
+    gpu = _gpu_build(w, qo, True, kmax)
+    ref = svref.parallel_build(w.logits, qo, w.temperature, w.top_k, w.top_p, w.request_id,
+                               w.position0, w.seed, kmax=kmax, prob_rows=range(w.num_rows),
+                               threads=THREADS)
+    assert int((ref["kept_count"] > 4096).sum()) >= R // 2
+    compare_build(gpu, ref, label=f"quantized build V={V}")
+
+
 def _build_full(w, qo, label, prob_rows):
     """Build parity at a workload's full shape: every row's max, argmax, lse,
     kept count and first 1024 kept ids, dense probabilities on prob_rows, and
